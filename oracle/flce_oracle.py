@@ -1,0 +1,184 @@
+"""Plain CPU float64 oracle for fused linear + cross-entropy (FLCE), forward and backward.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports this module; it is
+used by the tests, by the smoke check and by the benchmark's CPU-baseline leg.
+
+What is computed follows the PR description on the page "[AOTAutograd] tweak
+min-cut partitioner to avoid saving softmax output" (PyTorch PR #126348): the
+linear layer produces the softmax input (the logits), a per-row maximum and a
+per-row sum of exponentials are formed from it in two separate passes, the
+negative log-likelihood needs only the label's entry of each row, and the
+backward pass needs the whole softmax, which is a function of the logits and the
+small per-row max/sum tensors. The weight has the `nn.Linear(H, V, bias=False)`
+layout shown in that PR's test (W is [V, H], no bias). The optional logit
+softcap is the Gemma2 one mentioned in the comments of "Torch compiled FLCE is
+2x faster than the current FLCE" (Liger-Kernel issue #227); the pages name it
+without a formula, and this oracle takes s = c * tanh(z / c), with c = 0 meaning
+"off".
+
+Everything is done the plain way, on fully materialised float64 logits:
+
+    z   = X W^T                       (one BLAS call; the definition of the linear layer)
+    s   = c tanh(z / c)  or  z
+    m   = max_v s                      (first pass over the row)
+    lse = m + ln sum_v exp(s - m)      (second pass over the row)
+    l_t = lse_t - s_{t, y_t}           for rows whose label is not ignore_index
+    loss = sum_t l_t / N  (mean over the N valid rows)   or   sum_t l_t (sum)
+
+    backward with d loss = 1:
+    g_t   = 1/N (mean) or 1 (sum) on valid rows, 0 on ignored rows
+    ds_tv = g_t (exp(s_tv - lse_t) - [v == y_t])
+    dz_tv = ds_tv (1 - (s_tv / c)^2)   when the softcap is on (d/dz c tanh(z/c) = 1 - tanh^2)
+    dX = dZ W,   dW = dZ^T X           (two BLAS calls)
+
+Readings taken where the pages are silent (the same list is kept with the design notes):
+  * mean is over the valid rows of the whole call; with N = 0 the loss and all
+    gradients are 0 (PyTorch would give NaN);
+  * a label outside [0, V) that is not ignore_index is an error here;
+  * no intermediate is rounded to bf16: the inputs' exact values are widened to
+    float64 and every step stays in float64.
+
+There is no blocking, online softmax, chunking or fusion here: rows are
+independent, and the whole [BT, V] logits matrix of the rows asked for is built.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "logits",
+    "apply_softcap",
+    "row_logsumexp",
+    "valid_mask",
+    "flce_forward_backward",
+    "flce_rows",
+]
+
+
+def _f64(a) -> np.ndarray:
+    """Widen an array (numpy, or a CPU torch tensor of any float dtype) to float64."""
+    if hasattr(a, "detach"):  # a torch tensor: bf16 has no numpy dtype, so widen in torch first
+        import torch
+
+        return a.detach().to(device="cpu", dtype=torch.float64).numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def _labels(y) -> np.ndarray:
+    if hasattr(y, "detach"):
+        y = y.detach().cpu().numpy()
+    return np.asarray(y, dtype=np.int64).reshape(-1)
+
+
+def logits(X: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Step 1 of the PR description: the linear layer, z = X W^T, W in nn.Linear's [V, H] layout."""
+    return X @ W.T
+
+
+def apply_softcap(Z: np.ndarray, softcap: float) -> np.ndarray:
+    """Gemma2 logit softcap c tanh(z / c) (named in Liger-Kernel issue #227; formula is this oracle's reading)."""
+    if softcap > 0.0:
+        return softcap * np.tanh(Z / softcap)
+    return Z
+
+
+def row_logsumexp(S: np.ndarray):
+    """Steps 2 and 3 of the PR description: one pass for the row max, a second for the row sum.
+
+    Returns (m, lse) with lse = m + ln sum_v exp(s_v - m).
+    """
+    m = S.max(axis=1)
+    total = np.exp(S - m[:, None]).sum(axis=1)
+    return m, m + np.log(total)
+
+
+def valid_mask(y: np.ndarray, V: int, ignore_index: int) -> np.ndarray:
+    """Rows that take part in the loss: label != ignore_index. Any other label must lie in [0, V)."""
+    valid = y != ignore_index
+    bad = valid & ((y < 0) | (y >= V))
+    if bad.any():
+        raise ValueError(f"label out of range [0, {V}) at rows {np.nonzero(bad)[0][:8].tolist()}")
+    return valid
+
+
+def _check(X, W, y, softcap, reduction):
+    if X.ndim != 2 or W.ndim != 2 or X.shape[1] != W.shape[1]:
+        raise ValueError(f"bad shapes X{X.shape} W{W.shape}")
+    if y.shape[0] != X.shape[0]:
+        raise ValueError("labels must have one entry per row of X")
+    if not (softcap >= 0.0):  # also rejects NaN
+        raise ValueError("softcap must be >= 0 (0 = off)")
+    if reduction not in ("mean", "sum"):
+        raise ValueError("reduction must be 'mean' or 'sum'")
+
+
+def _row_terms(X, W, y, ignore_index, softcap, reduction, n_valid):
+    """Per-row forward quantities and dZ for the rows of X (all of them materialised)."""
+    V = W.shape[0]
+    valid = valid_mask(y, V, ignore_index)
+    N = int(valid.sum()) if n_valid is None else int(n_valid)
+    Z = logits(X, W)
+    S = apply_softcap(Z, softcap)
+    m, lse = row_logsumexp(S)
+    rows = np.arange(X.shape[0])
+    y_safe = np.where(valid, y, 0)
+    s_label = S[rows, y_safe]
+    loss_rows = np.where(valid, lse - s_label, 0.0)
+
+    if reduction == "mean":
+        g = np.where(valid, 1.0 / N, 0.0) if N > 0 else np.zeros(X.shape[0])
+    else:
+        g = np.where(valid, 1.0, 0.0)
+    P = np.exp(S - lse[:, None])  # the softmax, rebuilt from the logits and lse
+    dS = P
+    dS[rows[valid], y_safe[valid]] -= 1.0
+    dS *= g[:, None]
+    if softcap > 0.0:
+        dZ = dS * (1.0 - (S / softcap) ** 2)
+    else:
+        dZ = dS
+    return dict(valid=valid, N=N, m=m, lse=lse, s_label=s_label, loss_rows=loss_rows, g=g, dZ=dZ)
+
+
+def flce_forward_backward(X, W, y, ignore_index: int = -100, softcap: float = 0.0,
+                          reduction: str = "mean", return_details: bool = False):
+    """Loss, dL/dX and dL/dW of mean/sum NLL over softmax(softcap(X W^T)), with dL/dloss = 1.
+
+    X: [BT, H], W: [V, H], y: [BT] integer labels. Inputs of any float dtype are
+    widened exactly to float64. Returns (loss: float, dX: [BT, H] f64, dW: [V, H] f64)
+    and, with return_details, a dict of per-row quantities (lse, loss_rows, dZ, ...).
+    """
+    X = _f64(X)
+    W = _f64(W)
+    y = _labels(y)
+    _check(X, W, y, softcap, reduction)
+    t = _row_terms(X, W, y, ignore_index, softcap, reduction, None)
+    total = float(t["loss_rows"].sum())
+    if reduction == "mean":
+        loss = total / t["N"] if t["N"] > 0 else 0.0
+    else:
+        loss = total
+    dX = t["dZ"] @ W
+    dW = t["dZ"].T @ X
+    if return_details:
+        return loss, dX, dW, t
+    return loss, dX, dW
+
+
+def flce_rows(X, W, y, rows, n_valid: int, ignore_index: int = -100, softcap: float = 0.0,
+              reduction: str = "mean"):
+    """Per-row results for a subset of the rows of a larger call.
+
+    Rows of the method are independent except for the mean's divisor N, which is
+    the number of valid rows of the whole call and is passed in. Returns a dict
+    with, for each requested row: lse, loss_row (lse - s_label, 0 if ignored) and
+    the dX row. Used to check sampled rows of full-size runs.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    Xr = _f64(X[rows] if not hasattr(X, "detach") else X[rows.tolist()])
+    Wf = _f64(W)
+    yr = _labels(y)[rows]
+    _check(Xr, Wf, yr, softcap, reduction)
+    t = _row_terms(Xr, Wf, yr, ignore_index, softcap, reduction, n_valid)
+    return dict(lse=t["lse"], loss_rows=t["loss_rows"], dX=t["dZ"] @ Wf, valid=t["valid"],
+                s_label=t["s_label"])

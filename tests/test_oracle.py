@@ -1,0 +1,325 @@
+"""Pins for the CPU float64 oracle (no GPU).
+
+Each test ties the oracle to something other than itself: closed forms of the
+loss and gradients, central finite differences of the oracle's own loss, an
+independent library implementation (PyTorch CPU float64 cross_entropy +
+autograd), invariants that hold exactly, and metamorphic relations. A final
+group plants mistakes in the oracle and checks that the pins catch them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import flce_oracle as O
+
+IGN = -100
+
+
+def _rand_case(rng, BT, H, V, ignore=0, w_scale=1.0):
+    X = rng.standard_normal((BT, H))
+    W = rng.standard_normal((V, H)) * w_scale / math.sqrt(H)
+    y = rng.integers(0, V, size=BT)
+    if ignore:
+        y[rng.permutation(BT)[:ignore]] = IGN
+    return X, W, y
+
+
+def _torch_reference(X, W, y, softcap, reduction):
+    """Independent implementation: torch float64 linear + (softcap) + F.cross_entropy + autograd."""
+    Xt = torch.tensor(X, dtype=torch.float64, requires_grad=True)
+    Wt = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    yt = torch.tensor(y, dtype=torch.int64)
+    z = torch.nn.functional.linear(Xt, Wt)
+    if softcap > 0:
+        z = softcap * torch.tanh(z / softcap)
+    loss = torch.nn.functional.cross_entropy(z, yt, ignore_index=IGN, reduction=reduction)
+    loss.backward()
+    return loss.item(), Xt.grad.numpy(), Wt.grad.numpy()
+
+
+def _rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("softcap", [0.0, 5.0])
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_zero_weight_closed_form(softcap, reduction):
+    """W = 0: every logit is 0, softmax is uniform, loss = ln V per valid row; dX = 0;
+    dW[v] = g * ((1/V) sum_valid x_t - sum_{valid t, y_t = v} x_t)."""
+    rng = np.random.default_rng(1)
+    BT, H, V = 13, 6, 11
+    X = rng.standard_normal((BT, H))
+    W = np.zeros((V, H))
+    y = rng.integers(0, V, size=BT)
+    y[[2, 7]] = IGN
+    valid = y != IGN
+    N = int(valid.sum())
+    loss, dX, dW = oracle.flce_forward_backward(X, W, y, IGN, softcap, reduction)
+    g = 1.0 / N if reduction == "mean" else 1.0
+    expect_loss = math.log(V) * (1.0 if reduction == "mean" else N)
+    assert abs(loss - expect_loss) <= 1e-13 * expect_loss
+    assert np.all(dX == 0.0)
+    expect_dW = np.zeros((V, H))
+    xs = X[valid].sum(axis=0)
+    for v in range(V):
+        expect_dW[v] = g * (xs / V - X[valid & (y == v)].sum(axis=0))
+    np.testing.assert_allclose(dW, expect_dW, rtol=0, atol=1e-14)
+
+
+def test_single_class_is_zero():
+    """V = 1: softmax is 1 at the label, so the loss and every gradient are 0."""
+    rng = np.random.default_rng(2)
+    X = rng.standard_normal((5, 4))
+    W = rng.standard_normal((1, 4))
+    y = np.zeros(5, dtype=np.int64)
+    loss, dX, dW = oracle.flce_forward_backward(X, W, y)
+    assert loss == 0.0
+    assert np.abs(dX).max() < 1e-15 and np.abs(dW).max() < 1e-15
+
+
+def test_two_class_softplus_closed_form():
+    """V = 2, H = 1: loss = softplus(z_other - z_label), dX = sigma * (w_other - w_label),
+    dW_label = -sigma * x, dW_other = sigma * x with sigma = logistic(z_other - z_label)."""
+    x, a, b = 1.5, 0.5, -0.25
+    X = np.array([[x]])
+    W = np.array([[a], [b]])
+    for label, (wl, wo) in ((0, (a, b)), (1, (b, a))):
+        loss, dX, dW = oracle.flce_forward_backward(X, W, np.array([label]))
+        u = x * (wo - wl)
+        sig = 1.0 / (1.0 + math.exp(-u))
+        assert abs(loss - math.log1p(math.exp(u))) < 1e-15
+        assert abs(dX[0, 0] - sig * (wo - wl)) < 1e-15
+        assert abs(dW[label, 0] + sig * x) < 1e-15
+        assert abs(dW[1 - label, 0] - sig * x) < 1e-15
+
+
+def test_no_valid_rows_gives_zero():
+    rng = np.random.default_rng(3)
+    X, W, _ = _rand_case(rng, 6, 4, 9)
+    y = np.full(6, IGN)
+    for red in ("mean", "sum"):
+        loss, dX, dW = oracle.flce_forward_backward(X, W, y, reduction=red)
+        assert loss == 0.0 and not dX.any() and not dW.any()
+
+
+def test_label_out_of_range_raises():
+    X, W, _ = _rand_case(np.random.default_rng(4), 3, 4, 5)
+    with pytest.raises(ValueError):
+        oracle.flce_forward_backward(X, W, np.array([0, 5, 1]))
+    with pytest.raises(ValueError):
+        oracle.flce_forward_backward(X, W, np.array([0, -1, 1]))
+
+
+# ---------------------------------------------------------------- finite differences
+
+@pytest.mark.parametrize("softcap", [0.0, 1.5])
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_finite_differences(softcap, reduction):
+    """Central differences of the oracle's loss match its analytic dX and dW entry by entry."""
+    rng = np.random.default_rng(5)
+    BT, H, V = 4, 8, 16
+    X, W, y = _rand_case(rng, BT, H, V, w_scale=3.0)
+    y[1] = IGN
+    _, dX, dW = oracle.flce_forward_backward(X, W, y, IGN, softcap, reduction)
+    h = 1e-5
+
+    def L(Xp, Wp):
+        return oracle.flce_forward_backward(Xp, Wp, y, IGN, softcap, reduction)[0]
+
+    fdX = np.zeros_like(X)
+    for i in range(BT):
+        for j in range(H):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[i, j] += h
+            Xm[i, j] -= h
+            fdX[i, j] = (L(Xp, W) - L(Xm, W)) / (2 * h)
+    fdW = np.zeros_like(W)
+    for i in range(V):
+        for j in range(H):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[i, j] += h
+            Wm[i, j] -= h
+            fdW[i, j] = (L(X, Wp) - L(X, Wm)) / (2 * h)
+    np.testing.assert_allclose(dX, fdX, rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dW, fdW, rtol=1e-6, atol=1e-8)
+    assert np.all(dX[1] == 0.0)
+
+
+# ---------------------------------------------------------------- library cross-check
+
+@pytest.mark.parametrize("softcap", [0.0, 4.0])
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+@pytest.mark.parametrize("shape", [(256, 64, 1000), (64, 32, 50), (7, 8, 3)])
+def test_matches_torch_cross_entropy(softcap, reduction, shape):
+    BT, H, V = shape
+    rng = np.random.default_rng(6)
+    X, W, y = _rand_case(rng, BT, H, V, ignore=max(1, BT // 10), w_scale=4.0)
+    loss, dX, dW = oracle.flce_forward_backward(X, W, y, IGN, softcap, reduction)
+    tl, tdX, tdW = _torch_reference(X, W, y, softcap, reduction)
+    assert abs(loss - tl) <= 1e-12 * abs(tl)
+    assert _rel(dX, tdX) < 1e-12
+    assert _rel(dW, tdW) < 1e-12
+
+
+# ---------------------------------------------------------------- invariants and metamorphic relations
+
+@pytest.mark.parametrize("softcap", [0.0, 3.0])
+def test_invariants(softcap):
+    rng = np.random.default_rng(7)
+    X, W, y = _rand_case(rng, 40, 16, 30, ignore=5, w_scale=5.0)
+    loss, dX, dW, t = oracle.flce_forward_backward(X, W, y, IGN, softcap, "mean", return_details=True)
+    # each valid row of dlogits sums to 0 only without the softcap factor; sum over v of dS is 0,
+    # so without softcap sum_v dW[v, h] = 0 for every h
+    if softcap == 0.0:
+        assert np.abs(t["dZ"].sum(axis=1)).max() < 1e-15
+        assert np.abs(dW.sum(axis=0)).max() < 1e-14
+    # <dW, W> = <dX, X> = sum dZ * Z holds with or without softcap
+    assert abs((dW * W).sum() - (dX * X).sum()) < 1e-12
+    # ignored rows contribute nothing
+    ign = y == IGN
+    assert np.all(dX[ign] == 0.0) and np.all(t["loss_rows"][ign] == 0.0)
+    # sum = mean * N
+    ls, dXs, dWs = oracle.flce_forward_backward(X, W, y, IGN, softcap, "sum")
+    N = int((~ign).sum())
+    assert abs(ls - loss * N) < 1e-12 * ls
+    np.testing.assert_allclose(dXs, dX * N, rtol=1e-12, atol=1e-15)
+
+
+def test_ignored_row_content_is_irrelevant():
+    rng = np.random.default_rng(8)
+    X, W, y = _rand_case(rng, 10, 8, 12)
+    y[3] = IGN
+    a = oracle.flce_forward_backward(X, W, y)
+    X2 = X.copy()
+    X2[3] = rng.standard_normal(8) * 100
+    b = oracle.flce_forward_backward(X2, W, y)
+    assert a[0] == b[0]
+    np.testing.assert_array_equal(a[1], b[1])
+    np.testing.assert_allclose(a[2], b[2], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("a", [64.0, 128.0, 1024.0])
+def test_logit_shift_invariance(a):
+    """Append a ones-column to X and a constant-a column to W: every logit shifts by a, which the
+    softmax ignores (no softcap). Loss and the original gradient columns are unchanged; the new
+    dX column is a * sum_v dZ = 0 and the new dW column is sum_t dZ[t, v]."""
+    rng = np.random.default_rng(9)
+    X, W, y = _rand_case(rng, 20, 8, 25, ignore=2, w_scale=3.0)
+    loss, dX, dW, t = oracle.flce_forward_backward(X, W, y, return_details=True)
+    Xa = np.concatenate([X, np.ones((20, 1)), np.zeros((20, 7))], axis=1)
+    Wa = np.concatenate([W, np.full((25, 1), a), np.zeros((25, 7))], axis=1)
+    la, dXa, dWa = oracle.flce_forward_backward(Xa, Wa, y)
+    assert abs(la - loss) < 1e-12 * abs(loss) + 1e-13 * a
+    np.testing.assert_allclose(dXa[:, :8], dX, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dWa[:, :8], dW, rtol=1e-9, atol=1e-12)
+    assert np.abs(dXa[:, 8]).max() < 1e-9
+    np.testing.assert_allclose(dWa[:, 8], t["dZ"].sum(axis=0), rtol=0, atol=1e-9)
+
+
+def test_row_permutation():
+    rng = np.random.default_rng(10)
+    X, W, y = _rand_case(rng, 16, 8, 20, ignore=3)
+    perm = rng.permutation(16)
+    a = oracle.flce_forward_backward(X, W, y)
+    b = oracle.flce_forward_backward(X[perm], W, y[perm])
+    assert abs(a[0] - b[0]) < 1e-13
+    np.testing.assert_allclose(b[1], a[1][perm], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(b[2], a[2], rtol=1e-11, atol=1e-15)
+
+
+def test_vocab_permutation():
+    rng = np.random.default_rng(11)
+    X, W, y = _rand_case(rng, 16, 8, 20, ignore=3)
+    perm = rng.permutation(20)          # new row i of W is old row perm[i]
+    inv = np.argsort(perm)
+    y2 = np.where(y == IGN, IGN, inv[np.where(y == IGN, 0, y)])
+    a = oracle.flce_forward_backward(X, W, y)
+    b = oracle.flce_forward_backward(X, W[perm], y2)
+    assert abs(a[0] - b[0]) < 1e-13
+    np.testing.assert_allclose(b[2], a[2][perm], rtol=1e-12, atol=1e-15)
+
+
+def test_softcap_limits():
+    rng = np.random.default_rng(12)
+    X, W, y = _rand_case(rng, 30, 16, 40, ignore=3, w_scale=30.0)
+    c = 2.0
+    loss = oracle.flce_forward_backward(X, W, y, IGN, c)[0]
+    assert loss <= math.log(40) + 2 * c
+    big = oracle.flce_forward_backward(X, W, y, IGN, 1e6)
+    off = oracle.flce_forward_backward(X, W, y, IGN, 0.0)
+    assert abs(big[0] - off[0]) < 1e-6 * abs(off[0])
+    assert _rel(big[1], off[1]) < 1e-6 and _rel(big[2], off[2]) < 1e-6
+
+
+def test_loss_expectation_at_tiny_workload():
+    """x ~ N(0,1), W ~ N(0, 1/H) gives logits ~ N(0, |x|^2/H) roughly; E[loss] is close to
+    ln V + sigma^2/2 for uniform labels (a coarse statistical sanity band)."""
+    from linear_cross_entropy_07_amd import inputs
+
+    w = inputs.WORKLOADS["tiny_fp32"]
+    X, W, y = inputs.make_inputs(w, seed=0)
+    loss = oracle.flce_forward_backward(X, W, y)[0]
+    sigma2 = float((X.double() ** 2).sum(1).mean()) / w.H
+    assert abs(loss - (math.log(w.V) + sigma2 / 2)) < 0.1
+
+
+def test_flce_rows_matches_full():
+    rng = np.random.default_rng(13)
+    X, W, y = _rand_case(rng, 30, 8, 25, ignore=4)
+    loss, dX, dW, t = oracle.flce_forward_backward(X, W, y, return_details=True)
+    rows = [0, 5, 17, 29]
+    r = oracle.flce_rows(X, W, y, rows, n_valid=t["N"])
+    np.testing.assert_allclose(r["dX"], dX[rows], rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(r["lse"], t["lse"][rows], rtol=1e-14)
+
+
+# ---------------------------------------------------------------- planted mistakes must be caught
+
+def _pins_pass(monkeypatch=None):
+    rng = np.random.default_rng(14)
+    X, W, y = _rand_case(rng, 9, 8, 12, ignore=2, w_scale=3.0)
+    for softcap in (0.0, 2.5):
+        loss, dX, dW = O.flce_forward_backward(X, W, y, IGN, softcap, "mean")
+        tl, tdX, tdW = _torch_reference(X, W, y, softcap, "mean")
+        if abs(loss - tl) > 1e-10 or _rel(dX, tdX) > 1e-10 or _rel(dW, tdW) > 1e-10:
+            return False
+    return True
+
+
+def test_pins_accept_the_oracle():
+    assert _pins_pass()
+
+
+@pytest.mark.parametrize("mutation", ["no_softcap", "transposed_logits_use", "drop_onehot",
+                                      "wrong_sign", "lse_without_max", "softcap_grad_dropped"])
+def test_pins_catch_planted_mistakes(monkeypatch, mutation):
+    if mutation == "no_softcap":
+        monkeypatch.setattr(O, "apply_softcap", lambda Z, c: Z)
+    elif mutation == "transposed_logits_use":
+        monkeypatch.setattr(O, "logits", lambda X, W: (X @ W.T)[:, ::-1].copy())
+    elif mutation == "lse_without_max":
+        monkeypatch.setattr(O, "row_logsumexp", lambda S: (S.max(1), np.log(np.exp(S).sum(1)) + 0.01))
+    else:
+        real = O._row_terms
+
+        def patched(*a, **k):
+            t = real(*a, **k)
+            X, W, y, ign, softcap = a[0], a[1], a[2], a[3], a[4]
+            if mutation == "drop_onehot":
+                rows = np.nonzero(t["valid"])[0]
+                t["dZ"][rows, y[rows]] += t["g"][rows] * (1.0 if softcap == 0 else 0.5)
+            elif mutation == "wrong_sign":
+                t["dZ"] = -t["dZ"]
+            elif mutation == "softcap_grad_dropped" and softcap > 0:
+                Z = O.apply_softcap(O.logits(X, W), softcap)
+                t["dZ"] = t["dZ"] / (1.0 - (Z / softcap) ** 2)
+            return t
+
+        monkeypatch.setattr(O, "_row_terms", patched)
+    assert not _pins_pass()
