@@ -1,0 +1,196 @@
+"""Benchmark: fused linear + cross-entropy forward+backward on one MI355X.
+
+One step = one flce_forward_backward call over the whole batch (label pre-pass, label logits, and per
+BT chunk: logits GEMM + epilogue, row merge, grad_hidden GEMM, grad_W GEMM; then the loss), with
+inputs and outputs resident in HBM. Prints one JSON line.
+
+Workload (default): the Llama-3-8B LM head, BT=8192, H=4096, V=128256, bf16, RMS-normalised hidden,
+W ~ N(0, 0.02^2), Zipf(1.1) labels with 5% ignore_index, mean reduction, seed 0 (synthetic).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FLCE fwd+bwd tokens/sec at H=4096,V=128256 bf16; % bf16 MFMA peak; peak bytes"
+PEAK_BF16 = 2.5e15          # dense bf16 MFMA, MI355X published
+PEAK_HBM = 8.0e12
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b_head")
+    ap.add_argument("--chunk", type=int, default=0, help="chunk_rows_max (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=3072, help="rows of the oracle's bounded sample")
+    ap.add_argument("--profile-only", action="store_true", help="warmup + steps, no extras (for rocprofv3)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "linear_cross_entropy_07_amd", "csrc", "flce_kernels.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, launches_bytes_key: str = "bytes_per_launch"):
+    """HBM bytes per launch measured by rocprofv3 counters for this exact kernel source, else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get(launches_bytes_key)
+
+
+def cpu_baseline(w, X, W, y, rows: int):
+    """The oracle as it stands, on the first `rows` rows of the same workload (bounded sample)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    Xs, ys = X[:rows], y[:rows]
+    t0 = time.perf_counter()
+    oracle.flce_forward_backward(Xs, W, ys, -100, w.softcap, w.reduction)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of {w.BT} rows of {w.name} (full H={w.H}, V={w.V}), fp64 numpy/OpenBLAS "
+                      f"forward+backward incl. widening inputs to fp64; {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from linear_cross_entropy_07_amd import build_lib, flce, inputs
+
+    build_lib.ensure_built()
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = inputs.WORKLOADS[args.workload]
+    print(f"# generating {w.name}: BT={w.BT} H={w.H} V={w.V} {w.dtype}", file=sys.stderr, flush=True)
+    X, W, y = inputs.make_inputs(w, seed=0)
+    eng = flce.FLCE(dev, chunk_rows_max=args.chunk)
+    BT, H, V = w.BT, w.H, w.V
+    n_chunks, chunk_rows = eng.chunk_plan(BT)
+
+    base_alloc = torch.cuda.memory_allocated(dev)
+    Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    gh = torch.empty_like(Xd)
+    gw = torch.empty((V, H), dtype=torch.float32, device=dev)
+    ws_bytes = eng.workspace_size(BT, H, V, Xd.dtype)
+    torch.cuda.synchronize(dev)
+    io_alloc = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def step():
+        eng.forward_backward(Xd, Wd, yd, -100, w.softcap, w.reduction, out=(loss, gh, gw), workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    print(f"# warmup done, loss {float(loss):.6f}", file=sys.stderr, flush=True)
+    if args.profile_only:
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize(dev)
+        print(f"# profiled {args.steps} steps", file=sys.stderr, flush=True)
+        return
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    ms_med = statistics.median(per)
+    peak_extra = torch.cuda.max_memory_allocated(dev) - io_alloc
+
+    # per-kernel durations: HIP events bracketing each launch on the launch stream, over a second
+    # timed pass of the same steps
+    eng.profile_begin(max_launches=64 * args.steps)
+    for _ in range(args.steps):
+        step()
+    kt = eng.profile_end(stream)
+    print(f"# kernel ms/launch: " + ", ".join(f"{k} {v[0] / max(v[1], 1):.3f}x{v[1] // args.steps}"
+                                            for k, v in kt.items() if v[1]), file=sys.stderr, flush=True)
+    gemm = {k: kt[k] for k in ("fwd", "dx", "dw")}
+    dom = max(gemm, key=lambda k: gemm[k][0])
+    dom_ms = gemm[dom][0] / gemm[dom][1]
+    flops_per_launch = 2.0 * chunk_rows * H * V  # one GEMM of a full chunk: 2*C*H*V
+    # the last chunk may be shorter: average algorithmic flops over the launches actually made
+    flops_per_launch = 2.0 * BT * H * V / n_chunks
+    achieved = flops_per_launch / (dom_ms * 1e-3)
+
+    tokens_per_s = BT / (ms_med * 1e-3)
+    step_flops = 6.0 * BT * H * V
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_med, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "BT": BT, "H": H, "V": V, "softcap": w.softcap,
+                   "labels": w.labels, "ignore_frac": w.ignore_frac, "reduction": w.reduction,
+                   "chunk_rows": chunk_rows, "n_chunks": n_chunks, "parallelism": "single GPU"},
+        "mfma_frac_step": round(step_flops / (ms_med * 1e-3) / PEAK_BF16, 4),
+        "ms_p10_p90": [round(per[len(per) // 10], 4), round(per[(9 * len(per)) // 10], 4)],
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "peak_bytes": {"workspace": ws_bytes, "max_allocated_beyond_io": int(peak_extra),
+                       "inputs_outputs": int(io_alloc - base_alloc),
+                       "full_bf16_logits_not_allocated": BT * V * 2},
+        "kernels_ms_per_launch": {k: round(v[0] / v[1], 4) for k, v in kt.items() if v[1]},
+        "roofline": {"kernel": f"k_{dom}", "bound": "mfma", "achieved": round(achieved / 1e12, 2),
+                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
+                     "traffic": traffic_from_profiles(dom),
+                     "flops_per_launch": flops_per_launch},
+    }
+    if not args.no_cpu_baseline:
+        print(f"# timing the oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, X, W, y, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,139 @@
+/*
+ * flce.h - C ABI of the MI355X (gfx950) fused linear + cross-entropy library (libflce.so).
+ *
+ * What one call computes (forward and backward in one pass over the data):
+ *
+ *   z   = hidden[BT, H] . W[V, H]^T          the LM-head linear layer, W in nn.Linear(H, V, bias=False)
+ *                                            layout (the test in PyTorch PR #126348, "[AOTAutograd]
+ *                                            tweak min-cut partitioner to avoid saving softmax output")
+ *   s   = softcap * tanh(z / softcap)        Gemma2-style logit softcap when softcap > 0 (named in
+ *                                            Liger-Kernel issue #227, "Torch compiled FLCE is 2x faster
+ *                                            than the current FLCE"; the formula is this library's reading)
+ *   lse = log sum_v exp(s_v)                 per row: the row max and row sum-of-exponentials of the
+ *                                            PR #126348 description, here formed online over V tiles
+ *   loss = sum over valid rows of (lse - s[label]) / N    (FLCE_MEAN, N = number of valid rows)
+ *        = sum over valid rows of (lse - s[label])        (FLCE_SUM)
+ *   grad_hidden = dZ . W,   grad_W = dZ^T . hidden,
+ *   dZ = g * (softmax(s) - onehot(label)) * (1 - (s/softcap)^2 if softcap > 0),
+ *   g = 1/N (mean) or 1 (sum) on valid rows, 0 on rows whose label is ignore_index.
+ *
+ * The softmax is never stored: as the PR #126348 description proposes, the backward rebuilds it from
+ * the logits and the small per-row max/sum statistics. Logits exist only as a bounded 16-bit
+ * [chunk_rows, V] workspace; no [BT, V] buffer is allocated by the library or required of the caller.
+ * B*T may be any value (ragged batches, as in the benchmark comment of Liger-Kernel issue #227): the
+ * library splits the rows into balanced chunks of at most chunk_rows_max rows with one code object.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are HIP device pointers on the handle's device; "host" pointers are
+ *     ordinary host memory. The caller owns every buffer passed in; the library never frees them.
+ *   - Row-major, contiguous, densely packed: hidden and grad_hidden are [BT][H], W and grad_W are
+ *     [V][H], labels is [BT]. Device pointers must be 16-byte aligned.
+ *   - Errors are reported synchronously by the return code before anything is enqueued; the
+ *     outputs are then untouched. flce_forward_backward never allocates, never synchronises and
+ *     enqueues all its work on `stream`.
+ *   - A handle may be used by one stream at a time (it holds a small device status word).
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct flce_ctx* flce_handle;
+
+/* Element type of hidden, W and grad_hidden. grad_W is always fp32 (it is the accumulator). */
+typedef enum { FLCE_BF16 = 0, FLCE_FP32 = 1 } flce_dtype;
+
+/* Loss reduction. Per-row output (reduction 'none') is not part of this boundary. */
+typedef enum { FLCE_MEAN = 1, FLCE_SUM = 2 } flce_reduction;
+
+/* Return codes. */
+enum {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARG = -1,        /* null pointer, bad size, bad enum, misaligned pointer, bad softcap */
+  FLCE_ERR_UNSUPPORTED = -2,        /* a valid request this build does not implement (e.g. H % 8 != 0) */
+  FLCE_ERR_WORKSPACE_TOO_SMALL = -3,/* workspace_bytes < flce_workspace_size(...) */
+  FLCE_ERR_HIP = -4,                /* a HIP runtime call or kernel launch failed */
+  FLCE_ERR_LABEL_RANGE = -5         /* (flce_status) a label outside [0, V) that is not ignore_index */
+};
+
+/* Configuration passed to flce_create; a NULL pointer or zero fields select the defaults. */
+typedef struct {
+  int64_t chunk_rows_max; /* rows per chunk (0 = 4096); rounded up to a multiple of 256 */
+  int64_t reserved[3];    /* must be zero */
+} flce_config;
+
+/* Create a handle on HIP device `device`. Allocates a few hundred bytes of device memory for the
+ * status word (freed by flce_destroy). *out receives the handle. Returns FLCE_OK, or
+ * FLCE_ERR_INVALID_ARG (out == NULL, nonzero reserved fields, negative chunk_rows_max) or
+ * FLCE_ERR_HIP (no such device / allocation failed). */
+int flce_create(flce_handle* out, int device, const flce_config* cfg);
+
+/* Release the handle and its device memory. NULL is accepted. Pending work that uses the handle
+ * must have completed. */
+int flce_destroy(flce_handle h);
+
+/* Bytes of device workspace flce_forward_backward needs for this problem (host-only arithmetic, no
+ * device call). h may be NULL (default configuration). The workspace holds one chunk of 16-bit
+ * logits-derived values ([chunk_rows][V rounded up to 256], fp16 for FLCE_BF16, fp32 for
+ * FLCE_FP32), per-(row, 128-wide V segment) statistics, per-row label data, and split-K partials
+ * of grad_hidden. It never grows with BT beyond O(BT) bytes of per-row data.
+ * Returns FLCE_OK and writes *bytes, or FLCE_ERR_INVALID_ARG. */
+int flce_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, size_t* bytes);
+
+/* Chunk plan for BT rows (host-only): n = ceil(BT / chunk_rows_max) chunks of chunk_rows rows
+ * (a multiple of 256, at most chunk_rows_max), the last one holding BT - (n-1)*chunk_rows rows.
+ * h may be NULL. Returns FLCE_OK or FLCE_ERR_INVALID_ARG. */
+int flce_chunk_plan(flce_handle h, int64_t BT, int64_t* n_chunks, int64_t* chunk_rows);
+
+/* The fused forward + backward.
+ *   hidden       device, [BT][H] of dtype          (read)
+ *   W            device, [V][H] of dtype           (read)
+ *   labels       device, [BT] int64                (read); ignore_index marks rows left out
+ *   BT >= 0, H > 0 with H % 8 == 0, V > 0
+ *   dtype        FLCE_BF16 or FLCE_FP32
+ *   softcap      0 = off, > 0 = cap; negative or NaN is FLCE_ERR_INVALID_ARG
+ *   reduction    FLCE_MEAN or FLCE_SUM (dLoss/dloss = 1 is assumed; scale the grads for other upstream grads)
+ *   loss         device, 1 float (written)
+ *   grad_hidden  device, [BT][H] of dtype (overwritten)
+ *   grad_W       device, [V][H] fp32 (overwritten)
+ *   workspace    device, >= flce_workspace_size bytes, 256-byte aligned; contents are scratch
+ *   stream       a hipStream_t (NULL = the null stream)
+ * Mean over zero valid rows gives loss 0 and zero gradients. A label outside [0, V) that is not
+ * ignore_index is treated as ignored and flagged in the handle's status word (see flce_status).
+ * BT == 0 writes loss = 0 and grad_W = 0. Returns FLCE_OK or an error code before enqueueing. */
+int flce_forward_backward(flce_handle h,
+                          const void* hidden, const void* W, const int64_t* labels,
+                          int64_t BT, int64_t H, int64_t V, int dtype,
+                          int64_t ignore_index, float softcap, int reduction,
+                          float* loss, void* grad_hidden, float* grad_W,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Synchronise `stream` and report the status word of the last flce_forward_backward on it:
+ * FLCE_OK, or FLCE_ERR_LABEL_RANGE if some label was outside [0, V) and not ignore_index. */
+int flce_status(flce_handle h, void* stream);
+
+/* Kernel timing (diagnostics). Between flce_profile_begin and flce_profile_end, every kernel that
+ * flce_forward_backward enqueues on the handle is bracketed by a pair of HIP events recorded on the
+ * same stream, for at most max_launches launches. flce_profile_end synchronises `stream`, writes for
+ * each kernel kind k (FLCE_K_*) the summed duration in ms_out[k] and the launch count in count_out[k]
+ * (arrays of FLCE_K_COUNT entries, host memory), and releases the events. Events are created in
+ * flce_profile_begin, never inside flce_forward_backward. Returns FLCE_OK, FLCE_ERR_INVALID_ARG or
+ * FLCE_ERR_HIP. */
+enum { FLCE_K_PREPASS = 0, FLCE_K_LABEL = 1, FLCE_K_FWD = 2, FLCE_K_MERGE = 3, FLCE_K_DX = 4,
+       FLCE_K_DX_REDUCE = 5, FLCE_K_DW = 6, FLCE_K_FINALIZE = 7, FLCE_K_COUNT = 8 };
+int flce_profile_begin(flce_handle h, int max_launches);
+int flce_profile_end(flce_handle h, void* stream, double* ms_out, int64_t* count_out);
+
+/* Static description of a return code. */
+const char* flce_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

@@ -1,0 +1,49 @@
+"""Build step for libflce.so (gfx950): hipcc compiles the HIP kernels and the C-ABI host code in-tree."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libflce.so")
+SOURCES = ["flce_kernels.hip", "flce_api.cpp"]
+
+# Packed fp32 VALU forms stay off: ordinary float code is left to scalar VALU instructions.
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libflce.so)")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libflce.so for gfx950 into the package directory and return its path."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", INCLUDE, "-I", CSRC,
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-8000:]}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def ensure_built() -> str:
+    """Return the library path, building it only if no library exists yet."""
+    if not os.path.exists(LIB):
+        build()
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,61 @@
+// Internal interface between the host scheduler (flce_api.cpp) and the kernels (flce_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace flce {
+
+// Tile geometry shared by host planning and kernels.
+constexpr int kTile = 256;      // rows/cols of every GEMM block tile
+constexpr int kSeg = 128;       // width (in V) of one row-statistics segment (one wave's M extent)
+constexpr int kRowAlign = 256;  // chunk sizes are multiples of this
+
+// Per-call device parameters written by the label pre-pass and read by later kernels.
+struct DevParams {
+  int n_valid;   // N = number of rows whose label is in [0, V)
+  float ginv;    // 1/N (mean, N > 0), 0 (mean, N == 0), 1 (sum)
+  int status;    // bit 0: a label outside [0, V) that is not ignore_index was seen
+  int pad;
+};
+
+// Views of the workspace for one call (carved by the host).
+struct Work {
+  void* ws_e;          // [chunk_rows][V_pad] fp16 (bf16 path) or fp32 (fp32 path)
+  float* seg_m;        // [chunk_rows][nseg]: segment max, then (after merge) per-segment scale
+  float* seg_s;        // [chunk_rows][nseg]: segment sum of exp(s - segment max)
+  int* y32;            // [BT] label or -1 for rows that do not count
+  float* s_label;      // [BT] softcapped label logit
+  float* og;           // [BT] g * d s_label / d z_label (one-hot coefficient of dZ)
+  float* loss_row;     // [BT]
+  float* dx_part;      // [splits][chunk_rows][H] fp32 split-K partials of grad_hidden (may be null)
+  DevParams* params;   // in the workspace
+};
+
+struct Problem {
+  int64_t BT, H, V, V_pad, nseg;
+  int dtype;           // 0 bf16, 1 fp32
+  int64_t ignore_index;
+  float softcap;
+  int reduction;       // 1 mean, 2 sum
+};
+
+// Launchers (all enqueue on `stream`, return hipError_t of the launch).
+hipError_t launch_prepass(const Problem& p, const int64_t* labels, const Work& w, int* status_out,
+                          hipStream_t stream);
+hipError_t launch_label_logit(const Problem& p, const void* hidden, const void* W, const Work& w,
+                              hipStream_t stream);
+hipError_t launch_fwd(const Problem& p, const void* hidden, const void* W, const Work& w,
+                      int64_t row0, int64_t rows, hipStream_t stream);
+hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream);
+hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_hidden, int64_t row0,
+                     int64_t rows, int splits, hipStream_t stream);
+hipError_t launch_dx_reduce(const Problem& p, const Work& w, void* grad_hidden, int64_t row0, int64_t rows,
+                            int splits, hipStream_t stream);
+hipError_t launch_dw(const Problem& p, const void* hidden, const Work& w, float* grad_W, int64_t row0,
+                     int64_t rows, bool accumulate, hipStream_t stream);
+hipError_t launch_finalize(const Problem& p, const Work& w, float* loss, hipStream_t stream);
+hipError_t launch_zero_f32(float* ptr, int64_t n, hipStream_t stream);
+
+}  // namespace flce

@@ -1,0 +1,105 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports what include/flce.h declares,
+sizes its workspace, plans chunks, and rejects bad arguments before touching a device."""
+import ctypes
+import math
+
+import pytest
+import torch
+
+from linear_cross_entropy_07_amd import build_lib, flce
+
+build_lib.ensure_built()
+L = flce.lib()
+NULL = None
+
+
+def test_exports_every_declared_symbol():
+    names = flce.header_functions()
+    assert set(names) >= {"flce_create", "flce_destroy", "flce_workspace_size", "flce_chunk_plan",
+                          "flce_forward_backward", "flce_status", "flce_error_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_error_strings():
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(L.flce_error_string(code), bytes)
+
+
+@pytest.mark.parametrize("BT,expect", [
+    (0, (0, 0)), (1, (1, 256)), (256, (1, 256)), (4096, (1, 4096)), (4097, (2, 2304)),
+    (8192, (2, 4096)), (33768, (9, 3840)), (32768, (8, 4096)), (12345, (4, 3328))])
+def test_chunk_plan_default(BT, expect):
+    """Balanced plan with the default 4096-row cap: n = ceil(BT / 4096) chunks of a multiple of 256 rows."""
+    n, c = flce.chunk_plan(BT)
+    assert (n, c) == expect
+    if BT:
+        assert (n - 1) * c < BT <= n * c and c % 256 == 0 and c <= 4096
+
+
+def test_chunk_plan_ragged_sweep_covers_rows():
+    from linear_cross_entropy_07_amd import inputs
+
+    for bt in inputs.ragged_bt_list(0, 20):
+        n, c = flce.chunk_plan(bt)
+        assert (n - 1) * c < bt <= n * c
+
+
+def test_workspace_size_bounded_by_chunk_not_bt():
+    H, V = 4096, 128256
+    small = flce.workspace_size(8192, H, V)
+    big = flce.workspace_size(33768, H, V)
+    # 16-bit logits of one chunk (4096 rows) plus O(BT) per-row data; never a [BT, V] buffer
+    assert small < 8192 * V * 2
+    # chunk rows never exceed 4096, so the logits part never grows with BT; per-row data is O(BT)
+    assert big < 4096 * V * 2 * 1.1 + 64 * 33768
+    assert small >= 4096 * V * 2
+
+
+def test_workspace_size_rejects_bad_sizes():
+    out = ctypes.c_size_t()
+    assert L.flce_workspace_size(NULL, -1, 64, 10, 0, ctypes.byref(out)) == -1
+    assert L.flce_workspace_size(NULL, 4, 0, 10, 0, ctypes.byref(out)) == -1
+    assert L.flce_workspace_size(NULL, 4, 64, 0, 0, ctypes.byref(out)) == -1
+    assert L.flce_workspace_size(NULL, 4, 64, 10, 9, ctypes.byref(out)) == -1
+    assert L.flce_workspace_size(NULL, 4, 60, 10, 0, ctypes.byref(out)) == -2   # H % 8 != 0
+    assert L.flce_workspace_size(NULL, 4, 64, 10, 0, None) == -1
+    assert L.flce_workspace_size(NULL, 4, 64, 10, 0, ctypes.byref(out)) == 0
+
+
+def _fb(h=NULL, BT=4, H=64, V=10, dtype=0, softcap=0.0, red=1, ptr=256, ws_bytes=1 << 30):
+    p = ctypes.c_void_p(ptr)
+    return L.flce_forward_backward(h, p, p, p, BT, H, V, dtype, -100, softcap, red, p, p, p, p,
+                                   ws_bytes, NULL)
+
+
+def test_forward_backward_rejects_before_any_device_call():
+    assert _fb(h=NULL) == -1                     # no handle
+    fake = ctypes.c_void_p(1)                    # never dereferenced: size checks come first
+    assert _fb(h=fake, BT=-1) == -1
+    assert _fb(h=fake, H=12) == -2
+    assert _fb(h=fake, dtype=3) == -1
+    assert _fb(h=fake, red=0) == -1
+    assert _fb(h=fake, red=3) == -1
+    assert _fb(h=fake, softcap=-1.0) == -1
+    assert _fb(h=fake, softcap=float("nan")) == -1
+    assert _fb(h=fake, softcap=float("inf")) == -1
+    assert _fb(h=fake, ptr=0) == -1              # null pointers
+    assert _fb(h=fake, ptr=264) == -1            # misaligned workspace (needs 256)
+
+
+def test_create_without_gpu_fails_cleanly():
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    h = ctypes.c_void_p()
+    assert L.flce_create(ctypes.byref(h), 0, None) == -4
+    assert L.flce_create(None, 0, None) == -1
+    assert L.flce_destroy(None) == 0
+
+
+def test_config_validation():
+    cfg = flce._Config(0, (ctypes.c_int64 * 3)(1, 0, 0))
+    h = ctypes.c_void_p()
+    assert L.flce_create(ctypes.byref(h), 0, ctypes.byref(cfg)) == -1
+    cfg = flce._Config(-5, (ctypes.c_int64 * 3)(0, 0, 0))
+    assert L.flce_create(ctypes.byref(h), 0, ctypes.byref(cfg)) == -1

@@ -1,0 +1,93 @@
+"""Full-size GPU checks at the workloads' real shapes, in the launch configuration the benchmark times
+(default chunk plan): sampled rows of grad_hidden against the oracle computed row by row, the loss of a
+row subset against the oracle, and relations that hold at any size (loss additivity over row subsets,
+mean = sum / N, <grad_W, W> = <grad_hidden, hidden>, ignored rows exactly zero)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import TOL, announce, device, rel_fro
+from linear_cross_entropy_07_amd import flce, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(y, BT, rng, chunk=4096):
+    rows = set(rng.choice(BT, 12, replace=False).tolist())
+    rows |= {0, BT - 1, min(chunk - 1, BT - 1), min(chunk, BT - 1)}
+    ign = np.nonzero(y.numpy() == -100)[0]
+    if len(ign):
+        rows |= set(ign[:3].tolist())
+    return np.array(sorted(rows))
+
+
+def _fullsize_check(X, W, y, softcap, label):
+    dev = device()
+    e = flce.FLCE(dev)
+    BT, H = X.shape
+    announce(label, f"BT={BT} H={H} V={W.shape[0]} softcap={softcap}")
+    Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
+    loss, gh, gw = e.forward_backward(Xd, Wd, yd, softcap=softcap)
+    torch.cuda.synchronize()
+    assert e.status() == 0
+    loss = float(loss)
+    valid = (y != -100).numpy()
+    N = int(valid.sum())
+    tol = TOL["bf16"]
+
+    # sampled grad_hidden rows vs the oracle, row by row (N of the whole call passed in)
+    rng = np.random.default_rng(123)
+    rows = _sample_rows(y, BT, rng)
+    ref = oracle.flce_rows(X, W, y, rows, n_valid=N, softcap=softcap)
+    got = gh[torch.from_numpy(rows).to(dev)].double().cpu().numpy()
+    err = rel_fro(got[ref["valid"]], ref["dX"][ref["valid"]])
+    print(f"   loss {loss:.6f}; sampled dX rows rel err {err:.2e}", flush=True)
+    assert err <= tol["grad"]
+    assert not np.any(got[~ref["valid"]])
+
+    # loss of a 256-row subset (sum reduction) vs the oracle's per-row losses
+    sub = np.sort(rng.choice(BT, 256, replace=False))
+    sub_t = torch.from_numpy(sub)
+    ls, _, _ = e.forward_backward(Xd[sub_t.to(dev)].contiguous(), Wd, yd[sub_t.to(dev)].contiguous(),
+                                  softcap=softcap, reduction="sum")
+    ref_sub = oracle.flce_rows(X, W, y, sub, n_valid=N, softcap=softcap)
+    o_sum = float(ref_sub["loss_rows"].sum())
+    print(f"   subset sum loss gpu {float(ls):.5f} oracle {o_sum:.5f}", flush=True)
+    assert abs(float(ls) - o_sum) <= tol["loss"] * abs(o_sum)
+
+    # mean = sum / N and additivity over a split of the rows
+    lsum, _, _ = e.forward_backward(Xd, Wd, yd, softcap=softcap, reduction="sum")
+    half = BT // 2
+    l1, _, _ = e.forward_backward(Xd[:half].contiguous(), Wd, yd[:half].contiguous(), softcap=softcap,
+                                  reduction="sum")
+    l2, _, _ = e.forward_backward(Xd[half:].contiguous(), Wd, yd[half:].contiguous(), softcap=softcap,
+                                  reduction="sum")
+    lsum, l1, l2 = float(lsum), float(l1), float(l2)
+    assert abs(lsum / N - loss) <= 1e-5 * loss
+    assert abs(l1 + l2 - lsum) <= 1e-5 * lsum
+
+    # <grad_W, W> = <grad_hidden, hidden> (both equal sum dZ * Z)
+    a = float((gw.double() * Wd.double()).sum())
+    b = float((gh.double() * Xd.double()).sum())
+    print(f"   <dW,W> {a:.6e} <dX,X> {b:.6e}", flush=True)
+    assert abs(a - b) <= 2e-2 * max(abs(a), abs(b)) + 1e-6
+    # without softcap every valid row of dZ sums to zero, so sum_v grad_W[v, :] vanishes
+    if softcap == 0.0:
+        colsum = gw.double().sum(0)
+        assert float(colsum.norm()) <= 2e-2 * float(gw.double().norm())
+    assert torch.isfinite(gw).all() and torch.isfinite(gh.float()).all()
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_head", "gemma2_head", "gpt2_head"])
+def test_fullsize_workload(name):
+    w = inputs.WORKLOADS[name]
+    X, W, y = inputs.make_inputs(w, seed=0)
+    _fullsize_check(X, W, y, w.softcap, name)
+
+
+def test_ragged_sweep_samples():
+    bts = inputs.ragged_bt_list(0, 20)
+    for i in (0, 7, len(bts) - 1):
+        X, W, y = inputs.make_ragged_call(bts[i], seed=100 + i)
+        _fullsize_check(X, W, y, 0.0, f"ragged call {i}")
