@@ -94,7 +94,7 @@ int flce_chunk_plan(flce_handle h, int64_t BT, int64_t* n_chunks, int64_t* chunk
  *   hidden       device, [BT][H] of dtype          (read)
  *   W            device, [V][H] of dtype           (read)
  *   labels       device, [BT] int64                (read); ignore_index marks rows left out
- *   BT >= 0, H > 0 with H % 8 == 0, V > 0
+ *   BT >= 0, 0 < H <= 65536 with H % 8 == 0, 0 < V <= 2^20 (larger sizes: FLCE_ERR_UNSUPPORTED)
  *   dtype        FLCE_BF16 or FLCE_FP32
  *   softcap      0 = off, > 0 = cap; negative or NaN is FLCE_ERR_INVALID_ARG
  *   reduction    FLCE_MEAN or FLCE_SUM (dLoss/dloss = 1 is assumed; scale the grads for other upstream grads)
@@ -124,8 +124,8 @@ int flce_status(flce_handle h, void* stream);
  * (arrays of FLCE_K_COUNT entries, host memory), and releases the events. Events are created in
  * flce_profile_begin, never inside flce_forward_backward. Returns FLCE_OK, FLCE_ERR_INVALID_ARG or
  * FLCE_ERR_HIP. */
-enum { FLCE_K_PREPASS = 0, FLCE_K_LABEL = 1, FLCE_K_FWD = 2, FLCE_K_MERGE = 3, FLCE_K_DX = 4,
-       FLCE_K_DX_REDUCE = 5, FLCE_K_DW = 6, FLCE_K_FINALIZE = 7, FLCE_K_COUNT = 8 };
+enum { FLCE_K_PREPASS = 0, FLCE_K_FWD = 1, FLCE_K_MERGE = 2, FLCE_K_DX = 3, FLCE_K_DX_REDUCE = 4,
+       FLCE_K_DW = 5, FLCE_K_FINALIZE = 6, FLCE_K_COUNT = 7 };
 int flce_profile_begin(flce_handle h, int max_launches);
 int flce_profile_end(flce_handle h, void* stream, double* ms_out, int64_t* count_out);
 

@@ -32,7 +32,7 @@ namespace {
 
 constexpr int64_t kDefaultChunk = 4096;
 constexpr int64_t kMaxH = 1 << 16;
-constexpr int64_t kMaxV = int64_t(1) << 30;
+constexpr int64_t kMaxV = int64_t(1) << 20;  // keeps every per-tile buffer range below 2 GiB
 constexpr int64_t kMaxBT = (int64_t(1) << 31) - 1;
 constexpr int kCUs = 256;
 
@@ -59,7 +59,7 @@ int dx_splits(int64_t rows, int64_t H, int64_t V_pad, int dtype) {
   // Split K (= V) only when it shortens the wave-quantised schedule: with T tiles on kCUs CUs and
   // s splits the time goes as ceil(T*s / kCUs) / s, plus a small per-split cost for the reduction.
   const int64_t tiles = ((rows + flce::kTile - 1) / flce::kTile) * ((H + flce::kTile - 1) / flce::kTile);
-  const int64_t nk = V_pad / (dtype == 0 ? 64 : 32);
+  const int64_t nk = V_pad * (dtype == 0 ? 2 : 4) / flce::kStepBytes;
   int best = 1;
   double best_cost = 1e30;
   for (int s = 1; s <= 32; ++s) {
@@ -259,7 +259,6 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
     FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
     return FLCE_OK;
   }
-  FLCE_LAUNCH(FLCE_K_LABEL, flce::launch_label_logit(p, hidden, W, w, stream));
   int64_t n_chunks, crows;
   plan(BT, h->chunk_rows_max, &n_chunks, &crows);
   for (int64_t ci = 0; ci < n_chunks; ++ci) {

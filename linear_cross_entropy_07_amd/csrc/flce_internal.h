@@ -11,6 +11,7 @@ namespace flce {
 constexpr int kTile = 256;      // rows/cols of every GEMM block tile
 constexpr int kSeg = 128;       // width (in V) of one row-statistics segment (one wave's M extent)
 constexpr int kRowAlign = 256;  // chunk sizes are multiples of this
+constexpr int kStepBytes = 64;  // bytes of K per GEMM pipeline step
 
 // Per-call device parameters written by the label pre-pass and read by later kernels.
 struct DevParams {
@@ -26,7 +27,7 @@ struct Work {
   float* seg_m;        // [chunk_rows][nseg]: segment max, then (after merge) per-segment scale
   float* seg_s;        // [chunk_rows][nseg]: segment sum of exp(s - segment max)
   int* y32;            // [BT] label or -1 for rows that do not count
-  float* s_label;      // [BT] softcapped label logit
+  float* s_label;      // [BT] softcapped label logit (written by the logits epilogue)
   float* og;           // [BT] g * d s_label / d z_label (one-hot coefficient of dZ)
   float* loss_row;     // [BT]
   float* dx_part;      // [splits][chunk_rows][H] fp32 split-K partials of grad_hidden (may be null)
@@ -44,8 +45,6 @@ struct Problem {
 // Launchers (all enqueue on `stream`, return hipError_t of the launch).
 hipError_t launch_prepass(const Problem& p, const int64_t* labels, const Work& w, int* status_out,
                           hipStream_t stream);
-hipError_t launch_label_logit(const Problem& p, const void* hidden, const void* W, const Work& w,
-                              hipStream_t stream);
 hipError_t launch_fwd(const Problem& p, const void* hidden, const void* W, const Work& w,
                       int64_t row0, int64_t rows, hipStream_t stream);
 hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream);

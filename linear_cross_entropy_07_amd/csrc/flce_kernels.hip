@@ -9,12 +9,12 @@
 //   k_fwd     Z^T tile = W_tile . X_tile^T on MFMA (bf16 -> fp32), epilogue: optional softcap,
 //             per-(row, 128-wide V segment) max and sum of exp, and one 16-bit store per logit of
 //             q = exp(s - segment max) * (softcap derivative). No [BT, V] tensor exists.
-//   k_merge   per row: lse from the segment statistics, loss term, and the per-segment scale
-//             g * exp(segment max - lse) that turns q into dZ.
-//   k_dx      grad_hidden chunk = dZ . W on MFMA; the A-operand loader rebuilds dZ tiles in registers
-//             from q, the scale and the label (no dlogits tensor is stored).
+//   k_merge_dlogits  per row: lse from the segment statistics and the loss term; then one sweep
+//             over the row rebuilds the softmax from q and turns it into dZ in place, in the operand
+//             type of the backward GEMMs. No separate softmax or dlogits tensor exists.
+//   k_dx      grad_hidden chunk = dZ . W on MFMA (W transposed in registers on its way to LDS).
 //   k_dw      grad_W (+)= dZ^T . X on MFMA; both operands are transposed in registers on the way to
-//             LDS, dZ rebuilt the same way; fp32 accumulation in place across chunks.
+//             LDS; fp32 accumulation in place across chunks.
 //
 // One GEMM core serves the three products: 256 threads (4 waves of 64) compute a 256 x 256 tile,
 // each wave a 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (or 32x32x2f32 for
@@ -36,7 +36,6 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int NTHR = 256;        // threads per GEMM block
-constexpr int KCH = 8;           // 16-byte chunks per LDS tile row per k-step (128 bytes of K)
 constexpr int TILE = kTile;      // 256
 constexpr int WT = TILE / 2;     // wave tile (128)
 constexpr int TB = WT / 32;      // 32x32 MFMA blocks per wave tile side (4)
@@ -142,194 +141,164 @@ __device__ __forceinline__ void grouped(int t, int mt, int nt, int gm, int& tm, 
   tn = in / gsz;
 }
 
-// ---- operand loaders: global -> registers (load) -> LDS chunks (store) ------------------------
-// K-contiguous rows: tile row r is source row r (stride ld), k-step ks covers 8*KV elements.
+// ---- LDS DMA: global -> LDS without registers ------------------------------------------------
+// buffer_load_dwordx4 ... lds writes each lane's 16 bytes to LDS at M0 + 16 * lane, so one wave
+// instruction fills 1 KiB of LDS contiguously; the global address of each lane is free. The loads are
+// issued from inline asm and their completion is awaited with explicit vmcnt waits, so that several
+// stages can be in flight (the compiler's own tracking would wait for all of them before any LDS
+// read). The buffer range makes out-of-range lanes write zeros, which covers every tile edge.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+constexpr u32 kOOB = 0x80000000u;  // an offset no buffer range here reaches (all ranges < 2 GiB)
+
+__device__ __forceinline__ i32x4 make_desc(const void* base, u32 bytes) {
+  const uint64_t a = (uint64_t)base;
+  return i32x4{(int)__builtin_amdgcn_readfirstlane((u32)a), (int)__builtin_amdgcn_readfirstlane((u32)(a >> 32)),
+               (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+__device__ __forceinline__ u32 lds_addr(const void* p) {
+  return (u32)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+__device__ __forceinline__ void dma16(i32x4 desc, u32 voff, u32 lds) {
+  // M0 must be written one instruction before an LDS-DMA load reads it.
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(desc), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// ---- pipeline geometry ---------------------------------------------------------------------
+// A stage holds 64 bytes of K for the 256 rows (or columns) of each operand: 16 KiB per operand.
+constexpr int kStages = 4;
+constexpr int kStageBytes = 32768;              // A + B
+constexpr int kOpBytes = 16384;
+constexpr int kDmaPerOp = kOpBytes / (NTHR * 16);  // 4 DMA instructions per thread per operand
+constexpr int kLoadsPerStage = 2 * kDmaPerOp;
+// vmcnt field encoding of s_waitcnt (gfx9): low 4 bits and bits 15:14; expcnt and lgkmcnt left at max.
+constexpr int vmcnt_only(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
+// K-contiguous operand: tile row r (an M or N index) is a source row, K runs along it. In LDS each
+// row holds 64 bytes = 4 chunks of 16 bytes, chunk kc stored at slot kc ^ ((r >> 2) & 3) so that the
+// 16 rows read at one chunk index cover all banks. A fragment is one ds_read_b128.
 template <typename T>
-struct LoadK {
-  static constexpr int KV = 16 / sizeof(T), N = TILE * KCH / NTHR;  // 8 chunks per thread
-  const T* p;
-  int64_t ld;
-  int rows;   // valid tile rows
-  int kmax;   // valid K elements
-  u32x4 r[N];
-  __device__ __forceinline__ void load(int ks) {
+struct OpK {
+  static constexpr int KV = 16 / sizeof(T), BK = 4 * KV;
+  i32x4 desc;          // rows [0, valid rows) of the tile
+  u32 rowoff[kDmaPerOp];
+  int slot;            // this lane's chunk slot within its row
+  int kc[kDmaPerOp];   // chunk of K this lane loads for each of its rows
+  int kmax;            // valid K elements (also the end of this block's K range)
+  __device__ __forceinline__ void init(const T* p, int64_t ld, int rows, int kmax_) {
+    desc = make_desc(p, (u32)(rows > 0 ? rows : 0) * (u32)(ld * sizeof(T)));
+    kmax = kmax_;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int it = 0; it < N; ++it) {
-      const int q = it * NTHR + threadIdx.x, row = q >> 3, kc = q & 7;
-      const int k = ks * KCH * KV + kc * KV;
-      r[it] = (row < rows && k < kmax) ? *(const u32x4*)(p + (int64_t)row * ld + k) : zero4();
+    for (int q = 0; q < kDmaPerOp; ++q) {
+      const int row = 16 * (kDmaPerOp * wave + q) + (lane >> 2);
+      rowoff[q] = (u32)(row * ld * (int64_t)sizeof(T));
+      kc[q] = (lane & 3) ^ ((row >> 2) & 3);
     }
   }
-  __device__ __forceinline__ void store(u32x4* s) const {
+  __device__ __forceinline__ void issue(int ks, u32 lds) const {
+    const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int it = 0; it < N; ++it) {
-      const int q = it * NTHR + threadIdx.x;
-      s[swz(q >> 3, q & 7)] = r[it];
+    for (int q = 0; q < kDmaPerOp; ++q) {
+      const int k = ks * BK + kc[q] * KV;
+      dma16(desc, k < kmax ? rowoff[q] + (u32)(k * sizeof(T)) : kOOB, lds + (kDmaPerOp * wave + q) * 1024);
+    }
+  }
+  // fragment of rows rowbase + 32 i + lane % 32 for chunk kcol
+  __device__ __forceinline__ void frag(const char* st, int rowbase, int kcol, u32x4 (&f)[TB]) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      const int row = rowbase + 32 * i + (lane & 31);
+      f[i] = *(const u32x4*)(st + row * 64 + ((kcol ^ ((row >> 2) & 3)) << 4));
     }
   }
 };
 
-// Source stored with the tile's N index contiguous and K as its row index (MN-contiguous):
-// each task loads a KV (k) x KV (n) block with KV 16-byte loads and transposes it in registers.
+// MN-contiguous operand: a source row is one K index holding the tile's 256 M/N elements
+// contiguously. In LDS a row keeps that layout (256 * sizeof(T) bytes), 16-byte chunk c stored at
+// slot c ^ (4 * (k & 3)). bf16 fragments come from two ds_read_b64_tr_b16: in each 16-lane group,
+// lane j points at row k0 + j/4, columns nb + 4 (j % 4) .. +3, and lane i receives column nb + i of
+// rows k0 .. k0+3 (gfx950 transpose read). fp32 fragments are four ds_read_b32.
 template <typename T>
-struct LoadT {
-  static constexpr int KV = 16 / sizeof(T), NG = TILE / KV, TASKS = NG * KCH, N = TASKS / NTHR;
-  const T* p;     // element (k = 0, n = 0) of the tile
-  int64_t ld;     // source row stride (elements)
-  int kvalid;     // valid k rows counted from k = 0
-  int nvalid;     // valid n columns in the tile
-  u32x4 r[N][KV];
-  __device__ __forceinline__ void load(int ks) {
+struct OpMN {
+  static constexpr int KV = 16 / sizeof(T), BK = 4 * KV;
+  static constexpr int ROWB = TILE * (int)sizeof(T);  // LDS bytes per K row
+  static constexpr int CPR = ROWB / 16;               // chunks per row
+  static constexpr int RPI = 64 / CPR;                // rows per DMA instruction (1 KiB)
+  const char* p;       // element (k = 0, n = 0) of the tile
+  int64_t ldb;         // source row stride in bytes
+  int kvalid;          // valid K rows (also the end of this block's K range)
+  u32 off[kDmaPerOp];  // byte offset of this lane's chunk within a stage's rows (kOOB if n invalid)
+  __device__ __forceinline__ void init(const T* p_, int64_t ld, int kvalid_, int nvalid) {
+    p = (const char*)p_;
+    ldb = ld * (int64_t)sizeof(T);
+    kvalid = kvalid_;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int it = 0; it < N; ++it) {
-      const int t = it * NTHR + threadIdx.x, ng = t % NG, kg = t / NG, n = ng * KV;
-#pragma unroll
-      for (int kk = 0; kk < KV; ++kk) {
-        const int k = ks * KCH * KV + kg * KV + kk;
-        r[it][kk] = (k < kvalid && n < nvalid) ? *(const u32x4*)(p + (int64_t)k * ld + n) : zero4();
-      }
+    for (int q = 0; q < kDmaPerOp; ++q) {
+      const int row = RPI * (kDmaPerOp * wave + q) + lane / CPR;
+      const int c = (lane % CPR) ^ (4 * (row & 3));
+      off[q] = c * KV < nvalid ? (u32)(row * ldb + c * 16) : kOOB;
     }
   }
-  __device__ __forceinline__ void store(u32x4* s) const {
+  __device__ __forceinline__ void issue(int ks, u32 lds) const {
+    const int wave = threadIdx.x >> 6, k0 = ks * BK;
+    const int nrows = kvalid - k0 < 0 ? 0 : (kvalid - k0 > BK ? BK : kvalid - k0);
+    const i32x4 desc = make_desc(p + (int64_t)k0 * ldb, (u32)nrows * (u32)ldb);
 #pragma unroll
-    for (int it = 0; it < N; ++it) {
-      const int t = it * NTHR + threadIdx.x, ng = t % NG, kg = t / NG;
-      u32x4 o[KV];
-      transpose(r[it], o);
-#pragma unroll
-      for (int e = 0; e < KV; ++e) s[swz(ng * KV + e, kg)] = o[e];
-    }
+    for (int q = 0; q < kDmaPerOp; ++q) dma16(desc, off[q], lds + (kDmaPerOp * wave + q) * 1024);
   }
-};
-
-// dZ rows for the grad_hidden product (M = chunk row c, K = v, K-contiguous in the workspace):
-// d = q * scale[c][segment(v)] - [v == y_c] * og_c, formed in fp32 and rounded to T.
-template <typename T>
-struct LoadDzK {
-  using S = typename Traits<T>::S;
-  static constexpr int KV = Traits<T>::KV, N = TILE * KCH / NTHR;
-  const S* p;           // workspace row 0 of the tile
-  int64_t ld;           // V_pad
-  int rows;             // valid rows
-  const float* scale;   // [rows][nseg], tile row 0
-  int nseg;
-  int yv[N];
-  float og[N];
-  u32x4 r[N];
-  float sc[N];
-  __device__ __forceinline__ void init(const int* y, const float* ogp) {
+  __device__ __forceinline__ void frag(const char* st, int colbase, int kcol, u32x4 (&f)[TB]) const {
+    const int lane = threadIdx.x & 63;
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int it = 0; it < N; ++it) {
-      const int row = (it * NTHR + threadIdx.x) >> 3;
-      yv[it] = row < rows ? y[row] : -1;
-      og[it] = row < rows ? ogp[row] : 0.0f;
-    }
-  }
-  __device__ __forceinline__ void load(int ks) {
+      for (int i = 0; i < TB; ++i) {
+        const int n = colbase + 32 * i + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        u32x4 v;
 #pragma unroll
-    for (int it = 0; it < N; ++it) {
-      const int q = it * NTHR + threadIdx.x, row = q >> 3, kc = q & 7;
-      const int k = ks * KCH * KV + kc * KV;
-      const bool ok = row < rows;
-      r[it] = ok ? *(const u32x4*)(p + (int64_t)row * ld + k) : zero4();
-      sc[it] = ok ? scale[(int64_t)row * nseg + (k / kSeg)] : 0.0f;
-    }
-  }
-  __device__ __forceinline__ void store(u32x4* s, int ks) const {
-#pragma unroll
-    for (int it = 0; it < N; ++it) {
-      const int q = it * NTHR + threadIdx.x, row = q >> 3, kc = q & 7;
-      const int k = ks * KCH * KV + kc * KV;
-      float f[KV];
-      unpack(r[it], f, (S*)nullptr);
-#pragma unroll
-      for (int e = 0; e < KV; ++e) f[e] *= sc[it];
-      const unsigned rel = (unsigned)(yv[it] - k);
-      if (rel < (unsigned)KV) {
-#pragma unroll
-        for (int e = 0; e < KV; ++e) f[e] -= (rel == (unsigned)e) ? og[it] : 0.0f;
-      }
-      s[swz(row, kc)] = pack(f, (T*)nullptr);
-    }
-  }
-};
-
-// dZ^T for the grad_W product (M = v, K = chunk row c): the workspace is [c][v], so each task loads
-// KV rows c x KV columns v, forms d per element with the row's scale and label, rounds to T and
-// transposes in registers so that LDS holds K(c)-contiguous chunks per v.
-template <typename T>
-struct LoadDzT {
-  using S = typename Traits<T>::S;
-  static constexpr int KV = Traits<T>::KV, NG = TILE / KV, TASKS = NG * KCH, N = TASKS / NTHR;
-  const S* p;           // workspace element (c = 0, v = v0)
-  int64_t ld;           // V_pad
-  int rows;             // valid chunk rows (K extent)
-  const float* scale;   // [rows][nseg] (chunk row 0)
-  int nseg;
-  int v0;               // first v of the tile
-  const int* y;         // chunk row 0
-  const float* ogp;
-  u32x4 r[N][KV];
-  float sc[N][KV];
-  int yv[N][KV];
-  float og[N][KV];
-  __device__ __forceinline__ void load(int ks) {
-#pragma unroll
-    for (int it = 0; it < N; ++it) {
-      const int t = it * NTHR + threadIdx.x, ng = t % NG, kg = t / NG;
-      const int seg = (v0 + ng * KV) / kSeg;
-#pragma unroll
-      for (int kk = 0; kk < KV; ++kk) {
-        const int c = ks * KCH * KV + kg * KV + kk;
-        const bool ok = c < rows;
-        r[it][kk] = ok ? *(const u32x4*)(p + (int64_t)c * ld + ng * KV) : zero4();
-        sc[it][kk] = ok ? scale[(int64_t)c * nseg + seg] : 0.0f;
-        yv[it][kk] = ok ? y[c] : -1;
-        og[it][kk] = ok ? ogp[c] : 0.0f;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(u32x4* s, int) const {
-#pragma unroll
-    for (int it = 0; it < N; ++it) {
-      const int t = it * NTHR + threadIdx.x, ng = t % NG, kg = t / NG;
-      const int vb = v0 + ng * KV;
-      u32x4 d[KV];
-#pragma unroll
-      for (int kk = 0; kk < KV; ++kk) {
-        float f[KV];
-        unpack(r[it][kk], f, (S*)nullptr);
-#pragma unroll
-        for (int e = 0; e < KV; ++e) f[e] *= sc[it][kk];
-        const unsigned rel = (unsigned)(yv[it][kk] - vb);
-        if (rel < (unsigned)KV) {
-#pragma unroll
-          for (int e = 0; e < KV; ++e) f[e] -= (rel == (unsigned)e) ? og[it][kk] : 0.0f;
+        for (int r = 0; r < 2; ++r) {
+          const int k = 4 * (2 * kcol + r) + ((lane & 15) >> 2);  // kcol = 2 s + half
+          const char* a = st + k * ROWB + (((n >> 3) ^ (4 * (k & 3))) << 4) + ((n & 7) << 1);
+          const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(size_t)lds_addr(a));
+          const u32x2 w = __builtin_bit_cast(u32x2, t);
+          v[2 * r] = w[0];
+          v[2 * r + 1] = w[1];
         }
-        d[kk] = pack(f, (T*)nullptr);
+        f[i] = v;
       }
-      u32x4 o[KV];
-      transpose(d, o);
+    } else {
 #pragma unroll
-      for (int e = 0; e < KV; ++e) s[swz(ng * KV + e, kg)] = o[e];
+      for (int i = 0; i < TB; ++i) {
+        const int n = colbase + 32 * i + (lane & 31);
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 4 * kcol + e;
+          v[e] = *(const u32*)(st + k * ROWB + (((n >> 2) ^ (4 * (k & 3))) << 4) + ((n & 3) << 2));
+        }
+        f[i] = v;
+      }
     }
   }
 };
-
-// Adapters so that plain loaders and the dZ loaders share one call shape.
-template <class L> __device__ __forceinline__ void store_chunks(const L& l, u32x4* s, int) { l.store(s); }
-template <typename T> __device__ __forceinline__ void store_chunks(const LoadDzK<T>& l, u32x4* s, int ks) { l.store(s, ks); }
-template <typename T> __device__ __forceinline__ void store_chunks(const LoadDzT<T>& l, u32x4* s, int ks) { l.store(s, ks); }
 
 // ---- the MFMA tile core --------------------------------------------------------------------
 // acc[i][j] is the 32x32 block (wave_m*128 + 32 i, wave_n*128 + 32 j) of the 256 x 256 tile. In the
 // 32x32 MFMA result layout, lane l holds column (l % 32) and, in register r, row
 // 8 * (r / 4) + 4 * (l / 32) + r % 4 of its block.
+//
+// K is consumed in steps of 64 bytes through a ring of kStages LDS stages filled by DMA, kStages-1
+// steps ahead. A step is two substeps of 16 MFMAs; the fragments of substep 1 are read while
+// substep 0 runs, and those of the next step's substep 0 right after the step's single barrier,
+// while substep 1 runs.
 template <typename T, class LA, class LB>
-__device__ __forceinline__ void gemm_core(LA& la, LB& lb, int kb, int ke, u32x4* sA, u32x4* sB,
+__device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int kb, int ke, char* smem,
                                           f32x16 (&acc)[TB][TB]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 1, wn = wave >> 1, half = lane >> 5;
 #pragma unroll
   for (int i = 0; i < TB; ++i)
 #pragma unroll
@@ -337,42 +306,43 @@ __device__ __forceinline__ void gemm_core(LA& la, LB& lb, int kb, int ke, u32x4*
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   if (kb >= ke) return;
-
-  la.load(kb);
-  lb.load(kb);
-  store_chunks(la, sA, kb);
-  store_chunks(lb, sB, kb);
-  __syncthreads();
-
-  const int arow = wm * WT + (lane & 31), brow = wn * WT + (lane & 31), half = lane >> 5;
-  for (int ks = kb; ks < ke; ++ks) {
-    const int cur = (ks - kb) & 1;
-    const u32x4* a = sA + cur * TILE * KCH;
-    const u32x4* b = sB + cur * TILE * KCH;
-    const bool more = ks + 1 < ke;
-    if (more) {
-      la.load(ks + 1);
-      lb.load(ks + 1);
-    }
+  const u32 lbase = lds_addr(smem);
 #pragma unroll
-    for (int s = 0; s < KCH / 2; ++s) {
-      const int kc = 2 * s + half;
-      u32x4 fa[TB], fb[TB];
-#pragma unroll
-      for (int i = 0; i < TB; ++i) fa[i] = a[swz(arow + 32 * i, kc)];
-#pragma unroll
-      for (int j = 0; j < TB; ++j) fb[j] = b[swz(brow + 32 * j, kc)];
-#pragma unroll
-      for (int i = 0; i < TB; ++i)
-#pragma unroll
-        for (int j = 0; j < TB; ++j) mma(acc[i][j], fa[i], fb[j], (T*)nullptr);
-    }
-    if (more) {
-      store_chunks(la, sA + (cur ^ 1) * TILE * KCH, ks + 1);
-      store_chunks(lb, sB + (cur ^ 1) * TILE * KCH, ks + 1);
-    }
-    __syncthreads();
+  for (int st = 0; st < kStages - 1; ++st) {
+    la.issue(kb + st, lbase + st * kStageBytes);
+    lb.issue(kb + st, lbase + st * kStageBytes + kOpBytes);
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
+  asm volatile("s_barrier" ::: "memory");
+  u32x4 fa[2][TB], fb[2][TB];
+  la.frag(smem, wm * WT, half, fa[0]);
+  lb.frag(smem + kOpBytes, wn * WT, half, fb[0]);
+  for (int ks = kb; ks < ke; ++ks) {
+    const int slot = (ks - kb) % kStages;
+    const char* st = smem + slot * kStageBytes;
+    la.frag(st, wm * WT, 2 + half, fa[1]);
+    lb.frag(st + kOpBytes, wn * WT, 2 + half, fb[1]);
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int j = 0; j < TB; ++j) mma(acc[i][j], fa[0][i], fb[0][j], (T*)nullptr);
+    // refill the slot read in the previous step (every wave passed that step's barrier after its
+    // last read of it); steps past the end load zeros
+    const int nslot = (ks - kb + kStages - 1) % kStages;
+    la.issue(ks + kStages - 1, lbase + nslot * kStageBytes);
+    lb.issue(ks + kStages - 1, lbase + nslot * kStageBytes + kOpBytes);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const char* nx = smem + ((ks - kb + 1) % kStages) * kStageBytes;
+    la.frag(nx, wm * WT, half, fa[0]);
+    lb.frag(nx + kOpBytes, wn * WT, half, fb[0]);
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int j = 0; j < TB; ++j) mma(acc[i][j], fa[1][i], fb[1][j], (T*)nullptr);
+  }
+  // drain the DMA of the steps past the end before the block's LDS can be reused or the block ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
 }
 
 // ---- kernel arguments ------------------------------------------------------------------------
@@ -382,6 +352,10 @@ struct FwdArgs {
   void* ws;
   float* seg_m;
   float* seg_s;
+  const int* y;       // chunk row 0: label or -1
+  float* s_label;     // chunk row 0
+  float* og;          // chunk row 0
+  const DevParams* prm;
   int64_t H, V, V_pad;
   int nseg, rows;
   float softcap;
@@ -389,25 +363,19 @@ struct FwdArgs {
 
 struct DxArgs {
   const void* W;
-  const void* ws;
-  const float* scale;
-  const int* y;       // chunk row 0
-  const float* og;    // chunk row 0
+  const void* ws;     // dZ of the chunk, [rows][V_pad]
   void* out;          // grad_hidden, chunk row 0 (splits == 1)
   float* part;        // [splits][rows][H] (splits > 1)
   int64_t H, V, V_pad;
-  int nseg, rows, splits, ksteps_per_split;
+  int rows, splits, ksteps_per_split;
 };
 
 struct DwArgs {
   const void* X;      // hidden, chunk row 0
-  const void* ws;
-  const float* scale;
-  const int* y;
-  const float* og;
+  const void* ws;     // dZ of the chunk, [rows][V_pad]
   float* dW;
   int64_t H, V, V_pad;
-  int nseg, rows, accumulate;
+  int rows, accumulate;
 };
 
 constexpr int kGroupFwd = 16;
@@ -419,19 +387,19 @@ template <typename T>
 __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
   using S = typename Traits<T>::S;
   constexpr int KV = Traits<T>::KV;
-  __shared__ u32x4 sA[2 * TILE * KCH];
-  __shared__ u32x4 sB[2 * TILE * KCH];
+  __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes];
 
   const int mt = (int)(a.V_pad / TILE), nt = (a.rows + TILE - 1) / TILE;
   int tm, tn;
   grouped(xcd_remap(blockIdx.x, gridDim.x), mt, nt, kGroupFwd, tm, tn);
   const int v0 = tm * TILE, c0 = tn * TILE;
 
-  LoadK<T> la{(const T*)a.W + (int64_t)v0 * a.H, a.H, (int)min<int64_t>(TILE, a.V - v0), (int)a.H, {}};
-  LoadK<T> lb{(const T*)a.X + (int64_t)c0 * a.H, a.H, min(TILE, a.rows - c0), (int)a.H, {}};
+  OpK<T> la, lb;
+  la.init((const T*)a.W + (int64_t)v0 * a.H, a.H, (int)min<int64_t>(TILE, a.V - v0), (int)a.H);
+  lb.init((const T*)a.X + (int64_t)c0 * a.H, a.H, min(TILE, a.rows - c0), (int)a.H);
   f32x16 acc[TB][TB];
-  const int nk = (int)((a.H + KCH * KV - 1) / (KCH * KV));
-  gemm_core<T>(la, lb, 0, nk, sA, sB, acc);
+  const int nk = (int)((a.H + OpK<T>::BK - 1) / OpK<T>::BK);
+  gemm_core<T>(la, lb, 0, nk, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int vw = v0 + wm * WT, seg = vw / kSeg, half = lane >> 5;
@@ -454,7 +422,24 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
         if (full || v < a.V) mx = fmaxf(mx, s);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float msl = (mx == kNegInf ? 0.0f : mx) * kLog2e;
+    // the label logit of row c, taken from the same fp32 value that enters the row statistics;
+    // exactly one lane of the whole grid holds (v = y_c, c)
+    const unsigned rel = (unsigned)((row_ok ? a.y[c] : -1) - vw);
+    const bool mine = rel < (unsigned)WT && (int)((rel >> 2) & 1) == half;
+    if (__any(mine)) {
+      float sy = 0.0f;
+#pragma unroll
+      for (int i = 0; i < TB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (rel == (unsigned)(32 * i + 8 * (r >> 2) + 4 * half + (r & 3))) sy = acc[i][j][r];
+      if (mine) {
+        const float g = a.prm->ginv, t = sy * icap;
+        a.s_label[c] = sy;
+        a.og[c] = cap > 0.0f ? g * (1.0f - t * t) : g;
+      }
+    }
+    const float ms = mx == kNegInf ? 0.0f : mx;
     float sum = 0.0f;
     S* dst = ws + (int64_t)c * a.V_pad + vw + 4 * half;
 #pragma unroll
@@ -466,7 +451,7 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
         for (int rr = 0; rr < 4; ++rr) {
           const float s = acc[i][j][4 * g + rr];
           const int v = vw + 32 * i + 8 * g + 4 * half + rr;
-          float e = ex2(s * kLog2e - msl);
+          float e = ex2((s - ms) * kLog2e);  // exactly 1 at the segment max
           if (!full && v >= a.V) e = 0.0f;
           sum += e;
           const float t = s * icap;
@@ -492,9 +477,7 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
 // ---- grad_hidden = dZ . W ---------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
-  using S = typename Traits<T>::S;
-  __shared__ u32x4 sA[2 * TILE * KCH];
-  __shared__ u32x4 sB[2 * TILE * KCH];
+  __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes];
 
   const int mt = (a.rows + TILE - 1) / TILE, nt = (int)((a.H + TILE - 1) / TILE);
   const int t = xcd_remap(blockIdx.x, gridDim.x), per = mt * nt;
@@ -503,20 +486,16 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
   grouped(t - split * per, mt, nt, kGroupDx, tm, tn);
   const int c0 = tm * TILE, h0 = tn * TILE;
 
-  LoadDzK<T> la;
-  la.p = (const S*)a.ws + (int64_t)c0 * a.V_pad;
-  la.ld = a.V_pad;
-  la.rows = min(TILE, a.rows - c0);
-  la.scale = a.scale + (int64_t)c0 * a.nseg;
-  la.nseg = a.nseg;
-  la.init(a.y + c0, a.og + c0);
-  LoadT<T> lb{(const T*)a.W + h0, a.H, (int)a.V, (int)min<int64_t>(TILE, a.H - h0), {}};
-
+  constexpr int BK = OpK<T>::BK;
+  const int nk = (int)(a.V_pad / BK);
   const int kb = split * a.ksteps_per_split;
-  const int nk = (int)(a.V_pad / (KCH * Traits<T>::KV));
   const int ke = min(nk, kb + a.ksteps_per_split);
+  OpK<T> la;  // dZ rows of the chunk, K = v (only this split's K range is loaded)
+  la.init((const T*)a.ws + (int64_t)c0 * a.V_pad, a.V_pad, min(TILE, a.rows - c0), ke * BK);
+  OpMN<T> lb;  // W: source rows are v (K), columns h
+  lb.init((const T*)a.W + h0, a.H, (int)min<int64_t>(a.V, (int64_t)ke * BK), (int)min<int64_t>(TILE, a.H - h0));
   f32x16 acc[TB][TB];
-  gemm_core<T>(la, lb, kb, ke, sA, sB, acc);
+  gemm_core<T>(la, lb, kb, ke, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
 #pragma unroll
@@ -552,29 +531,21 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const float* part, int splits
 // ---- grad_W (+)= dZ^T . X -----------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
-  using S = typename Traits<T>::S;
-  __shared__ u32x4 sA[2 * TILE * KCH];
-  __shared__ u32x4 sB[2 * TILE * KCH];
+  __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes];
 
   const int mt = (int)((a.V + TILE - 1) / TILE), nt = (int)((a.H + TILE - 1) / TILE);
   int tm, tn;
   grouped(xcd_remap(blockIdx.x, gridDim.x), mt, nt, kGroupDw, tm, tn);
   const int v0 = tm * TILE, h0 = tn * TILE;
 
-  LoadDzT<T> la;
-  la.p = (const S*)a.ws + v0;
-  la.ld = a.V_pad;
-  la.rows = a.rows;
-  la.scale = a.scale;
-  la.nseg = a.nseg;
-  la.v0 = v0;
-  la.y = a.y;
-  la.ogp = a.og;
-  LoadT<T> lb{(const T*)a.X + h0, a.H, a.rows, (int)min<int64_t>(TILE, a.H - h0), {}};
+  OpMN<T> la;  // dZ^T: source rows are chunk rows (K), columns are v (M); v0 + 256 <= V_pad
+  la.init((const T*)a.ws + v0, a.V_pad, a.rows, TILE);
+  OpMN<T> lb;  // X: source rows are chunk rows (K), columns h
+  lb.init((const T*)a.X + h0, a.H, a.rows, (int)min<int64_t>(TILE, a.H - h0));
 
-  const int nk = (a.rows + KCH * Traits<T>::KV - 1) / (KCH * Traits<T>::KV);
+  const int nk = (a.rows + OpMN<T>::BK - 1) / OpMN<T>::BK;
   f32x16 acc[TB][TB];
-  gemm_core<T>(la, lb, 0, nk, sA, sB, acc);
+  gemm_core<T>(la, lb, 0, nk, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
 #pragma unroll
@@ -641,83 +612,59 @@ __global__ __launch_bounds__(1024) void k_prepass(const int64_t* labels, int64_t
   }
 }
 
-// Label logit per row (one wave per row): s_y = softcap(x . W[y]) and og = g * ds_y/dz_y.
+// Row merge + dlogits (one block per chunk row): lse from the segment statistics, the loss term,
+// then one sweep over the row turning q into dZ = q * g * exp(m_seg - lse) - [v == y] * og, written
+// in place in the operand type of the backward GEMMs. This is where the softmax is rebuilt from the
+// logits-derived q and the small per-row max/sum statistics.
 template <typename T>
-__global__ __launch_bounds__(256) void k_label_logit(const T* X, const T* W, const int* y32,
-                                                     const DevParams* prm, int64_t BT, int64_t H,
-                                                     float softcap, float* s_label, float* og) {
-  constexpr int KV = 16 / sizeof(T);
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (t >= BT) return;
-  const int y = y32[t];
-  if (y < 0) {
-    if (lane == 0) {
-      s_label[t] = 0.0f;
-      og[t] = 0.0f;
-    }
-    return;
-  }
-  const T* x = X + t * H;
-  const T* w = W + (int64_t)y * H;
-  float acc = 0.0f;
-  for (int64_t h = (int64_t)lane * KV; h < H; h += 64 * KV) {
-    float fx[KV], fw[KV];
-    const u32x4 vx = *(const u32x4*)(x + h), vw = *(const u32x4*)(w + h);
-    if constexpr (sizeof(T) == 2) {
-      const bf16x8 bx = __builtin_bit_cast(bf16x8, vx), bw = __builtin_bit_cast(bf16x8, vw);
-#pragma unroll
-      for (int e = 0; e < KV; ++e) {
-        fx[e] = (float)bx[e];
-        fw[e] = (float)bw[e];
-      }
-    } else {
-      const f32x4 bx = __builtin_bit_cast(f32x4, vx), bw = __builtin_bit_cast(f32x4, vw);
-#pragma unroll
-      for (int e = 0; e < KV; ++e) {
-        fx[e] = bx[e];
-        fw[e] = bw[e];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < KV; ++e) acc = fmaf(fx[e], fw[e], acc);
-  }
-  const float z = wave_sum(acc);
-  if (lane == 0) {
-    const float g = prm->ginv;
-    if (softcap > 0.0f) {
-      const float th = tanh_via_exp(z / softcap);
-      s_label[t] = softcap * th;
-      og[t] = g * (1.0f - th * th);
-    } else {
-      s_label[t] = z;
-      og[t] = g;
-    }
-  }
-}
-
-// Row merge (one wave per row): lse from the segment statistics, loss term, per-segment scale.
-__global__ __launch_bounds__(256) void k_merge(float* seg_m, const float* seg_s, int nseg, int rows,
-                                               const int* y32, const float* s_label,
-                                               const DevParams* prm, float* loss_row) {
-  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (c >= rows) return;
-  float* m = seg_m + (int64_t)c * nseg;
-  const float* s = seg_s + (int64_t)c * nseg;
+__global__ __launch_bounds__(256) void k_merge_dlogits(void* ws, const float* seg_m, const float* seg_s,
+                                                       int nseg, int64_t V_pad, const int* y32,
+                                                       const float* s_label, const float* og,
+                                                       const DevParams* prm, float* loss_row) {
+  using S = typename Traits<T>::S;
+  constexpr int KV = Traits<T>::KV;
+  __shared__ float red[4];
+  __shared__ float s_lse;
+  const int c = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* m = seg_m + (int64_t)c * nseg;
+  const float* sp = seg_s + (int64_t)c * nseg;
   float M = kNegInf;
-  for (int j = lane; j < nseg; j += 64) M = fmaxf(M, m[j]);
+  for (int j = threadIdx.x; j < nseg; j += 256) M = fmaxf(M, m[j]);
   M = wave_max(M);
-  const float Ml = M * kLog2e;
-  float S = 0.0f;
-  for (int j = lane; j < nseg; j += 64) S += s[j] * ex2(m[j] * kLog2e - Ml);
-  S = wave_sum(S);
-  const float lse = M + __logf(S);
-  const bool valid = y32[c] >= 0;
-  const float g = valid ? prm->ginv : 0.0f;
-  const float lsel = lse * kLog2e;
-  for (int j = lane; j < nseg; j += 64) m[j] = g * ex2(m[j] * kLog2e - lsel);
-  if (lane == 0) loss_row[c] = valid ? lse - s_label[c] : 0.0f;
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float Ssum = 0.0f;
+  for (int j = threadIdx.x; j < nseg; j += 256) Ssum += sp[j] * ex2((m[j] - M) * kLog2e);
+  Ssum = wave_sum(Ssum);
+  if (lane == 0) red[wave] = Ssum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float lse = M + __logf((red[0] + red[1]) + (red[2] + red[3]));
+    s_lse = lse;
+    loss_row[c] = y32[c] >= 0 ? lse - s_label[c] : 0.0f;
+  }
+  __syncthreads();
+  const int y = y32[c];
+  const float g = y >= 0 ? prm->ginv : 0.0f;
+  const float lse = s_lse;
+  const float oc = og[c];
+  S* row = (S*)ws + (int64_t)c * V_pad;
+  for (int64_t v0 = (int64_t)threadIdx.x * KV; v0 < V_pad; v0 += 256 * KV) {
+    const float sc = g * ex2((m[v0 / kSeg] - lse) * kLog2e);
+    float f[KV];
+    unpack(*(const u32x4*)(row + v0), f, (S*)nullptr);
+#pragma unroll
+    for (int e = 0; e < KV; ++e) f[e] *= sc;
+    const unsigned rel = (unsigned)(y - v0);
+    if (rel < (unsigned)KV) {
+#pragma unroll
+      for (int e = 0; e < KV; ++e) f[e] -= (rel == (unsigned)e) ? oc : 0.0f;
+    }
+    *(u32x4*)(row + v0) = pack(f, (T*)nullptr);
+  }
 }
 
 // Fixed-order loss reduction (one block).
@@ -753,18 +700,6 @@ hipError_t launch_prepass(const Problem& p, const int64_t* labels, const Work& w
   return hipGetLastError();
 }
 
-hipError_t launch_label_logit(const Problem& p, const void* hidden, const void* W, const Work& w,
-                              hipStream_t stream) {
-  const unsigned grid = (unsigned)((p.BT + 3) / 4);
-  if (p.dtype == 0)
-    k_label_logit<__bf16><<<grid, 256, 0, stream>>>((const __bf16*)hidden, (const __bf16*)W, w.y32,
-                                                    w.params, p.BT, p.H, p.softcap, w.s_label, w.og);
-  else
-    k_label_logit<float><<<grid, 256, 0, stream>>>((const float*)hidden, (const float*)W, w.y32, w.params,
-                                                   p.BT, p.H, p.softcap, w.s_label, w.og);
-  return hipGetLastError();
-}
-
 hipError_t launch_fwd(const Problem& p, const void* hidden, const void* W, const Work& w, int64_t row0,
                       int64_t rows, hipStream_t stream) {
   const size_t esz = p.dtype == 0 ? 2 : 4;
@@ -774,6 +709,10 @@ hipError_t launch_fwd(const Problem& p, const void* hidden, const void* W, const
   a.ws = w.ws_e;
   a.seg_m = w.seg_m;
   a.seg_s = w.seg_s;
+  a.y = w.y32 + row0;
+  a.s_label = w.s_label + row0;
+  a.og = w.og + row0;
+  a.prm = w.params;
   a.H = p.H;
   a.V = p.V;
   a.V_pad = p.V_pad;
@@ -789,29 +728,29 @@ hipError_t launch_fwd(const Problem& p, const void* hidden, const void* W, const
 }
 
 hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream) {
-  const unsigned grid = (unsigned)((rows + 3) / 4);
-  k_merge<<<grid, 256, 0, stream>>>(w.seg_m, w.seg_s, (int)p.nseg, (int)rows, w.y32 + row0,
-                                    w.s_label + row0, w.params, w.loss_row + row0);
+  if (p.dtype == 0)
+    k_merge_dlogits<__bf16><<<(unsigned)rows, 256, 0, stream>>>(w.ws_e, w.seg_m, w.seg_s, (int)p.nseg, p.V_pad,
+                                                              w.y32 + row0, w.s_label + row0, w.og + row0,
+                                                              w.params, w.loss_row + row0);
+  else
+    k_merge_dlogits<float><<<(unsigned)rows, 256, 0, stream>>>(w.ws_e, w.seg_m, w.seg_s, (int)p.nseg, p.V_pad,
+                                                             w.y32 + row0, w.s_label + row0, w.og + row0,
+                                                             w.params, w.loss_row + row0);
   return hipGetLastError();
 }
 
 hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_hidden, int64_t row0,
                      int64_t rows, int splits, hipStream_t stream) {
   const size_t esz = p.dtype == 0 ? 2 : 4;
-  const int kv = p.dtype == 0 ? 8 : 4;
-  const int nk = (int)(p.V_pad / (KCH * kv));
+  const int nk = (int)(p.V_pad * (p.dtype == 0 ? 2 : 4) / kStepBytes);
   DxArgs a;
   a.W = W;
   a.ws = w.ws_e;
-  a.scale = w.seg_m;
-  a.y = w.y32 + row0;
-  a.og = w.og + row0;
   a.out = (char*)grad_hidden + row0 * p.H * esz;
   a.part = w.dx_part;
   a.H = p.H;
   a.V = p.V;
   a.V_pad = p.V_pad;
-  a.nseg = (int)p.nseg;
   a.rows = (int)rows;
   a.splits = splits;
   a.ksteps_per_split = (nk + splits - 1) / splits;
@@ -842,14 +781,10 @@ hipError_t launch_dw(const Problem& p, const void* hidden, const Work& w, float*
   DwArgs a;
   a.X = (const char*)hidden + row0 * p.H * esz;
   a.ws = w.ws_e;
-  a.scale = w.seg_m;
-  a.y = w.y32 + row0;
-  a.og = w.og + row0;
   a.dW = grad_W;
   a.H = p.H;
   a.V = p.V;
   a.V_pad = p.V_pad;
-  a.nseg = (int)p.nseg;
   a.rows = (int)rows;
   a.accumulate = accumulate ? 1 : 0;
   const unsigned grid = (unsigned)(((p.V + TILE - 1) / TILE) * ((p.H + TILE - 1) / TILE));
