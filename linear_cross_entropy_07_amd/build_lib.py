@@ -9,7 +9,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-LIB = os.path.join(PKG, "libflce.so")
+# FLCE_LIB selects another build of the library (e.g. a different pipeline geometry); build() and
+# ensure_built() always refer to the in-tree default.
+DEFAULT_LIB = os.path.join(PKG, "libflce.so")
+LIB = os.environ.get("FLCE_LIB", DEFAULT_LIB)
 SOURCES = ["flce_kernels.hip", "flce_api.cpp"]
 
 # Packed fp32 VALU forms stay off: ordinary float code is left to scalar VALU instructions.
@@ -26,7 +29,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile libflce.so for gfx950 into the package directory and return its path."""
-    tmp = LIB + ".tmp"
+    tmp = DEFAULT_LIB + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", INCLUDE, "-I", CSRC,
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
@@ -34,13 +37,15 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-8000:]}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, DEFAULT_LIB)
+    return DEFAULT_LIB
 
 
 def ensure_built() -> str:
     """Return the library path, building it only if no library exists yet."""
     if not os.path.exists(LIB):
+        if LIB != DEFAULT_LIB:
+            raise FileNotFoundError(f"FLCE_LIB={LIB} does not exist")
         build()
     return LIB
 

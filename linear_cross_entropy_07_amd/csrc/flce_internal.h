@@ -11,7 +11,14 @@ namespace flce {
 constexpr int kTile = 256;      // rows/cols of every GEMM block tile
 constexpr int kSeg = 128;       // width (in V) of one row-statistics segment (one wave's M extent)
 constexpr int kRowAlign = 256;  // chunk sizes are multiples of this
-constexpr int kStepBytes = 64;  // bytes of K per GEMM pipeline step
+#ifndef FLCE_STEP_BYTES
+#define FLCE_STEP_BYTES 64
+#endif
+#ifndef FLCE_STAGES
+#define FLCE_STAGES 4
+#endif
+constexpr int kStepBytes = FLCE_STEP_BYTES;  // bytes of K per GEMM pipeline step (64 or 128)
+constexpr int kPipeStages = FLCE_STAGES;     // LDS stages of the GEMM pipeline
 
 // Per-call device parameters written by the label pre-pass and read by later kernels.
 struct DevParams {

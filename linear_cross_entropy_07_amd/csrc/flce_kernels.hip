@@ -165,25 +165,77 @@ __device__ __forceinline__ void dma16(i32x4 desc, u32 voff, u32 lds) {
                :: "v"(voff), "s"(desc), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
+// Range-checked buffer accesses for epilogues: loads outside the range return 0, stores outside it
+// are dropped, so tile edges need no branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const u32 n = bytes <= 0 ? 0u : (u32)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(n), 0x00020000);
+}
+__device__ __forceinline__ void bstore_b64(rsrc_t r, u32 off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void bstore_b128(rsrc_t r, u32 off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
+// Accumulator addressing for row-major [rows][ld] output tiles whose element (0, 0) is the buffer
+// base: a per-lane offset for each 32-column block j (kOOB past ncols) plus a wave-uniform row offset
+// for (i, r), passed as the scalar offset of the buffer instruction. All tiles here keep
+// row * ld * ESZ below 2^31, so 32-bit arithmetic is exact.
+template <int ESZ>
+struct AccAddr {
+  u32 col[TB];
+  int ld;
+  __device__ __forceinline__ AccAddr(int ld_, int ncols) : ld(ld_) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+    const int row0 = wm * WT + 4 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const int c = wn * WT + 32 * j + (lane & 31);
+      col[j] = c < ncols ? (u32)(row0 * ld + c) * (u32)ESZ : kOOB;
+    }
+  }
+  __device__ __forceinline__ u32 row(int i, int r) const {
+    return (u32)((32 * i + 8 * (r >> 2) + (r & 3)) * ld) * (u32)ESZ;
+  }
+};
+__device__ __forceinline__ float bload_f32(rsrc_t r, u32 voff, u32 soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ void bstore_f32(rsrc_t r, u32 voff, u32 soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, v), r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void bstore_b16(rsrc_t r, u32 voff, u32 soff, unsigned short v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)voff, (int)soff, 0);
+}
+
 // ---- pipeline geometry ---------------------------------------------------------------------
-// A stage holds 64 bytes of K for the 256 rows (or columns) of each operand: 16 KiB per operand.
-constexpr int kStages = 4;
-constexpr int kStageBytes = 32768;              // A + B
-constexpr int kOpBytes = 16384;
-constexpr int kDmaPerOp = kOpBytes / (NTHR * 16);  // 4 DMA instructions per thread per operand
+// A stage holds kStepBytes of K for the 256 rows (or columns) of each operand.
+constexpr int kChunks = kStepBytes / 16;           // 16-byte K chunks per row per step
+constexpr int kSub = kChunks / 2;                  // MFMA substeps per step
+constexpr int kStages = kPipeStages;
+constexpr int kOpBytes = TILE * kStepBytes;        // per operand per stage
+constexpr int kStageBytes = 2 * kOpBytes;          // A + B
+constexpr int kDmaPerOp = kOpBytes / (NTHR * 16);  // DMA instructions per thread per operand
 constexpr int kLoadsPerStage = 2 * kDmaPerOp;
+static_assert(kChunks == 4 || kChunks == 8, "64 or 128 bytes of K per step");
+static_assert(kStages >= 2 && kStages * kStageBytes <= 160 * 1024, "LDS ring must fit in 160 KiB");
 // vmcnt field encoding of s_waitcnt (gfx9): low 4 bits and bits 15:14; expcnt and lgkmcnt left at max.
 constexpr int vmcnt_only(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
 // K-contiguous operand: tile row r (an M or N index) is a source row, K runs along it. In LDS each
-// row holds 64 bytes = 4 chunks of 16 bytes, chunk kc stored at slot kc ^ ((r >> 2) & 3) so that the
-// 16 rows read at one chunk index cover all banks. A fragment is one ds_read_b128.
+// row holds kStepBytes (kChunks chunks of 16 bytes); chunk kc is stored at slot kc ^ swz(r), where
+// swz changes every 256 bytes of rows, so that 16 rows read at one chunk index cover all banks.
+// A fragment is one ds_read_b128.
 template <typename T>
 struct OpK {
-  static constexpr int KV = 16 / sizeof(T), BK = 4 * KV;
+  static constexpr int KV = 16 / sizeof(T), BK = kChunks * KV;
+  static constexpr int RPI = 1024 / kStepBytes;  // rows per DMA instruction
+  static __device__ __forceinline__ int swz(int row) { return (row / (256 / kStepBytes)) & (kChunks - 1); }
   i32x4 desc;          // rows [0, valid rows) of the tile
   u32 rowoff[kDmaPerOp];
-  int slot;            // this lane's chunk slot within its row
   int kc[kDmaPerOp];   // chunk of K this lane loads for each of its rows
   int kmax;            // valid K elements (also the end of this block's K range)
   __device__ __forceinline__ void init(const T* p, int64_t ld, int rows, int kmax_) {
@@ -192,9 +244,9 @@ struct OpK {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int q = 0; q < kDmaPerOp; ++q) {
-      const int row = 16 * (kDmaPerOp * wave + q) + (lane >> 2);
+      const int row = RPI * (kDmaPerOp * wave + q) + lane / kChunks;
       rowoff[q] = (u32)(row * ld * (int64_t)sizeof(T));
-      kc[q] = (lane & 3) ^ ((row >> 2) & 3);
+      kc[q] = (lane % kChunks) ^ swz(row);
     }
   }
   __device__ __forceinline__ void issue(int ks, u32 lds) const {
@@ -211,7 +263,7 @@ struct OpK {
 #pragma unroll
     for (int i = 0; i < TB; ++i) {
       const int row = rowbase + 32 * i + (lane & 31);
-      f[i] = *(const u32x4*)(st + row * 64 + ((kcol ^ ((row >> 2) & 3)) << 4));
+      f[i] = *(const u32x4*)(st + row * kStepBytes + ((kcol ^ swz(row)) << 4));
     }
   }
 };
@@ -223,7 +275,7 @@ struct OpK {
 // rows k0 .. k0+3 (gfx950 transpose read). fp32 fragments are four ds_read_b32.
 template <typename T>
 struct OpMN {
-  static constexpr int KV = 16 / sizeof(T), BK = 4 * KV;
+  static constexpr int KV = 16 / sizeof(T), BK = kChunks * KV;
   static constexpr int ROWB = TILE * (int)sizeof(T);  // LDS bytes per K row
   static constexpr int CPR = ROWB / 16;               // chunks per row
   static constexpr int RPI = 64 / CPR;                // rows per DMA instruction (1 KiB)
@@ -290,10 +342,10 @@ struct OpMN {
 // 32x32 MFMA result layout, lane l holds column (l % 32) and, in register r, row
 // 8 * (r / 4) + 4 * (l / 32) + r % 4 of its block.
 //
-// K is consumed in steps of 64 bytes through a ring of kStages LDS stages filled by DMA, kStages-1
-// steps ahead. A step is two substeps of 16 MFMAs; the fragments of substep 1 are read while
-// substep 0 runs, and those of the next step's substep 0 right after the step's single barrier,
-// while substep 1 runs.
+// K is consumed in steps of kStepBytes through a ring of kStages LDS stages filled by DMA, kStages-1
+// steps ahead; a step's DMA is issued at its start, into the slot the previous step read. A step is
+// kSub substeps of 16 MFMAs; the fragments of substep s+1 are read while substep s runs, and those
+// of the next step's substep 0 right after the step's single barrier, while its last substep runs.
 template <typename T, class LA, class LB>
 __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int kb, int ke, char* smem,
                                           f32x16 (&acc)[TB][TB]) {
@@ -318,28 +370,30 @@ __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int kb, in
   la.frag(smem, wm * WT, half, fa[0]);
   lb.frag(smem + kOpBytes, wn * WT, half, fb[0]);
   for (int ks = kb; ks < ke; ++ks) {
-    const int slot = (ks - kb) % kStages;
-    const char* st = smem + slot * kStageBytes;
-    la.frag(st, wm * WT, 2 + half, fa[1]);
-    lb.frag(st + kOpBytes, wn * WT, 2 + half, fb[1]);
-#pragma unroll
-    for (int i = 0; i < TB; ++i)
-#pragma unroll
-      for (int j = 0; j < TB; ++j) mma(acc[i][j], fa[0][i], fb[0][j], (T*)nullptr);
-    // refill the slot read in the previous step (every wave passed that step's barrier after its
-    // last read of it); steps past the end load zeros
-    const int nslot = (ks - kb + kStages - 1) % kStages;
+    const int t = ks - kb;
+    const char* st = smem + (t % kStages) * kStageBytes;
+    // refill the slot the previous step read (every wave passed that step's barrier after its last
+    // read of it); steps past the end load zeros
+    const int nslot = (t + kStages - 1) % kStages;
     la.issue(ks + kStages - 1, lbase + nslot * kStageBytes);
     lb.issue(ks + kStages - 1, lbase + nslot * kStageBytes + kOpBytes);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const char* nx = smem + ((ks - kb + 1) % kStages) * kStageBytes;
-    la.frag(nx, wm * WT, half, fa[0]);
-    lb.frag(nx + kOpBytes, wn * WT, half, fb[0]);
 #pragma unroll
-    for (int i = 0; i < TB; ++i)
+    for (int s = 0; s < kSub; ++s) {
+      if (s + 1 < kSub) {
+        la.frag(st, wm * WT, 2 * (s + 1) + half, fa[(s + 1) & 1]);
+        lb.frag(st + kOpBytes, wn * WT, 2 * (s + 1) + half, fb[(s + 1) & 1]);
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const char* nx = smem + ((t + 1) % kStages) * kStageBytes;
+        la.frag(nx, wm * WT, half, fa[(s + 1) & 1]);
+        lb.frag(nx + kOpBytes, wn * WT, half, fb[(s + 1) & 1]);
+      }
 #pragma unroll
-      for (int j = 0; j < TB; ++j) mma(acc[i][j], fa[1][i], fb[1][j], (T*)nullptr);
+      for (int i = 0; i < TB; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j) mma(acc[i][j], fa[s & 1][i], fb[s & 1][j], (T*)nullptr);
+    }
   }
   // drain the DMA of the steps past the end before the block's LDS can be reused or the block ends
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
@@ -378,9 +432,22 @@ struct DwArgs {
   int rows, accumulate;
 };
 
-constexpr int kGroupFwd = 16;
-constexpr int kGroupDx = 4;
-constexpr int kGroupDw = 8;
+// Tile-row group sizes of the grouped tile order. Each XCD runs 32 blocks at once; for the products
+// with M = V (logits, grad_W) a group of 2 V-tiles swept over all 16 tiles of the small operand
+// keeps the large operand's panels (W or dZ) in L2 for all their uses, so they are read from memory
+// once, while the small operand (a chunk of hidden, tens of MB) is re-read from the last-level cache.
+#ifndef FLCE_GROUP_FWD
+#define FLCE_GROUP_FWD 2
+#endif
+#ifndef FLCE_GROUP_DX
+#define FLCE_GROUP_DX 4
+#endif
+#ifndef FLCE_GROUP_DW
+#define FLCE_GROUP_DW 2
+#endif
+constexpr int kGroupFwd = FLCE_GROUP_FWD;
+constexpr int kGroupDx = FLCE_GROUP_DX;
+constexpr int kGroupDw = FLCE_GROUP_DW;
 
 // ---- forward: logits tile + softcap + segment statistics + q store -------------------------
 template <typename T>
@@ -405,7 +472,9 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
   const int vw = v0 + wm * WT, seg = vw / kSeg, half = lane >> 5;
   const bool full = vw + WT <= a.V;
   const float cap = a.softcap, icap = cap > 0.0f ? 1.0f / cap : 0.0f;
-  S* ws = (S*)a.ws;
+  // q tile: rows c0.. of the chunk (rows past the chunk are dropped), columns v0 .. v0+255 < V_pad
+  const rsrc_t rq = make_rsrc((S*)a.ws + (int64_t)c0 * a.V_pad + v0,
+                              (int64_t)min(TILE, a.rows - c0) * a.V_pad * (int64_t)sizeof(S));
 #pragma unroll
   for (int j = 0; j < TB; ++j) {
     const int c = c0 + wn * WT + 32 * j + (lane & 31);
@@ -441,7 +510,7 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
     }
     const float ms = mx == kNegInf ? 0.0f : mx;
     float sum = 0.0f;
-    S* dst = ws + (int64_t)c * a.V_pad + vw + 4 * half;
+    const u32 qrow = (u32)(((int64_t)(c - c0) * a.V_pad + wm * WT + 4 * half) * (int64_t)sizeof(S));
 #pragma unroll
     for (int i = 0; i < TB; ++i)
 #pragma unroll
@@ -457,13 +526,12 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
           const float t = s * icap;
           q[rr] = cap > 0.0f ? e * (1.0f - t * t) : e;
         }
-        if (row_ok) {
-          if constexpr (sizeof(S) == 2) {
-            f16x4 h{(S)q[0], (S)q[1], (S)q[2], (S)q[3]};
-            *(u32x2*)(dst + 32 * i + 8 * g) = __builtin_bit_cast(u32x2, h);
-          } else {
-            *(f32x4*)(dst + 32 * i + 8 * g) = f32x4{q[0], q[1], q[2], q[3]};
-          }
+        const u32 qoff = qrow + (u32)((32 * i + 8 * g) * sizeof(S));
+        if constexpr (sizeof(S) == 2) {
+          f16x4 h{(S)q[0], (S)q[1], (S)q[2], (S)q[3]};
+          bstore_b64(rq, qoff, __builtin_bit_cast(u32x2, h));
+        } else {
+          bstore_b128(rq, qoff, __builtin_bit_cast(u32x4, f32x4{q[0], q[1], q[2], q[3]}));
         }
       }
     sum += __shfl_xor(sum, 32);
@@ -497,25 +565,38 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
   f32x16 acc[TB][TB];
   gemm_core<T>(la, lb, kb, ke, smem, acc);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  // row-major [rows][H] output tile at (c0, h0); rows past the chunk and columns past H are dropped
+  const int vrows = min(TILE, a.rows - c0), ncols = (int)min<int64_t>(TILE, a.H - h0);
+  if (a.splits == 1) {
+    const rsrc_t ro = make_rsrc((T*)a.out + (int64_t)c0 * a.H + h0, ((int64_t)vrows * a.H - h0) * (int64_t)sizeof(T));
+    const AccAddr<sizeof(T)> ad((int)a.H, ncols);
 #pragma unroll
-  for (int i = 0; i < TB; ++i)
-#pragma unroll
-    for (int j = 0; j < TB; ++j) {
-      const int h = h0 + wn * WT + 32 * j + (lane & 31);
-      if (h >= a.H) continue;
+    for (int i = 0; i < TB; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int c = c0 + wm * WT + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (c >= a.rows) continue;
-        const float v = acc[i][j][r];
-        if (a.splits == 1) {
-          ((T*)a.out)[(int64_t)c * a.H + h] = (T)v;
-        } else {
-          a.part[((int64_t)split * a.rows + c) * a.H + h] = v;
+        const u32 so = ad.row(i, r);
+#pragma unroll
+        for (int j = 0; j < TB; ++j) {
+          if constexpr (sizeof(T) == 2)
+            bstore_b16(ro, ad.col[j], so, __builtin_bit_cast(unsigned short, (T)acc[i][j][r]));
+          else
+            bstore_f32(ro, ad.col[j], so, acc[i][j][r]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  } else {
+    const rsrc_t ro = make_rsrc(a.part + ((int64_t)split * a.rows + c0) * a.H + h0, ((int64_t)vrows * a.H - h0) * 4);
+    const AccAddr<4> ad((int)a.H, ncols);
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int j = 0; j < TB; ++j) bstore_f32(ro, ad.col[j], ad.row(i, r), acc[i][j][r]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 }
 
 // Fixed-order sum of the split-K partials of grad_hidden.
@@ -547,22 +628,33 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
   f32x16 acc[TB][TB];
   gemm_core<T>(la, lb, 0, nk, smem, acc);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  // row-major [V][H] fp32 tile at (v0, h0): written (first chunk) or read-modify-written (later
+  // chunks); a row block's loads are all issued before its adds and stores
+  const int vrows = (int)min<int64_t>(TILE, a.V - v0), ncols = (int)min<int64_t>(TILE, a.H - h0);
+  const rsrc_t rd = make_rsrc(a.dW + (int64_t)v0 * a.H + h0, ((int64_t)vrows * a.H - h0) * 4);
+  const AccAddr<4> ad((int)a.H, ncols);
+  if (a.accumulate) {
 #pragma unroll
-  for (int i = 0; i < TB; ++i)
+    for (int i = 0; i < TB; ++i)
 #pragma unroll
-    for (int j = 0; j < TB; ++j) {
-      const int h = h0 + wn * WT + 32 * j + (lane & 31);
-      if (h >= a.H) continue;
+      for (int j = 0; j < TB; ++j) {
+        float old[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = v0 + wm * WT + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (v >= a.V) continue;
-        float* d = a.dW + (int64_t)v * a.H + h;
-        const float val = acc[i][j][r];
-        *d = a.accumulate ? *d + val : val;
+        for (int r = 0; r < 16; ++r) old[r] = bload_f32(rd, ad.col[j], ad.row(i, r));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bstore_f32(rd, ad.col[j], ad.row(i, r), acc[i][j][r] + old[r]);
+        __builtin_amdgcn_sched_barrier(0);  // one 32x32 block of loads in flight at a time
       }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int j = 0; j < TB; ++j) bstore_f32(rd, ad.col[j], ad.row(i, r), acc[i][j][r]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  }
 }
 
 // ---- small kernels ----------------------------------------------------------------------------
