@@ -80,8 +80,8 @@ int flce_destroy(flce_handle h);
 /* Bytes of device workspace flce_forward_backward needs for this problem (host-only arithmetic, no
  * device call). h may be NULL (default configuration). The workspace holds one chunk of 16-bit
  * logits-derived values ([chunk_rows][V rounded up to 256], fp16 for FLCE_BF16, fp32 for
- * FLCE_FP32), per-(row, 128-wide V segment) statistics, per-row label data, and split-K partials
- * of grad_hidden. It never grows with BT beyond O(BT) bytes of per-row data.
+ * FLCE_FP32), per-(row, 128-wide V segment) statistics, per-row label data, split-K partials
+ * of grad_hidden and one chunk of hidden transposed. It never grows with BT beyond O(BT) bytes of per-row data.
  * Returns FLCE_OK and writes *bytes, or FLCE_ERR_INVALID_ARG. */
 int flce_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, size_t* bytes);
 
@@ -125,7 +125,7 @@ int flce_status(flce_handle h, void* stream);
  * flce_profile_begin, never inside flce_forward_backward. Returns FLCE_OK, FLCE_ERR_INVALID_ARG or
  * FLCE_ERR_HIP. */
 enum { FLCE_K_PREPASS = 0, FLCE_K_FWD = 1, FLCE_K_MERGE = 2, FLCE_K_DX = 3, FLCE_K_DX_REDUCE = 4,
-       FLCE_K_DW = 5, FLCE_K_FINALIZE = 6, FLCE_K_COUNT = 7 };
+       FLCE_K_DW = 5, FLCE_K_FINALIZE = 6, FLCE_K_TRANSPOSE = 7, FLCE_K_COUNT = 8 };
 int flce_profile_begin(flce_handle h, int max_launches);
 int flce_profile_end(flce_handle h, void* stream, double* ms_out, int64_t* count_out);
 

@@ -75,7 +75,7 @@ int dx_splits(int64_t rows, int64_t H, int64_t V_pad, int dtype) {
 }
 
 struct Layout {
-  size_t off_e, off_m, off_s, off_y, off_sl, off_og, off_loss, off_part, off_params, total;
+  size_t off_e, off_m, off_s, off_y, off_sl, off_og, off_loss, off_part, off_xt, off_params, total;
   int splits;
   int64_t chunk_rows;
 };
@@ -104,6 +104,7 @@ Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax) {
   L.off_og = take((size_t)BT * 4);
   L.off_loss = take((size_t)BT * 4);
   L.off_part = take(L.splits > 1 ? (size_t)L.splits * rows * H * 4 : 0);
+  L.off_xt = take((size_t)rows * H * esz);
   L.total = off;
   return L;
 }
@@ -235,6 +236,8 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
   w.loss_row = (float*)(base + L.off_loss);
   w.dx_part = L.splits > 1 ? (float*)(base + L.off_part) : nullptr;
   w.params = (flce::DevParams*)(base + L.off_params);
+  w.xt = base + L.off_xt;
+  w.chunk_cap = L.chunk_rows;
 
   // Each launch is optionally bracketed by a pre-created event pair (kernel timing diagnostics).
   auto run = [&](int kind, auto&& launch) -> bool {
@@ -264,7 +267,8 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
   for (int64_t ci = 0; ci < n_chunks; ++ci) {
     const int64_t row0 = ci * crows;
     const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
-    FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, hidden, W, w, row0, rows, stream));
+    FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
+    FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, stream));
     FLCE_LAUNCH(FLCE_K_MERGE, flce::launch_merge(p, w, row0, rows, stream));
     int splits = L.splits > 1 ? dx_splits(rows, H, p.V_pad, dtype) : 1;
     if (splits > L.splits) splits = L.splits;

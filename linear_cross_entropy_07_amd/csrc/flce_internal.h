@@ -38,6 +38,8 @@ struct Work {
   float* og;           // [BT] g * d s_label / d z_label (one-hot coefficient of dZ)
   float* loss_row;     // [BT]
   float* dx_part;      // [splits][chunk_rows][H] fp32 split-K partials of grad_hidden (may be null)
+  void* xt;            // [H][chunk_cap] the current chunk of hidden, transposed
+  int64_t chunk_cap;   // row capacity of one chunk (a multiple of 256)
   DevParams* params;   // in the workspace
 };
 
@@ -52,8 +54,10 @@ struct Problem {
 // Launchers (all enqueue on `stream`, return hipError_t of the launch).
 hipError_t launch_prepass(const Problem& p, const int64_t* labels, const Work& w, int* status_out,
                           hipStream_t stream);
-hipError_t launch_fwd(const Problem& p, const void* hidden, const void* W, const Work& w,
-                      int64_t row0, int64_t rows, hipStream_t stream);
+hipError_t launch_transpose(const Problem& p, const void* hidden, const Work& w, int64_t row0, int64_t rows,
+                            hipStream_t stream);
+hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t row0, int64_t rows,
+                      hipStream_t stream);
 hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream);
 hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_hidden, int64_t row0,
                      int64_t rows, int splits, hipStream_t stream);

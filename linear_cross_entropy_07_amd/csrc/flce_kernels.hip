@@ -401,7 +401,8 @@ __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int kb, in
 
 // ---- kernel arguments ------------------------------------------------------------------------
 struct FwdArgs {
-  const void* X;      // hidden, chunk row 0
+  const void* XT;     // [H][ldt]: the chunk of hidden, transposed
+  int64_t ldt;
   const void* W;
   void* ws;
   float* seg_m;
@@ -461,11 +462,13 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
   grouped(xcd_remap(blockIdx.x, gridDim.x), mt, nt, kGroupFwd, tm, tn);
   const int v0 = tm * TILE, c0 = tn * TILE;
 
-  OpK<T> la, lb;
+  OpK<T> la;   // W rows v0.., K = h contiguous
   la.init((const T*)a.W + (int64_t)v0 * a.H, a.H, (int)min<int64_t>(TILE, a.V - v0), (int)a.H);
-  lb.init((const T*)a.X + (int64_t)c0 * a.H, a.H, min(TILE, a.rows - c0), (int)a.H);
+  OpMN<T> lb;  // hidden^T: source rows are h (K), columns the chunk rows c0..
+  lb.init((const T*)a.XT + c0, a.ldt, (int)a.H, min(TILE, a.rows - c0));
   f32x16 acc[TB][TB];
   const int nk = (int)((a.H + OpK<T>::BK - 1) / OpK<T>::BK);
+  static_assert(OpK<T>::BK == OpMN<T>::BK, "operands step through K together");
   gemm_core<T>(la, lb, 0, nk, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
@@ -657,6 +660,25 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
   }
 }
 
+// ---- hidden chunk transpose: [rows][H] -> [H][ldt] through a 64 x 64 LDS tile ------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const T* X, int rows, int H, T* XT, int64_t ldt) {
+  __shared__ T tile[64][65];
+  const int r0 = blockIdx.y * 64, h0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = r0 + ty + 4 * k, h = h0 + tx;
+    tile[ty + 4 * k][tx] = (r < rows && h < H) ? X[(int64_t)r * H + h] : (T)0.0f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int h = h0 + ty + 4 * k, r = r0 + tx;
+    if (h < H && r < rows) XT[(int64_t)h * ldt + r] = tile[tx][ty + 4 * k];
+  }
+}
+
 // ---- small kernels ----------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -792,11 +814,23 @@ hipError_t launch_prepass(const Problem& p, const int64_t* labels, const Work& w
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const Problem& p, const void* hidden, const void* W, const Work& w, int64_t row0,
-                      int64_t rows, hipStream_t stream) {
-  const size_t esz = p.dtype == 0 ? 2 : 4;
+hipError_t launch_transpose(const Problem& p, const void* hidden, const Work& w, int64_t row0, int64_t rows,
+                            hipStream_t stream) {
+  const dim3 grid((unsigned)((p.H + 63) / 64), (unsigned)((rows + 63) / 64));
+  if (p.dtype == 0)
+    k_transpose<__bf16><<<grid, 256, 0, stream>>>((const __bf16*)hidden + row0 * p.H, (int)rows, (int)p.H,
+                                                  (__bf16*)w.xt, w.chunk_cap);
+  else
+    k_transpose<float><<<grid, 256, 0, stream>>>((const float*)hidden + row0 * p.H, (int)rows, (int)p.H,
+                                                 (float*)w.xt, w.chunk_cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t row0, int64_t rows,
+                      hipStream_t stream) {
   FwdArgs a;
-  a.X = (const char*)hidden + row0 * p.H * esz;
+  a.XT = w.xt;
+  a.ldt = w.chunk_cap;
   a.W = W;
   a.ws = w.ws_e;
   a.seg_m = w.seg_m;

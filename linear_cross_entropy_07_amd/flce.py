@@ -179,7 +179,7 @@ class FLCE:
         _check(rc, "flce_forward_backward")
         return loss, gh, gw
 
-    KERNELS = ("prepass", "fwd", "merge", "dx", "dx_reduce", "dw", "finalize")
+    KERNELS = ("prepass", "fwd", "merge", "dx", "dx_reduce", "dw", "finalize", "transpose")
 
     def profile_begin(self, max_launches: int = 4096):
         """Bracket every following kernel launch with HIP events on its stream (diagnostics)."""
