@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="rows of the oracle's bounded sample")
     ap.add_argument("--profile-only", action="store_true", help="warmup + steps, no extras (for rocprofv3)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for the FETCH_SIZE/WRITE_SIZE scale)")
     return ap.parse_args()
 
 
@@ -119,6 +121,13 @@ def main():
         step()
     torch.cuda.synchronize(dev)
     print(f"# warmup done, loss {float(loss):.6f}", file=sys.stderr, flush=True)
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)  # the reference dispatch: reads and writes exactly 1 GiB
+        torch.cuda.synchronize(dev)
+        del src, dst
     if args.profile_only:
         for _ in range(args.steps):
             step()
