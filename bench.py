@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_head")
     ap.add_argument("--chunk", type=int, default=0, help="chunk_rows_max (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=3072, help="rows of the oracle's bounded sample")
+    ap.add_argument("--cpu-rows", type=int, default=4608, help="rows of the oracle's bounded sample")
     ap.add_argument("--profile-only", action="store_true", help="warmup + steps, no extras (for rocprofv3)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for the FETCH_SIZE/WRITE_SIZE scale)")
