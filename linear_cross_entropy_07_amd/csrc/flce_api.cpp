@@ -20,6 +20,7 @@
 
 struct flce_ctx {
   int device;
+  int ncu;        // compute units of the device
   int64_t chunk_rows_max;
   int* d_status;  // device status word written by the label pre-pass
   // kernel timing (flce_profile_begin/end): event pairs recorded around each launch
@@ -31,15 +32,18 @@ struct flce_ctx {
 namespace {
 
 constexpr int64_t kDefaultChunk = 4096;
+constexpr int kDefaultCUs = 256;  // MI355X, for workspace sizes asked without a handle
 constexpr int64_t kMaxH = 1 << 16;
 constexpr int64_t kMaxV = int64_t(1) << 20;  // keeps every per-tile buffer range below 2 GiB
 constexpr int64_t kMaxBT = (int64_t(1) << 31) - 1;
-constexpr int kCUs = 256;
 
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
 int64_t chunk_max_of(const flce_ctx* h) {
   return h ? h->chunk_rows_max : kDefaultChunk;
+}
+int ncu_of(const flce_ctx* h) {
+  return h ? h->ncu : kDefaultCUs;
 }
 
 void plan(int64_t BT, int64_t cmax, int64_t* n, int64_t* rows) {
@@ -55,16 +59,16 @@ void plan(int64_t BT, int64_t cmax, int64_t* n, int64_t* rows) {
   *rows = c;
 }
 
-int dx_splits(int64_t rows, int64_t H, int64_t V_pad, int dtype) {
-  // Split K (= V) only when it shortens the wave-quantised schedule: with T tiles on kCUs CUs and
-  // s splits the time goes as ceil(T*s / kCUs) / s, plus a small per-split cost for the reduction.
+int dx_splits(int64_t rows, int64_t H, int64_t V_pad, int dtype, int ncu) {
+  // Split K (= V) only when it shortens the wave-quantised schedule: with T tiles on ncu CUs and
+  // s splits the time goes as ceil(T*s / ncu) / s, plus a small per-split cost for the reduction.
   const int64_t tiles = ((rows + flce::kTile - 1) / flce::kTile) * ((H + flce::kTile - 1) / flce::kTile);
   const int64_t nk = V_pad * (dtype == 0 ? 2 : 4) / flce::kStepBytes;
   int best = 1;
   double best_cost = 1e30;
   for (int s = 1; s <= 32; ++s) {
     if (s > 1 && nk / s < 16) break;  // keep at least 16 k-steps per split
-    const double waves = (double)((tiles * s + kCUs - 1) / kCUs);
+    const double waves = (double)((tiles * s + ncu - 1) / ncu);
     const double cost = waves / s + 0.02 * (s - 1);
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
@@ -80,7 +84,7 @@ struct Layout {
   int64_t chunk_rows;
 };
 
-Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax) {
+Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu) {
   Layout L{};
   int64_t n, rows;
   plan(BT, cmax, &n, &rows);
@@ -94,7 +98,7 @@ Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax) {
     return o;
   };
   L.chunk_rows = rows;
-  L.splits = rows > 0 ? dx_splits(rows, H, V_pad, dtype) : 1;
+  L.splits = rows > 0 ? dx_splits(rows, H, V_pad, dtype, ncu) : 1;
   L.off_params = take(sizeof(flce::DevParams));
   L.off_e = take((size_t)rows * V_pad * esz);
   L.off_m = take((size_t)rows * nseg * 4);
@@ -152,6 +156,9 @@ int flce_create(flce_handle* out, int device, const flce_config* cfg) {
   if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count) return FLCE_ERR_HIP;
   DeviceGuard g(device);
   if (!g.ok) return FLCE_ERR_HIP;
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || ncu <= 0)
+    return FLCE_ERR_HIP;
   int* st = nullptr;
   if (hipMalloc(&st, 256) != hipSuccess) return FLCE_ERR_HIP;
   if (hipMemset(st, 0, 256) != hipSuccess) {
@@ -160,6 +167,7 @@ int flce_create(flce_handle* out, int device, const flce_config* cfg) {
   }
   flce_ctx* h = new flce_ctx;
   h->device = device;
+  h->ncu = ncu;
   h->chunk_rows_max = cmax;
   h->d_status = st;
   *out = h;
@@ -182,7 +190,7 @@ int flce_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dty
   if (!bytes) return FLCE_ERR_INVALID_ARG;
   const int rc = check_sizes(BT, H, V, dtype);
   if (rc != FLCE_OK) return rc;
-  *bytes = layout(BT, H, V, dtype, chunk_max_of(h)).total;
+  *bytes = layout(BT, H, V, dtype, chunk_max_of(h), ncu_of(h)).total;
   return FLCE_OK;
 }
 
@@ -207,7 +215,7 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
     return FLCE_ERR_INVALID_ARG;
   if (BT > 0 && (!aligned(hidden, 16) || !aligned(labels, 8) || !aligned(grad_hidden, 16)))
     return FLCE_ERR_INVALID_ARG;
-  const Layout L = layout(BT, H, V, dtype, h->chunk_rows_max);
+  const Layout L = layout(BT, H, V, dtype, h->chunk_rows_max, h->ncu);
   if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
 
   DeviceGuard g(h->device);
@@ -224,6 +232,7 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
   p.ignore_index = ignore_index;
   p.softcap = softcap;
   p.reduction = reduction;
+  p.ncu = h->ncu;
 
   char* base = (char*)workspace;
   flce::Work w;
@@ -270,7 +279,7 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
     FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
     FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, stream));
     FLCE_LAUNCH(FLCE_K_MERGE, flce::launch_merge(p, w, row0, rows, stream));
-    int splits = L.splits > 1 ? dx_splits(rows, H, p.V_pad, dtype) : 1;
+    int splits = L.splits > 1 ? dx_splits(rows, H, p.V_pad, dtype, h->ncu) : 1;
     if (splits > L.splits) splits = L.splits;
     FLCE_LAUNCH(FLCE_K_DX, flce::launch_dx(p, W, w, grad_hidden, row0, rows, splits, stream));
     if (splits > 1)

@@ -49,6 +49,7 @@ struct Problem {
   int64_t ignore_index;
   float softcap;
   int reduction;       // 1 mean, 2 sum
+  int ncu;             // compute units of the device (sizes persistent grids)
 };
 
 // Launchers (all enqueue on `stream`, return hipError_t of the launch).

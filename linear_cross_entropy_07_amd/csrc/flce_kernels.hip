@@ -12,14 +12,15 @@
 //   k_merge_dlogits  per row: lse from the segment statistics and the loss term; then one sweep
 //             over the row rebuilds the softmax from q and turns it into dZ in place, in the operand
 //             type of the backward GEMMs. No separate softmax or dlogits tensor exists.
-//   k_dx      grad_hidden chunk = dZ . W on MFMA (W transposed in registers on its way to LDS).
-//   k_dw      grad_W (+)= dZ^T . X on MFMA; both operands are transposed in registers on the way to
-//             LDS; fp32 accumulation in place across chunks.
+//   k_dx      grad_hidden chunk = dZ . W on MFMA (W read MN-contiguous, transposed by the LDS
+//             transpose reads on its way to the matrix cores).
+//   k_dw      grad_W (+)= dZ^T . X on MFMA; both operands read MN-contiguous and transposed the same
+//             way; fp32 accumulation in place across chunks.
 //
 // One GEMM core serves the three products: 256 threads (4 waves of 64) compute a 256 x 256 tile,
 // each wave a 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (or 32x32x2f32 for
-// fp32 inputs). Operands are staged through a double-buffered, XOR-swizzled LDS tile of 128 bytes
-// of K per row; every operand reaches LDS as 16-byte K-contiguous chunks.
+// fp32 inputs). Operands reach LDS by DMA (buffer loads that write LDS directly) into a ring of
+// kStages stages of kStepBytes of K per row, XOR-swizzled against bank conflicts.
 #include "flce_internal.h"
 
 namespace flce {
@@ -51,13 +52,6 @@ template <> struct Traits<float> {
   using S = float;
   static constexpr int KV = 4;
 };
-
-__device__ __forceinline__ int swz(int row, int kc) {
-  // 8 chunks per 128-byte row; XOR with both the low and the next 3 bits of the row so that
-  // 16 consecutive rows read at one chunk index, and 8 rows 8 apart written at one chunk index,
-  // all land on distinct bank groups.
-  return (row << 3) | (kc ^ ((row ^ (row >> 3)) & 7));
-}
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -103,28 +97,6 @@ __device__ __forceinline__ u32x4 pack(const float (&f)[4], float*) {
   for (int i = 0; i < 4; ++i) v[i] = f[i];
   return __builtin_bit_cast(u32x4, v);
 }
-
-// In-register transpose of a KV x KV block: in[k] holds elements (k, n = 0..KV-1) of a row of the
-// source; out[n] receives elements (k = 0..KV-1, n). 2-byte elements: one v_perm_b32 per dword.
-__device__ __forceinline__ void transpose(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const u32 lo = in[2 * w][n >> 1], hi = in[2 * w + 1][n >> 1];
-      out[n][w] = (n & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
-                          : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-    }
-  }
-}
-__device__ __forceinline__ void transpose(const u32x4 (&in)[4], u32x4 (&out)[4]) {
-#pragma unroll
-  for (int n = 0; n < 4; ++n)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) out[n][k] = in[k][n];
-}
-
-__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 // ---- block -> tile mapping -------------------------------------------------------------------
 // Workgroups are dispatched round-robin over the 8 XCDs (block b on XCD b % 8). Give each XCD a
@@ -270,9 +242,13 @@ struct OpK {
 
 // MN-contiguous operand: a source row is one K index holding the tile's 256 M/N elements
 // contiguously. In LDS a row keeps that layout (256 * sizeof(T) bytes), 16-byte chunk c stored at
-// slot c ^ (4 * (k & 3)). bf16 fragments come from two ds_read_b64_tr_b16: in each 16-lane group,
+// slot c ^ (kMnXor * (k & 3)). bf16 fragments come from two ds_read_b64_tr_b16: in each 16-lane group,
 // lane j points at row k0 + j/4, columns nb + 4 (j % 4) .. +3, and lane i receives column nb + i of
 // rows k0 .. k0+3 (gfx950 transpose read). fp32 fragments are four ds_read_b32.
+#ifndef FLCE_MN_XOR
+#define FLCE_MN_XOR 4
+#endif
+constexpr int kMnXor = FLCE_MN_XOR;  // chunk XOR step per K row of an MN-contiguous operand in LDS
 template <typename T>
 struct OpMN {
   static constexpr int KV = 16 / sizeof(T), BK = kChunks * KV;
@@ -291,14 +267,19 @@ struct OpMN {
 #pragma unroll
     for (int q = 0; q < kDmaPerOp; ++q) {
       const int row = RPI * (kDmaPerOp * wave + q) + lane / CPR;
-      const int c = (lane % CPR) ^ (4 * (row & 3));
+      const int c = (lane % CPR) ^ (kMnXor * (row & 3));
       off[q] = c * KV < nvalid ? (u32)(row * ldb + c * 16) : kOOB;
     }
   }
-  __device__ __forceinline__ void issue(int ks, u32 lds) const {
-    const int wave = threadIdx.x >> 6, k0 = ks * BK;
+  // buffer descriptor of step ks: its BK source rows, rows past kvalid out of range
+  __device__ __forceinline__ i32x4 step_desc(int ks) const {
+    const int k0 = ks * BK;
     const int nrows = kvalid - k0 < 0 ? 0 : (kvalid - k0 > BK ? BK : kvalid - k0);
-    const i32x4 desc = make_desc(p + (int64_t)k0 * ldb, (u32)nrows * (u32)ldb);
+    return make_desc(p + (int64_t)k0 * ldb, (u32)nrows * (u32)ldb);
+  }
+  __device__ __forceinline__ void issue(int ks, u32 lds) const {
+    const int wave = threadIdx.x >> 6;
+    const i32x4 desc = step_desc(ks);
 #pragma unroll
     for (int q = 0; q < kDmaPerOp; ++q) dma16(desc, off[q], lds + (kDmaPerOp * wave + q) * 1024);
   }
@@ -312,7 +293,7 @@ struct OpMN {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int k = 4 * (2 * kcol + r) + ((lane & 15) >> 2);  // kcol = 2 s + half
-          const char* a = st + k * ROWB + (((n >> 3) ^ (4 * (k & 3))) << 4) + ((n & 7) << 1);
+          const char* a = st + k * ROWB + (((n >> 3) ^ (kMnXor * (k & 3))) << 4) + ((n & 7) << 1);
           const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) i16x4*)(size_t)lds_addr(a));
           const u32x2 w = __builtin_bit_cast(u32x2, t);
@@ -329,7 +310,7 @@ struct OpMN {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int k = 4 * kcol + e;
-          v[e] = *(const u32*)(st + k * ROWB + (((n >> 2) ^ (4 * (k & 3))) << 4) + ((n & 3) << 2));
+          v[e] = *(const u32*)(st + k * ROWB + (((n >> 2) ^ (kMnXor * (k & 3))) << 4) + ((n & 3) << 2));
         }
         f[i] = v;
       }
@@ -346,8 +327,20 @@ struct OpMN {
 // steps ahead; a step's DMA is issued at its start, into the slot the previous step read. A step is
 // kSub substeps of 16 MFMAs; the fragments of substep s+1 are read while substep s runs, and those
 // of the next step's substep 0 right after the step's single barrier, while its last substep runs.
+// Prologue: DMA of the first kStages-1 steps (no waits), so that it can be issued early, e.g. while
+// the previous tile of a persistent block is still in its epilogue.
+template <class LA, class LB>
+__device__ __forceinline__ void gemm_prologue(const LA& la, const LB& lb, int kb, char* smem) {
+  const u32 lbase = lds_addr(smem);
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st) {
+    la.issue(kb + st, lbase + st * kStageBytes);
+    lb.issue(kb + st, lbase + st * kStageBytes + kOpBytes);
+  }
+}
+
 template <typename T, class LA, class LB>
-__device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int kb, int ke, char* smem,
+__device__ __forceinline__ void gemm_main(const LA& la, const LB& lb, int kb, int ke, char* smem,
                                           f32x16 (&acc)[TB][TB]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1, half = lane >> 5;
@@ -357,13 +350,8 @@ __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int kb, in
     for (int j = 0; j < TB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  if (kb >= ke) return;
   const u32 lbase = lds_addr(smem);
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st) {
-    la.issue(kb + st, lbase + st * kStageBytes);
-    lb.issue(kb + st, lbase + st * kStageBytes + kOpBytes);
-  }
+  // any older vector-memory operations (loads and stores count alike) only make this wait stricter
   __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
   asm volatile("s_barrier" ::: "memory");
   u32x4 fa[2][TB], fb[2][TB];
@@ -395,8 +383,92 @@ __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int kb, in
         for (int j = 0; j < TB; ++j) mma(acc[i][j], fa[s & 1][i], fb[s & 1][j], (T*)nullptr);
     }
   }
-  // drain the DMA of the steps past the end before the block's LDS can be reused or the block ends
+  // the DMA of the steps past the end must land before the LDS is reused or the block ends; the
+  // barrier makes every wave finish its reads before a following prologue refills the ring
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The same pipeline with the step loop unrolled by kStages: stage slots and LDS offsets are
+// compile-time constants and the loop body has no exits. The step count is rounded up to a multiple
+// of kStages; steps past ke load zeros (out of range) and add nothing. With INTERLEAVE the scheduler
+// places one fragment read between consecutive MFMAs, so LDS requests trickle instead of queueing
+// behind the DMA writes (better for K-contiguous first operands).
+template <typename T, bool INTERLEAVE, class LA, class LB>
+__device__ __forceinline__ void gemm_main_u(const LA& la, const LB& lb, int kb, int ke, char* smem,
+                                            f32x16 (&acc)[TB][TB]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1, half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < TB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  const u32 lbase = lds_addr(smem);
+  __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
+  asm volatile("s_barrier" ::: "memory");
+  u32x4 fa[2][TB], fb[2][TB];
+  la.frag(smem, wm * WT, half, fa[0]);
+  lb.frag(smem + kOpBytes, wn * WT, half, fb[0]);
+  for (int ks0 = kb; ks0 < ke; ks0 += kStages) {
+#pragma unroll
+    for (int t = 0; t < kStages; ++t) {
+      const int ks = ks0 + t;
+      const char* st = smem + t * kStageBytes;
+      const int nslot = (t + kStages - 1) % kStages;
+      la.issue(ks + kStages - 1, lbase + nslot * kStageBytes);
+      lb.issue(ks + kStages - 1, lbase + nslot * kStageBytes + kOpBytes);
+#pragma unroll
+      for (int s = 0; s < kSub; ++s) {
+        if (s + 1 < kSub) {
+          la.frag(st, wm * WT, 2 * (s + 1) + half, fa[(s + 1) & 1]);
+          lb.frag(st + kOpBytes, wn * WT, 2 * (s + 1) + half, fb[(s + 1) & 1]);
+        } else {
+          __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          const char* nx = smem + ((t + 1) % kStages) * kStageBytes;
+          la.frag(nx, wm * WT, half, fa[(s + 1) & 1]);
+          lb.frag(nx + kOpBytes, wn * WT, half, fb[(s + 1) & 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < TB; ++i)
+#pragma unroll
+          for (int j = 0; j < TB; ++j) mma(acc[i][j], fa[s & 1][i], fb[s & 1][j], (T*)nullptr);
+        if constexpr (INTERLEAVE) {
+#pragma unroll
+          for (int q = 0; q < 3 * TB; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, TB * TB - 3 * TB, 0);
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Main-loop schedules of the GEMM core.
+enum Sched { kRolled = 0, kUnrolled = 1, kInterleaved = 2 };
+template <typename T, int SCHED, class LA, class LB>
+__device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int kb, int ke, char* smem,
+                                          f32x16 (&acc)[TB][TB]) {
+  if (kb >= ke) {
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int j = 0; j < TB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    return;
+  }
+  gemm_prologue(la, lb, kb, smem);
+  if constexpr (SCHED == kRolled)
+    gemm_main<T>(la, lb, kb, ke, smem, acc);
+  else
+    gemm_main_u<T, SCHED == kInterleaved>(la, lb, kb, ke, smem, acc);
 }
 
 // ---- kernel arguments ------------------------------------------------------------------------
@@ -446,15 +518,133 @@ struct DwArgs {
 #ifndef FLCE_GROUP_DW
 #define FLCE_GROUP_DW 2
 #endif
+// Main-loop schedule per product, measured on MI355X at the Llama-3-8B head: the interleaved
+// schedule helps the products whose first operand is K-contiguous and whose K is long (grad_hidden);
+// the plain unrolled one helps grad_W (both operands MN-contiguous).
+constexpr int kSchedFwd = kRolled;
+constexpr int kSchedDx = kInterleaved;
+constexpr int kSchedDw = kUnrolled;
 constexpr int kGroupFwd = FLCE_GROUP_FWD;
 constexpr int kGroupDx = FLCE_GROUP_DX;
 constexpr int kGroupDw = FLCE_GROUP_DW;
 
 // ---- forward: logits tile + softcap + segment statistics + q store -------------------------
+// Epilogue of one wave's 128 (v) x 128 (chunk row) quarter, specialised on the softcap (CAP) and on
+// whether the quarter crosses V (EDGE): the common case has no per-element masking at all. For each
+// 32-row block j, each lane holds column c (a chunk row) and 64 v values; the two lanes c and c+32
+// hold the two halves of the wave's 128-wide segment of row c.
+// Labels of this lane's 4 chunk rows (range-checked loads; -1 past the chunk).
+__device__ __forceinline__ void fwd_labels(const FwdArgs& a, int c0, int (&ylab)[TB]) {
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) >> 1;
+  const rsrc_t ry = make_rsrc(a.y, (int64_t)a.rows * 4);
+#pragma unroll
+  for (int j = 0; j < TB; ++j) {
+    const int c = c0 + wn * WT + 32 * j + (lane & 31);
+    const int yv = __builtin_amdgcn_raw_buffer_load_b32(ry, c * 4, 0, 0);
+    ylab[j] = c < a.rows ? yv : -1;
+  }
+}
+
+template <typename T, bool CAP, bool EDGE>
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16 (&acc)[TB][TB], int v0, int c0,
+                                             const int (&ylab)[TB]) {
+  using S = typename Traits<T>::S;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  const int vw = v0 + wm * WT, seg = vw / kSeg, half = lane >> 5;
+  const float cap = a.softcap, icap = CAP ? 1.0f / cap : 0.0f;
+  // q tile: rows c0.. of the chunk (rows past the chunk are dropped), columns v0 .. v0+255 < V_pad
+  const rsrc_t rq = make_rsrc((S*)a.ws + (int64_t)c0 * a.V_pad + v0,
+                              (int64_t)min(TILE, a.rows - c0) * a.V_pad * (int64_t)sizeof(S));
+#pragma unroll
+  for (int j = 0; j < TB; ++j) {
+    const int c = c0 + wn * WT + 32 * j + (lane & 31);
+    // softcap in place, then the segment max (4 independent chains)
+    float m4[TB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      m4[i] = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = acc[i][j][r];
+        if constexpr (CAP) {
+          s = cap * tanh_via_exp(s * icap);
+          acc[i][j][r] = s;
+        }
+        if constexpr (EDGE) {
+          const int v = vw + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+          s = v < a.V ? s : kNegInf;
+        }
+        m4[i] = fmaxf(m4[i], s);
+      }
+    }
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // the label logit of row c, taken from the same fp32 value that enters the row statistics;
+    // exactly one lane of the whole grid holds (v = y_c, c)
+    const unsigned rel = (unsigned)(ylab[j] - vw);
+    const bool mine = rel < (unsigned)WT && (int)((rel >> 2) & 1) == half;
+    if (__any(mine)) {
+      // for a lane that holds it: block i = rel / 32, register r = 4 ((rel / 8) % 4) + rel % 4
+      const int isel = (int)(rel >> 5), rsel = 4 * (int)((rel >> 3) & 3) + (int)(rel & 3);
+      float sy = 0.0f;
+#pragma unroll
+      for (int i = 0; i < TB; ++i) {
+        float t = acc[i][j][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) t = rsel == r ? acc[i][j][r] : t;
+        sy = isel == i ? t : sy;
+      }
+      if (mine) {
+        const float g = a.prm->ginv, t = sy * icap;
+        a.s_label[c] = sy;
+        a.og[c] = CAP ? g * (1.0f - t * t) : g;
+      }
+    }
+    const float ms = mx == kNegInf ? 0.0f : mx;
+    float sum4[TB];
+    const u32 qrow = (u32)(((int64_t)(c - c0) * a.V_pad + wm * WT + 4 * half) * (int64_t)sizeof(S));
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      sum4[i] = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float q[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float s = acc[i][j][4 * g + rr];
+          float e = ex2((s - ms) * kLog2e);  // exactly 1 at the segment max
+          if constexpr (EDGE) {
+            const int v = vw + 32 * i + 8 * g + 4 * half + rr;
+            e = v < a.V ? e : 0.0f;
+          }
+          sum4[i] += e;
+          if constexpr (CAP) {
+            const float t = s * icap;
+            q[rr] = e * (1.0f - t * t);
+          } else {
+            q[rr] = e;
+          }
+        }
+        const u32 qoff = qrow + (u32)((32 * i + 8 * g) * sizeof(S));
+        if constexpr (sizeof(S) == 2) {
+          f16x4 h{(S)q[0], (S)q[1], (S)q[2], (S)q[3]};
+          bstore_b64(rq, qoff, __builtin_bit_cast(u32x2, h));
+        } else {
+          bstore_b128(rq, qoff, __builtin_bit_cast(u32x4, f32x4{q[0], q[1], q[2], q[3]}));
+        }
+      }
+    }
+    float sum = (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
+    sum += __shfl_xor(sum, 32);
+    if (lane < 32 && c < a.rows) {
+      a.seg_m[(int64_t)c * a.nseg + seg] = mx;
+      a.seg_s[(int64_t)c * a.nseg + seg] = sum;
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
-  using S = typename Traits<T>::S;
-  constexpr int KV = Traits<T>::KV;
   __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes];
 
   const int mt = (int)(a.V_pad / TILE), nt = (a.rows + TILE - 1) / TILE;
@@ -466,82 +656,26 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
   la.init((const T*)a.W + (int64_t)v0 * a.H, a.H, (int)min<int64_t>(TILE, a.V - v0), (int)a.H);
   OpMN<T> lb;  // hidden^T: source rows are h (K), columns the chunk rows c0..
   lb.init((const T*)a.XT + c0, a.ldt, (int)a.H, min(TILE, a.rows - c0));
+  // the labels are loaded before the main loop, whose first wait on the operand loads covers them
+  int ylab[TB];
+  fwd_labels(a, c0, ylab);
   f32x16 acc[TB][TB];
   const int nk = (int)((a.H + OpK<T>::BK - 1) / OpK<T>::BK);
   static_assert(OpK<T>::BK == OpMN<T>::BK, "operands step through K together");
-  gemm_core<T>(la, lb, 0, nk, smem, acc);
+  gemm_core<T, kSchedFwd>(la, lb, 0, nk, smem, acc);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
-  const int vw = v0 + wm * WT, seg = vw / kSeg, half = lane >> 5;
-  const bool full = vw + WT <= a.V;
-  const float cap = a.softcap, icap = cap > 0.0f ? 1.0f / cap : 0.0f;
-  // q tile: rows c0.. of the chunk (rows past the chunk are dropped), columns v0 .. v0+255 < V_pad
-  const rsrc_t rq = make_rsrc((S*)a.ws + (int64_t)c0 * a.V_pad + v0,
-                              (int64_t)min(TILE, a.rows - c0) * a.V_pad * (int64_t)sizeof(S));
-#pragma unroll
-  for (int j = 0; j < TB; ++j) {
-    const int c = c0 + wn * WT + 32 * j + (lane & 31);
-    const bool row_ok = c < a.rows;
-    float mx = kNegInf;
-#pragma unroll
-    for (int i = 0; i < TB; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = acc[i][j][r];
-        if (cap > 0.0f) s = cap * tanh_via_exp(s * icap);
-        acc[i][j][r] = s;
-        const int v = vw + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (full || v < a.V) mx = fmaxf(mx, s);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // the label logit of row c, taken from the same fp32 value that enters the row statistics;
-    // exactly one lane of the whole grid holds (v = y_c, c)
-    const unsigned rel = (unsigned)((row_ok ? a.y[c] : -1) - vw);
-    const bool mine = rel < (unsigned)WT && (int)((rel >> 2) & 1) == half;
-    if (__any(mine)) {
-      float sy = 0.0f;
-#pragma unroll
-      for (int i = 0; i < TB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (rel == (unsigned)(32 * i + 8 * (r >> 2) + 4 * half + (r & 3))) sy = acc[i][j][r];
-      if (mine) {
-        const float g = a.prm->ginv, t = sy * icap;
-        a.s_label[c] = sy;
-        a.og[c] = cap > 0.0f ? g * (1.0f - t * t) : g;
-      }
-    }
-    const float ms = mx == kNegInf ? 0.0f : mx;
-    float sum = 0.0f;
-    const u32 qrow = (u32)(((int64_t)(c - c0) * a.V_pad + wm * WT + 4 * half) * (int64_t)sizeof(S));
-#pragma unroll
-    for (int i = 0; i < TB; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float q[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float s = acc[i][j][4 * g + rr];
-          const int v = vw + 32 * i + 8 * g + 4 * half + rr;
-          float e = ex2((s - ms) * kLog2e);  // exactly 1 at the segment max
-          if (!full && v >= a.V) e = 0.0f;
-          sum += e;
-          const float t = s * icap;
-          q[rr] = cap > 0.0f ? e * (1.0f - t * t) : e;
-        }
-        const u32 qoff = qrow + (u32)((32 * i + 8 * g) * sizeof(S));
-        if constexpr (sizeof(S) == 2) {
-          f16x4 h{(S)q[0], (S)q[1], (S)q[2], (S)q[3]};
-          bstore_b64(rq, qoff, __builtin_bit_cast(u32x2, h));
-        } else {
-          bstore_b128(rq, qoff, __builtin_bit_cast(u32x4, f32x4{q[0], q[1], q[2], q[3]}));
-        }
-      }
-    sum += __shfl_xor(sum, 32);
-    if (lane < 32 && row_ok) {
-      a.seg_m[(int64_t)c * a.nseg + seg] = mx;
-      a.seg_s[(int64_t)c * a.nseg + seg] = sum;
-    }
+  // wave-uniform selection of the specialised epilogue
+  const bool edge = v0 + (((int)threadIdx.x >> 6) & 1) * WT + WT > a.V;
+  if (a.softcap > 0.0f) {
+    if (edge)
+      fwd_epilogue<T, true, true>(a, acc, v0, c0, ylab);
+    else
+      fwd_epilogue<T, true, false>(a, acc, v0, c0, ylab);
+  } else {
+    if (edge)
+      fwd_epilogue<T, false, true>(a, acc, v0, c0, ylab);
+    else
+      fwd_epilogue<T, false, false>(a, acc, v0, c0, ylab);
   }
 }
 
@@ -566,7 +700,7 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
   OpMN<T> lb;  // W: source rows are v (K), columns h
   lb.init((const T*)a.W + h0, a.H, (int)min<int64_t>(a.V, (int64_t)ke * BK), (int)min<int64_t>(TILE, a.H - h0));
   f32x16 acc[TB][TB];
-  gemm_core<T>(la, lb, kb, ke, smem, acc);
+  gemm_core<T, kSchedDx>(la, lb, kb, ke, smem, acc);
 
   // row-major [rows][H] output tile at (c0, h0); rows past the chunk and columns past H are dropped
   const int vrows = min(TILE, a.rows - c0), ncols = (int)min<int64_t>(TILE, a.H - h0);
@@ -629,7 +763,7 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
 
   const int nk = (a.rows + OpMN<T>::BK - 1) / OpMN<T>::BK;
   f32x16 acc[TB][TB];
-  gemm_core<T>(la, lb, 0, nk, smem, acc);
+  gemm_core<T, kSchedDw>(la, lb, 0, nk, smem, acc);
 
   // row-major [V][H] fp32 tile at (v0, h0): written (first chunk) or read-modify-written (later
   // chunks); a row block's loads are all issued before its adds and stores
@@ -637,17 +771,27 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
   const rsrc_t rd = make_rsrc(a.dW + (int64_t)v0 * a.H + h0, ((int64_t)vrows * a.H - h0) * 4);
   const AccAddr<4> ad((int)a.H, ncols);
   if (a.accumulate) {
+    // software pipeline over the 16 blocks b = (i, j): the loads of block b + kAhead are issued
+    // before block b is added and stored, so kAhead blocks of loads cover the memory latency
+    constexpr int kAhead = 2, kNB = TB * TB;
+    float old[kAhead + 1][16];
 #pragma unroll
-    for (int i = 0; i < TB; ++i)
+    for (int b = 0; b < kAhead; ++b)
 #pragma unroll
-      for (int j = 0; j < TB; ++j) {
-        float old[16];
+      for (int r = 0; r < 16; ++r) old[b][r] = bload_f32(rd, ad.col[b % TB], ad.row(b / TB, r));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) old[r] = bload_f32(rd, ad.col[j], ad.row(i, r));
+    for (int b = 0; b < kNB; ++b) {
+      if (b + kAhead < kNB) {
+        const int bn = b + kAhead;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) bstore_f32(rd, ad.col[j], ad.row(i, r), acc[i][j][r] + old[r]);
-        __builtin_amdgcn_sched_barrier(0);  // one 32x32 block of loads in flight at a time
+        for (int r = 0; r < 16; ++r) old[bn % (kAhead + 1)][r] = bload_f32(rd, ad.col[bn % TB], ad.row(bn / TB, r));
       }
+      const int i = b / TB, j = b % TB;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        bstore_f32(rd, ad.col[j], ad.row(i, r), acc[i][j][r] + old[b % (kAhead + 1)][r]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < TB; ++i) {
