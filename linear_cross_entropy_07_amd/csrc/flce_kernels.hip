@@ -881,6 +881,7 @@ __global__ __launch_bounds__(256) void k_merge_dlogits(void* ws, const float* se
                                                        const DevParams* prm, float* loss_row) {
   using S = typename Traits<T>::S;
   constexpr int KV = Traits<T>::KV;
+  extern __shared__ float sc_seg[];  // [nseg]: g * exp(m_seg - lse)
   __shared__ float red[4];
   __shared__ float s_lse;
   const int c = blockIdx.x;
@@ -908,20 +909,29 @@ __global__ __launch_bounds__(256) void k_merge_dlogits(void* ws, const float* se
   const int y = y32[c];
   const float g = y >= 0 ? prm->ginv : 0.0f;
   const float lse = s_lse;
+  for (int j = threadIdx.x; j < nseg; j += 256) sc_seg[j] = g * ex2((m[j] - lse) * kLog2e);
+  __syncthreads();
   const float oc = og[c];
-  S* row = (S*)ws + (int64_t)c * V_pad;
-  for (int64_t v0 = (int64_t)threadIdx.x * KV; v0 < V_pad; v0 += 256 * KV) {
-    const float sc = g * ex2((m[v0 / kSeg] - lse) * kLog2e);
-    float f[KV];
-    unpack(*(const u32x4*)(row + v0), f, (S*)nullptr);
+  // one sweep over the row, four 16-byte chunks per thread in flight; range-checked accesses make
+  // the tail branch-free (loads past the row read zeros, stores past it are dropped)
+  const int nch = (int)(V_pad / KV);
+  const rsrc_t rr = make_rsrc((S*)ws + (int64_t)c * V_pad, V_pad * (int64_t)sizeof(S));
+  for (int base = threadIdx.x; base < nch; base += 4 * 256) {
+    u32x4 v[4];
 #pragma unroll
-    for (int e = 0; e < KV; ++e) f[e] *= sc;
-    const unsigned rel = (unsigned)(y - v0);
-    if (rel < (unsigned)KV) {
+    for (int u = 0; u < 4; ++u)
+      v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (base + 256 * u) * 16, 0, 0));
 #pragma unroll
-      for (int e = 0; e < KV; ++e) f[e] -= (rel == (unsigned)e) ? oc : 0.0f;
+    for (int u = 0; u < 4; ++u) {
+      const int q = base + 256 * u, v0 = q * KV;
+      const float sc = sc_seg[min(v0 / kSeg, nseg - 1)];
+      float f[KV];
+      unpack(v[u], f, (S*)nullptr);
+      const unsigned rel = (unsigned)(y - v0);
+#pragma unroll
+      for (int e = 0; e < KV; ++e) f[e] = f[e] * sc - (rel == (unsigned)e ? oc : 0.0f);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pack(f, (T*)nullptr)), rr, q * 16, 0, 0);
     }
-    *(u32x4*)(row + v0) = pack(f, (T*)nullptr);
   }
 }
 
@@ -999,11 +1009,11 @@ hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t ro
 
 hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream) {
   if (p.dtype == 0)
-    k_merge_dlogits<__bf16><<<(unsigned)rows, 256, 0, stream>>>(w.ws_e, w.seg_m, w.seg_s, (int)p.nseg, p.V_pad,
+    k_merge_dlogits<__bf16><<<(unsigned)rows, 256, (size_t)p.nseg * 4, stream>>>(w.ws_e, w.seg_m, w.seg_s, (int)p.nseg, p.V_pad,
                                                               w.y32 + row0, w.s_label + row0, w.og + row0,
                                                               w.params, w.loss_row + row0);
   else
-    k_merge_dlogits<float><<<(unsigned)rows, 256, 0, stream>>>(w.ws_e, w.seg_m, w.seg_s, (int)p.nseg, p.V_pad,
+    k_merge_dlogits<float><<<(unsigned)rows, 256, (size_t)p.nseg * 4, stream>>>(w.ws_e, w.seg_m, w.seg_s, (int)p.nseg, p.V_pad,
                                                              w.y32 + row0, w.s_label + row0, w.og + row0,
                                                              w.params, w.loss_row + row0);
   return hipGetLastError();
