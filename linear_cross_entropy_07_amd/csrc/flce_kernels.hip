@@ -545,20 +545,19 @@ __device__ __forceinline__ void fwd_labels(const FwdArgs& a, int c0, int (&ylab)
   }
 }
 
-template <typename T, bool CAP, bool EDGE>
-__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16 (&acc)[TB][TB], int v0, int c0,
-                                             const int (&ylab)[TB]) {
+template <typename T, bool CAP, bool EDGE, int J0, int JG>
+__device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc)[TB][TB], int v0, int c0,
+                                                  const int (&ylab)[TB]) {
   using S = typename Traits<T>::S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int vw = v0 + wm * WT, seg = vw / kSeg, half = lane >> 5;
   const float cap = a.softcap, icap = CAP ? 1.0f / cap : 0.0f;
-  // q tile: rows c0.. of the chunk (rows past the chunk are dropped), columns v0 .. v0+255 < V_pad
-  const rsrc_t rq = make_rsrc((S*)a.ws + (int64_t)c0 * a.V_pad + v0,
-                              (int64_t)min(TILE, a.rows - c0) * a.V_pad * (int64_t)sizeof(S));
+  // Row blocks J0 .. J0+JG-1. They are independent; each phase runs over all of them so that the
+  // single wave per SIMD has independent work (and the cross-half exchanges are in flight together).
+  // Phase 1: softcap in place and the maxima (4 chains per j).
+  float mx[TB] = {};
 #pragma unroll
-  for (int j = 0; j < TB; ++j) {
-    const int c = c0 + wn * WT + 32 * j + (lane & 31);
-    // softcap in place, then the segment max (4 independent chains)
+  for (int j = J0; j < J0 + JG; ++j) {
     float m4[TB];
 #pragma unroll
     for (int i = 0; i < TB; ++i) {
@@ -577,32 +576,27 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16 (&acc)[TB]
         m4[i] = fmaxf(m4[i], s);
       }
     }
-    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // the label logit of row c, taken from the same fp32 value that enters the row statistics;
-    // exactly one lane of the whole grid holds (v = y_c, c)
-    const unsigned rel = (unsigned)(ylab[j] - vw);
-    const bool mine = rel < (unsigned)WT && (int)((rel >> 2) & 1) == half;
-    if (__any(mine)) {
-      // for a lane that holds it: block i = rel / 32, register r = 4 ((rel / 8) % 4) + rel % 4
-      const int isel = (int)(rel >> 5), rsel = 4 * (int)((rel >> 3) & 3) + (int)(rel & 3);
-      float sy = 0.0f;
+    mx[j] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+  }
+  // Phase 2: the two lanes c and c + 32 hold the two halves of a row's 128-wide segment.
+  {
+    float o[TB];
 #pragma unroll
-      for (int i = 0; i < TB; ++i) {
-        float t = acc[i][j][0];
+    for (int j = J0; j < J0 + JG; ++j) o[j] = __shfl_xor(mx[j], 32);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) t = rsel == r ? acc[i][j][r] : t;
-        sy = isel == i ? t : sy;
-      }
-      if (mine) {
-        const float g = a.prm->ginv, t = sy * icap;
-        a.s_label[c] = sy;
-        a.og[c] = CAP ? g * (1.0f - t * t) : g;
-      }
-    }
-    const float ms = mx == kNegInf ? 0.0f : mx;
-    float sum4[TB];
+    for (int j = J0; j < J0 + JG; ++j) mx[j] = fmaxf(mx[j], o[j]);
+  }
+  // Phase 3: q = exp(s - segment max) (times the softcap derivative) to the workspace, and the sums.
+  // q tile: rows c0.. of the chunk (rows past the chunk are dropped), columns v0 .. v0+255 < V_pad
+  const rsrc_t rq = make_rsrc((S*)a.ws + (int64_t)c0 * a.V_pad + v0,
+                              (int64_t)min(TILE, a.rows - c0) * a.V_pad * (int64_t)sizeof(S));
+  float sum[TB] = {};
+#pragma unroll
+  for (int j = J0; j < J0 + JG; ++j) {
+    const int c = c0 + wn * WT + 32 * j + (lane & 31);
+    const float ms = mx[j] == kNegInf ? 0.0f : mx[j];
     const u32 qrow = (u32)(((int64_t)(c - c0) * a.V_pad + wm * WT + 4 * half) * (int64_t)sizeof(S));
+    float sum4[TB];
 #pragma unroll
     for (int i = 0; i < TB; ++i) {
       sum4[i] = 0.0f;
@@ -634,13 +628,55 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16 (&acc)[TB]
         }
       }
     }
-    float sum = (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
-    sum += __shfl_xor(sum, 32);
-    if (lane < 32 && c < a.rows) {
-      a.seg_m[(int64_t)c * a.nseg + seg] = mx;
-      a.seg_s[(int64_t)c * a.nseg + seg] = sum;
+    sum[j] = (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
+  }
+  // Phase 4: segment statistics of the tile's rows.
+  {
+    float o[TB];
+#pragma unroll
+    for (int j = J0; j < J0 + JG; ++j) o[j] = __shfl_xor(sum[j], 32);
+#pragma unroll
+    for (int j = J0; j < J0 + JG; ++j) {
+      const int c = c0 + wn * WT + 32 * j + (lane & 31);
+      if (lane < 32 && c < a.rows) {
+        a.seg_m[(int64_t)c * a.nseg + seg] = mx[j];
+        a.seg_s[(int64_t)c * a.nseg + seg] = sum[j] + o[j];
+      }
     }
   }
+  // Phase 5: the label logit of row c, taken from the same fp32 value that entered the row
+  // statistics; exactly one lane of the whole grid holds (v = y_c, c).
+#pragma unroll
+  for (int j = J0; j < J0 + JG; ++j) {
+    const unsigned rel = (unsigned)(ylab[j] - vw);
+    const bool mine = rel < (unsigned)WT && (int)((rel >> 2) & 1) == half;
+    if (__any(mine)) {
+      // for a lane that holds it: block i = rel / 32, register r = 4 ((rel / 8) % 4) + rel % 4
+      const int isel = (int)(rel >> 5), rsel = 4 * (int)((rel >> 3) & 3) + (int)(rel & 3);
+      float sy = 0.0f;
+#pragma unroll
+      for (int i = 0; i < TB; ++i) {
+        float t = acc[i][j][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) t = rsel == r ? acc[i][j][r] : t;
+        sy = isel == i ? t : sy;
+      }
+      if (mine) {
+        const int c = c0 + wn * WT + 32 * j + (lane & 31);
+        const float g = a.prm->ginv, t = sy * icap;
+        a.s_label[c] = sy;
+        a.og[c] = CAP ? g * (1.0f - t * t) : g;
+      }
+    }
+  }
+}
+
+template <typename T, bool CAP, bool EDGE>
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16 (&acc)[TB][TB], int v0, int c0,
+                                             const int (&ylab)[TB]) {
+  // two row blocks at a time: enough independent work, few enough live values to stay in registers
+  fwd_epilogue_part<T, CAP, EDGE, 0, 2>(a, acc, v0, c0, ylab);
+  fwd_epilogue_part<T, CAP, EDGE, 2, 2>(a, acc, v0, c0, ylab);
 }
 
 template <typename T>
