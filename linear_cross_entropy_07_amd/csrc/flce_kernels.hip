@@ -36,10 +36,20 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int NTHR = 256;        // threads per GEMM block
+// GEMM block: a 256 x 256 output tile split over NW waves as 2 (M) x NW/2 (N). With 8 waves each
+// wave owns 128 x 64 (128 accumulator registers) and two waves share each SIMD, which doubles the
+// LDS request rate a SIMD sustains; with 4 waves each owns 128 x 128 (256 accumulators).
+#ifndef FLCE_WAVES
+#define FLCE_WAVES 8
+#endif
+constexpr int NW = FLCE_WAVES;
+constexpr int NTHR = 64 * NW;    // threads per GEMM block
 constexpr int TILE = kTile;      // 256
-constexpr int WT = TILE / 2;     // wave tile (128)
-constexpr int TB = WT / 32;      // 32x32 MFMA blocks per wave tile side (4)
+constexpr int WM = TILE / 2;     // wave tile rows (M): 128, one 128-wide V segment in the logits GEMM
+constexpr int WN = TILE / (NW / 2);  // wave tile columns (N): 64 or 128
+constexpr int TBM = WM / 32;     // 32x32 MFMA blocks per wave tile along M (4)
+constexpr int TBN = WN / 32;     // ... along N (2 or 4)
+static_assert(NW == 4 || NW == 8, "4 or 8 waves per GEMM block");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -158,14 +168,14 @@ __device__ __forceinline__ void bstore_b128(rsrc_t r, u32 off, u32x4 v) {
 // row * ld * ESZ below 2^31, so 32-bit arithmetic is exact.
 template <int ESZ>
 struct AccAddr {
-  u32 col[TB];
+  u32 col[TBN];
   int ld;
   __device__ __forceinline__ AccAddr(int ld_, int ncols) : ld(ld_) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
-    const int row0 = wm * WT + 4 * (lane >> 5);
+    const int row0 = wm * WM + 4 * (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < TB; ++j) {
-      const int c = wn * WT + 32 * j + (lane & 31);
+    for (int j = 0; j < TBN; ++j) {
+      const int c = wn * WN + 32 * j + (lane & 31);
       col[j] = c < ncols ? (u32)(row0 * ld + c) * (u32)ESZ : kOOB;
     }
   }
@@ -230,10 +240,12 @@ struct OpK {
     }
   }
   // fragment of rows rowbase + 32 i + lane % 32 for chunk kcol
-  __device__ __forceinline__ void frag(const char* st, int rowbase, int kcol, u32x4 (&f)[TB]) const {
+  static constexpr int kFragReads = 1;  // LDS reads per 32-row fragment
+  template <int NB>
+  __device__ __forceinline__ void frag(const char* st, int rowbase, int kcol, u32x4 (&f)[NB]) const {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < TB; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const int row = rowbase + 32 * i + (lane & 31);
       f[i] = *(const u32x4*)(st + row * kStepBytes + ((kcol ^ swz(row)) << 4));
     }
@@ -283,11 +295,13 @@ struct OpMN {
 #pragma unroll
     for (int q = 0; q < kDmaPerOp; ++q) dma16(desc, off[q], lds + (kDmaPerOp * wave + q) * 1024);
   }
-  __device__ __forceinline__ void frag(const char* st, int colbase, int kcol, u32x4 (&f)[TB]) const {
+  static constexpr int kFragReads = sizeof(T) == 2 ? 2 : 4;  // LDS reads per 32-column fragment
+  template <int NB>
+  __device__ __forceinline__ void frag(const char* st, int colbase, int kcol, u32x4 (&f)[NB]) const {
     const int lane = threadIdx.x & 63;
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int i = 0; i < TB; ++i) {
+      for (int i = 0; i < NB; ++i) {
         const int n = colbase + 32 * i + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
         u32x4 v;
 #pragma unroll
@@ -304,7 +318,7 @@ struct OpMN {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < TB; ++i) {
+      for (int i = 0; i < NB; ++i) {
         const int n = colbase + 32 * i + (lane & 31);
         u32x4 v;
 #pragma unroll
@@ -341,22 +355,22 @@ __device__ __forceinline__ void gemm_prologue(const LA& la, const LB& lb, int kb
 
 template <typename T, class LA, class LB>
 __device__ __forceinline__ void gemm_main(const LA& la, const LB& lb, int kb, int ke, char* smem,
-                                          f32x16 (&acc)[TB][TB]) {
+                                          f32x16 (&acc)[TBM][TBN]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1, half = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < TB; ++i)
+  for (int i = 0; i < TBM; ++i)
 #pragma unroll
-    for (int j = 0; j < TB; ++j)
+    for (int j = 0; j < TBN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   const u32 lbase = lds_addr(smem);
   // any older vector-memory operations (loads and stores count alike) only make this wait stricter
   __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
   asm volatile("s_barrier" ::: "memory");
-  u32x4 fa[2][TB], fb[2][TB];
-  la.frag(smem, wm * WT, half, fa[0]);
-  lb.frag(smem + kOpBytes, wn * WT, half, fb[0]);
+  u32x4 fa[2][TBM], fb[2][TBN];
+  la.frag(smem, wm * WM, half, fa[0]);
+  lb.frag(smem + kOpBytes, wn * WN, half, fb[0]);
   for (int ks = kb; ks < ke; ++ks) {
     const int t = ks - kb;
     const char* st = smem + (t % kStages) * kStageBytes;
@@ -368,19 +382,19 @@ __device__ __forceinline__ void gemm_main(const LA& la, const LB& lb, int kb, in
 #pragma unroll
     for (int s = 0; s < kSub; ++s) {
       if (s + 1 < kSub) {
-        la.frag(st, wm * WT, 2 * (s + 1) + half, fa[(s + 1) & 1]);
-        lb.frag(st + kOpBytes, wn * WT, 2 * (s + 1) + half, fb[(s + 1) & 1]);
+        la.frag(st, wm * WM, 2 * (s + 1) + half, fa[(s + 1) & 1]);
+        lb.frag(st + kOpBytes, wn * WN, 2 * (s + 1) + half, fb[(s + 1) & 1]);
       } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         const char* nx = smem + ((t + 1) % kStages) * kStageBytes;
-        la.frag(nx, wm * WT, half, fa[(s + 1) & 1]);
-        lb.frag(nx + kOpBytes, wn * WT, half, fb[(s + 1) & 1]);
+        la.frag(nx, wm * WM, half, fa[(s + 1) & 1]);
+        lb.frag(nx + kOpBytes, wn * WN, half, fb[(s + 1) & 1]);
       }
 #pragma unroll
-      for (int i = 0; i < TB; ++i)
+      for (int i = 0; i < TBM; ++i)
 #pragma unroll
-        for (int j = 0; j < TB; ++j) mma(acc[i][j], fa[s & 1][i], fb[s & 1][j], (T*)nullptr);
+        for (int j = 0; j < TBN; ++j) mma(acc[i][j], fa[s & 1][i], fb[s & 1][j], (T*)nullptr);
     }
   }
   // the DMA of the steps past the end must land before the LDS is reused or the block ends; the
@@ -396,21 +410,21 @@ __device__ __forceinline__ void gemm_main(const LA& la, const LB& lb, int kb, in
 // behind the DMA writes (better for K-contiguous first operands).
 template <typename T, bool INTERLEAVE, class LA, class LB>
 __device__ __forceinline__ void gemm_main_u(const LA& la, const LB& lb, int kb, int ke, char* smem,
-                                            f32x16 (&acc)[TB][TB]) {
+                                            f32x16 (&acc)[TBM][TBN]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1, half = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < TB; ++i)
+  for (int i = 0; i < TBM; ++i)
 #pragma unroll
-    for (int j = 0; j < TB; ++j)
+    for (int j = 0; j < TBN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   const u32 lbase = lds_addr(smem);
   __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
   asm volatile("s_barrier" ::: "memory");
-  u32x4 fa[2][TB], fb[2][TB];
-  la.frag(smem, wm * WT, half, fa[0]);
-  lb.frag(smem + kOpBytes, wn * WT, half, fb[0]);
+  u32x4 fa[2][TBM], fb[2][TBN];
+  la.frag(smem, wm * WM, half, fa[0]);
+  lb.frag(smem + kOpBytes, wn * WN, half, fb[0]);
   for (int ks0 = kb; ks0 < ke; ks0 += kStages) {
 #pragma unroll
     for (int t = 0; t < kStages; ++t) {
@@ -422,26 +436,29 @@ __device__ __forceinline__ void gemm_main_u(const LA& la, const LB& lb, int kb, 
 #pragma unroll
       for (int s = 0; s < kSub; ++s) {
         if (s + 1 < kSub) {
-          la.frag(st, wm * WT, 2 * (s + 1) + half, fa[(s + 1) & 1]);
-          lb.frag(st + kOpBytes, wn * WT, 2 * (s + 1) + half, fb[(s + 1) & 1]);
+          la.frag(st, wm * WM, 2 * (s + 1) + half, fa[(s + 1) & 1]);
+          lb.frag(st + kOpBytes, wn * WN, 2 * (s + 1) + half, fb[(s + 1) & 1]);
         } else {
           __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           const char* nx = smem + ((t + 1) % kStages) * kStageBytes;
-          la.frag(nx, wm * WT, half, fa[(s + 1) & 1]);
-          lb.frag(nx + kOpBytes, wn * WT, half, fb[(s + 1) & 1]);
+          la.frag(nx, wm * WM, half, fa[(s + 1) & 1]);
+          lb.frag(nx + kOpBytes, wn * WN, half, fb[(s + 1) & 1]);
         }
 #pragma unroll
-        for (int i = 0; i < TB; ++i)
+        for (int i = 0; i < TBM; ++i)
 #pragma unroll
-          for (int j = 0; j < TB; ++j) mma(acc[i][j], fa[s & 1][i], fb[s & 1][j], (T*)nullptr);
+          for (int j = 0; j < TBN; ++j) mma(acc[i][j], fa[s & 1][i], fb[s & 1][j], (T*)nullptr);
         if constexpr (INTERLEAVE) {
+          constexpr int nr = TBM * LA::kFragReads + TBN * LB::kFragReads, nm = TBM * TBN;
+          constexpr int np = nr < nm ? nr : nm;
 #pragma unroll
-          for (int q = 0; q < 3 * TB; ++q) {
+          for (int q = 0; q < np; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, TB * TB - 3 * TB, 0);
+          if constexpr (nm > np) __builtin_amdgcn_sched_group_barrier(0x008, nm - np, 0);
+          if constexpr (nr > np) __builtin_amdgcn_sched_group_barrier(0x100, nr - np, 0);
         }
       }
     }
@@ -454,12 +471,12 @@ __device__ __forceinline__ void gemm_main_u(const LA& la, const LB& lb, int kb, 
 enum Sched { kRolled = 0, kUnrolled = 1, kInterleaved = 2 };
 template <typename T, int SCHED, class LA, class LB>
 __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int kb, int ke, char* smem,
-                                          f32x16 (&acc)[TB][TB]) {
+                                          f32x16 (&acc)[TBM][TBN]) {
   if (kb >= ke) {
 #pragma unroll
-    for (int i = 0; i < TB; ++i)
+    for (int i = 0; i < TBM; ++i)
 #pragma unroll
-      for (int j = 0; j < TB; ++j)
+      for (int j = 0; j < TBN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     return;
@@ -534,33 +551,33 @@ constexpr int kGroupDw = FLCE_GROUP_DW;
 // 32-row block j, each lane holds column c (a chunk row) and 64 v values; the two lanes c and c+32
 // hold the two halves of the wave's 128-wide segment of row c.
 // Labels of this lane's 4 chunk rows (range-checked loads; -1 past the chunk).
-__device__ __forceinline__ void fwd_labels(const FwdArgs& a, int c0, int (&ylab)[TB]) {
+__device__ __forceinline__ void fwd_labels(const FwdArgs& a, int c0, int (&ylab)[TBN]) {
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) >> 1;
   const rsrc_t ry = make_rsrc(a.y, (int64_t)a.rows * 4);
 #pragma unroll
-  for (int j = 0; j < TB; ++j) {
-    const int c = c0 + wn * WT + 32 * j + (lane & 31);
+  for (int j = 0; j < TBN; ++j) {
+    const int c = c0 + wn * WN + 32 * j + (lane & 31);
     const int yv = __builtin_amdgcn_raw_buffer_load_b32(ry, c * 4, 0, 0);
     ylab[j] = c < a.rows ? yv : -1;
   }
 }
 
 template <typename T, bool CAP, bool EDGE, int J0, int JG>
-__device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc)[TB][TB], int v0, int c0,
-                                                  const int (&ylab)[TB]) {
+__device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc)[TBM][TBN], int v0, int c0,
+                                                  const int (&ylab)[TBN]) {
   using S = typename Traits<T>::S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
-  const int vw = v0 + wm * WT, seg = vw / kSeg, half = lane >> 5;
+  const int vw = v0 + wm * WM, seg = vw / kSeg, half = lane >> 5;
   const float cap = a.softcap, icap = CAP ? 1.0f / cap : 0.0f;
   // Row blocks J0 .. J0+JG-1. They are independent; each phase runs over all of them so that the
   // single wave per SIMD has independent work (and the cross-half exchanges are in flight together).
   // Phase 1: softcap in place and the maxima (4 chains per j).
-  float mx[TB] = {};
+  float mx[TBN] = {};
 #pragma unroll
   for (int j = J0; j < J0 + JG; ++j) {
-    float m4[TB];
+    float m4[TBM];
 #pragma unroll
-    for (int i = 0; i < TB; ++i) {
+    for (int i = 0; i < TBM; ++i) {
       m4[i] = kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -580,7 +597,7 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
   }
   // Phase 2: the two lanes c and c + 32 hold the two halves of a row's 128-wide segment.
   {
-    float o[TB];
+    float o[TBN];
 #pragma unroll
     for (int j = J0; j < J0 + JG; ++j) o[j] = __shfl_xor(mx[j], 32);
 #pragma unroll
@@ -590,15 +607,15 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
   // q tile: rows c0.. of the chunk (rows past the chunk are dropped), columns v0 .. v0+255 < V_pad
   const rsrc_t rq = make_rsrc((S*)a.ws + (int64_t)c0 * a.V_pad + v0,
                               (int64_t)min(TILE, a.rows - c0) * a.V_pad * (int64_t)sizeof(S));
-  float sum[TB] = {};
+  float sum[TBN] = {};
 #pragma unroll
   for (int j = J0; j < J0 + JG; ++j) {
-    const int c = c0 + wn * WT + 32 * j + (lane & 31);
+    const int c = c0 + wn * WN + 32 * j + (lane & 31);
     const float ms = mx[j] == kNegInf ? 0.0f : mx[j];
-    const u32 qrow = (u32)(((int64_t)(c - c0) * a.V_pad + wm * WT + 4 * half) * (int64_t)sizeof(S));
-    float sum4[TB];
+    const u32 qrow = (u32)(((int64_t)(c - c0) * a.V_pad + wm * WM + 4 * half) * (int64_t)sizeof(S));
+    float sum4[TBM];
 #pragma unroll
-    for (int i = 0; i < TB; ++i) {
+    for (int i = 0; i < TBM; ++i) {
       sum4[i] = 0.0f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -632,12 +649,12 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
   }
   // Phase 4: segment statistics of the tile's rows.
   {
-    float o[TB];
+    float o[TBN];
 #pragma unroll
     for (int j = J0; j < J0 + JG; ++j) o[j] = __shfl_xor(sum[j], 32);
 #pragma unroll
     for (int j = J0; j < J0 + JG; ++j) {
-      const int c = c0 + wn * WT + 32 * j + (lane & 31);
+      const int c = c0 + wn * WN + 32 * j + (lane & 31);
       if (lane < 32 && c < a.rows) {
         a.seg_m[(int64_t)c * a.nseg + seg] = mx[j];
         a.seg_s[(int64_t)c * a.nseg + seg] = sum[j] + o[j];
@@ -649,20 +666,20 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
 #pragma unroll
   for (int j = J0; j < J0 + JG; ++j) {
     const unsigned rel = (unsigned)(ylab[j] - vw);
-    const bool mine = rel < (unsigned)WT && (int)((rel >> 2) & 1) == half;
+    const bool mine = rel < (unsigned)WM && (int)((rel >> 2) & 1) == half;
     if (__any(mine)) {
       // for a lane that holds it: block i = rel / 32, register r = 4 ((rel / 8) % 4) + rel % 4
       const int isel = (int)(rel >> 5), rsel = 4 * (int)((rel >> 3) & 3) + (int)(rel & 3);
       float sy = 0.0f;
 #pragma unroll
-      for (int i = 0; i < TB; ++i) {
+      for (int i = 0; i < TBM; ++i) {
         float t = acc[i][j][0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) t = rsel == r ? acc[i][j][r] : t;
         sy = isel == i ? t : sy;
       }
       if (mine) {
-        const int c = c0 + wn * WT + 32 * j + (lane & 31);
+        const int c = c0 + wn * WN + 32 * j + (lane & 31);
         const float g = a.prm->ginv, t = sy * icap;
         a.s_label[c] = sy;
         a.og[c] = CAP ? g * (1.0f - t * t) : g;
@@ -672,11 +689,11 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
 }
 
 template <typename T, bool CAP, bool EDGE>
-__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16 (&acc)[TB][TB], int v0, int c0,
-                                             const int (&ylab)[TB]) {
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16 (&acc)[TBM][TBN], int v0, int c0,
+                                             const int (&ylab)[TBN]) {
   // two row blocks at a time: enough independent work, few enough live values to stay in registers
   fwd_epilogue_part<T, CAP, EDGE, 0, 2>(a, acc, v0, c0, ylab);
-  fwd_epilogue_part<T, CAP, EDGE, 2, 2>(a, acc, v0, c0, ylab);
+  if constexpr (TBN > 2) fwd_epilogue_part<T, CAP, EDGE, 2, 2>(a, acc, v0, c0, ylab);
 }
 
 template <typename T>
@@ -693,15 +710,15 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
   OpMN<T> lb;  // hidden^T: source rows are h (K), columns the chunk rows c0..
   lb.init((const T*)a.XT + c0, a.ldt, (int)a.H, min(TILE, a.rows - c0));
   // the labels are loaded before the main loop, whose first wait on the operand loads covers them
-  int ylab[TB];
+  int ylab[TBN];
   fwd_labels(a, c0, ylab);
-  f32x16 acc[TB][TB];
+  f32x16 acc[TBM][TBN];
   const int nk = (int)((a.H + OpK<T>::BK - 1) / OpK<T>::BK);
   static_assert(OpK<T>::BK == OpMN<T>::BK, "operands step through K together");
   gemm_core<T, kSchedFwd>(la, lb, 0, nk, smem, acc);
 
   // wave-uniform selection of the specialised epilogue
-  const bool edge = v0 + (((int)threadIdx.x >> 6) & 1) * WT + WT > a.V;
+  const bool edge = v0 + (((int)threadIdx.x >> 6) & 1) * WM + WM > a.V;
   if (a.softcap > 0.0f) {
     if (edge)
       fwd_epilogue<T, true, true>(a, acc, v0, c0, ylab);
@@ -735,7 +752,7 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
   la.init((const T*)a.ws + (int64_t)c0 * a.V_pad, a.V_pad, min(TILE, a.rows - c0), ke * BK);
   OpMN<T> lb;  // W: source rows are v (K), columns h
   lb.init((const T*)a.W + h0, a.H, (int)min<int64_t>(a.V, (int64_t)ke * BK), (int)min<int64_t>(TILE, a.H - h0));
-  f32x16 acc[TB][TB];
+  f32x16 acc[TBM][TBN];
   gemm_core<T, kSchedDx>(la, lb, kb, ke, smem, acc);
 
   // row-major [rows][H] output tile at (c0, h0); rows past the chunk and columns past H are dropped
@@ -744,12 +761,12 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
     const rsrc_t ro = make_rsrc((T*)a.out + (int64_t)c0 * a.H + h0, ((int64_t)vrows * a.H - h0) * (int64_t)sizeof(T));
     const AccAddr<sizeof(T)> ad((int)a.H, ncols);
 #pragma unroll
-    for (int i = 0; i < TB; ++i) {
+    for (int i = 0; i < TBM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const u32 so = ad.row(i, r);
 #pragma unroll
-        for (int j = 0; j < TB; ++j) {
+        for (int j = 0; j < TBN; ++j) {
           if constexpr (sizeof(T) == 2)
             bstore_b16(ro, ad.col[j], so, __builtin_bit_cast(unsigned short, (T)acc[i][j][r]));
           else
@@ -762,11 +779,11 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
     const rsrc_t ro = make_rsrc(a.part + ((int64_t)split * a.rows + c0) * a.H + h0, ((int64_t)vrows * a.H - h0) * 4);
     const AccAddr<4> ad((int)a.H, ncols);
 #pragma unroll
-    for (int i = 0; i < TB; ++i) {
+    for (int i = 0; i < TBM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
 #pragma unroll
-        for (int j = 0; j < TB; ++j) bstore_f32(ro, ad.col[j], ad.row(i, r), acc[i][j][r]);
+        for (int j = 0; j < TBN; ++j) bstore_f32(ro, ad.col[j], ad.row(i, r), acc[i][j][r]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -798,7 +815,7 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
   lb.init((const T*)a.X + h0, a.H, a.rows, (int)min<int64_t>(TILE, a.H - h0));
 
   const int nk = (a.rows + OpMN<T>::BK - 1) / OpMN<T>::BK;
-  f32x16 acc[TB][TB];
+  f32x16 acc[TBM][TBN];
   gemm_core<T, kSchedDw>(la, lb, 0, nk, smem, acc);
 
   // row-major [V][H] fp32 tile at (v0, h0): written (first chunk) or read-modify-written (later
@@ -809,20 +826,20 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
   if (a.accumulate) {
     // software pipeline over the 16 blocks b = (i, j): the loads of block b + kAhead are issued
     // before block b is added and stored, so kAhead blocks of loads cover the memory latency
-    constexpr int kAhead = 2, kNB = TB * TB;
+    constexpr int kAhead = 2, kNB = TBM * TBN;
     float old[kAhead + 1][16];
 #pragma unroll
     for (int b = 0; b < kAhead; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) old[b][r] = bload_f32(rd, ad.col[b % TB], ad.row(b / TB, r));
+      for (int r = 0; r < 16; ++r) old[b][r] = bload_f32(rd, ad.col[b % TBN], ad.row(b / TBN, r));
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       if (b + kAhead < kNB) {
         const int bn = b + kAhead;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) old[bn % (kAhead + 1)][r] = bload_f32(rd, ad.col[bn % TB], ad.row(bn / TB, r));
+        for (int r = 0; r < 16; ++r) old[bn % (kAhead + 1)][r] = bload_f32(rd, ad.col[bn % TBN], ad.row(bn / TBN, r));
       }
-      const int i = b / TB, j = b % TB;
+      const int i = b / TBN, j = b % TBN;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         bstore_f32(rd, ad.col[j], ad.row(i, r), acc[i][j][r] + old[b % (kAhead + 1)][r]);
@@ -830,11 +847,11 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < TB; ++i) {
+    for (int i = 0; i < TBM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
 #pragma unroll
-        for (int j = 0; j < TB; ++j) bstore_f32(rd, ad.col[j], ad.row(i, r), acc[i][j][r]);
+        for (int j = 0; j < TBN; ++j) bstore_f32(rd, ad.col[j], ad.row(i, r), acc[i][j][r]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
