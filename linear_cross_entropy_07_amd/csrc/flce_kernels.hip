@@ -522,25 +522,35 @@ struct DwArgs {
   int rows, accumulate;
 };
 
-// Tile-row group sizes of the grouped tile order. Each XCD runs 32 blocks at once; for the products
-// with M = V (logits, grad_W) a group of 2 V-tiles swept over all 16 tiles of the small operand
-// keeps the large operand's panels (W or dZ) in L2 for all their uses, so they are read from memory
-// once, while the small operand (a chunk of hidden, tens of MB) is re-read from the last-level cache.
+// Tile-row group sizes of the grouped tile order (measured on MI355X at the Llama-3-8B head). Each
+// XCD runs 32 blocks at once; for the products with M = V (logits, grad_W) a group of 4 V-tiles
+// swept over the tiles of the small operand (a chunk of hidden) halves the small operand's re-reads
+// from the last-level cache against groups of 2, while the large operand's panels (W or dZ) stay in
+// the XCD's L2 for the round that uses them.
 #ifndef FLCE_GROUP_FWD
-#define FLCE_GROUP_FWD 2
+#define FLCE_GROUP_FWD 4
 #endif
 #ifndef FLCE_GROUP_DX
 #define FLCE_GROUP_DX 4
 #endif
 #ifndef FLCE_GROUP_DW
-#define FLCE_GROUP_DW 2
+#define FLCE_GROUP_DW 4
 #endif
-// Main-loop schedule per product, measured on MI355X at the Llama-3-8B head: the interleaved
-// schedule helps the products whose first operand is K-contiguous and whose K is long (grad_hidden);
-// the plain unrolled one helps grad_W (both operands MN-contiguous).
-constexpr int kSchedFwd = kRolled;
-constexpr int kSchedDx = kInterleaved;
-constexpr int kSchedDw = kUnrolled;
+// Main-loop schedule per product (0 rolled, 1 unrolled, 2 unrolled with one fragment read between
+// consecutive MFMAs); with two waves per SIMD the interleaved schedule measured best for all three
+// products on MI355X at the Llama-3-8B head.
+#ifndef FLCE_SCHED_FWD
+#define FLCE_SCHED_FWD 2
+#endif
+#ifndef FLCE_SCHED_DX
+#define FLCE_SCHED_DX 2
+#endif
+#ifndef FLCE_SCHED_DW
+#define FLCE_SCHED_DW 2
+#endif
+constexpr int kSchedFwd = FLCE_SCHED_FWD;
+constexpr int kSchedDx = FLCE_SCHED_DX;
+constexpr int kSchedDw = FLCE_SCHED_DW;
 constexpr int kGroupFwd = FLCE_GROUP_FWD;
 constexpr int kGroupDx = FLCE_GROUP_DX;
 constexpr int kGroupDw = FLCE_GROUP_DW;
