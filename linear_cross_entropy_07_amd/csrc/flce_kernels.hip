@@ -572,9 +572,17 @@ __device__ __forceinline__ void fwd_labels(const FwdArgs& a, int c0, int (&ylab)
   }
 }
 
+// q tiles of 16-bit values are staged through the (then idle) LDS ring and written out as whole
+// 128-byte lines; the accumulator layout alone gives 8-byte pieces of 32 different rows per store.
+template <typename T>
+constexpr bool kStageQ = sizeof(typename Traits<T>::S) == 2 && kStages * kStageBytes >= TILE * TILE * 2;
+__device__ __forceinline__ u32 qlds(int cl, int vl) {  // byte address of q(cl, vl) in the staged tile
+  return (u32)(cl * (TILE * 2) + (((vl >> 3) ^ (cl & 31)) << 4) + ((vl & 7) << 1));
+}
+
 template <typename T, bool CAP, bool EDGE, int J0, int JG>
 __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc)[TBM][TBN], int v0, int c0,
-                                                  const int (&ylab)[TBN]) {
+                                                  const int (&ylab)[TBN], char* smem) {
   using S = typename Traits<T>::S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int vw = v0 + wm * WM, seg = vw / kSeg, half = lane >> 5;
@@ -647,7 +655,10 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
           }
         }
         const u32 qoff = qrow + (u32)((32 * i + 8 * g) * sizeof(S));
-        if constexpr (sizeof(S) == 2) {
+        if constexpr (kStageQ<T>) {
+          f16x4 h{(S)q[0], (S)q[1], (S)q[2], (S)q[3]};
+          *(u32x2*)(smem + qlds(c - c0, wm * WM + 32 * i + 8 * g + 4 * half)) = __builtin_bit_cast(u32x2, h);
+        } else if constexpr (sizeof(S) == 2) {
           f16x4 h{(S)q[0], (S)q[1], (S)q[2], (S)q[3]};
           bstore_b64(rq, qoff, __builtin_bit_cast(u32x2, h));
         } else {
@@ -700,10 +711,26 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
 
 template <typename T, bool CAP, bool EDGE>
 __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16 (&acc)[TBM][TBN], int v0, int c0,
-                                             const int (&ylab)[TBN]) {
+                                             const int (&ylab)[TBN], char* smem) {
   // two row blocks at a time: enough independent work, few enough live values to stay in registers
-  fwd_epilogue_part<T, CAP, EDGE, 0, 2>(a, acc, v0, c0, ylab);
-  if constexpr (TBN > 2) fwd_epilogue_part<T, CAP, EDGE, 2, 2>(a, acc, v0, c0, ylab);
+  fwd_epilogue_part<T, CAP, EDGE, 0, 2>(a, acc, v0, c0, ylab, smem);
+  if constexpr (TBN > 2) fwd_epilogue_part<T, CAP, EDGE, 2, 2>(a, acc, v0, c0, ylab, smem);
+}
+
+// Staged q tile -> workspace: 32 threads per 512-byte row, each one 16-byte chunk; rows past the
+// chunk are dropped by the range-checked store.
+template <typename T>
+__device__ __forceinline__ void fwd_store_staged(const FwdArgs& a, int v0, int c0, const char* smem) {
+  using S = typename Traits<T>::S;
+  const rsrc_t rq = make_rsrc((S*)a.ws + (int64_t)c0 * a.V_pad + v0,
+                              (int64_t)min(TILE, a.rows - c0) * a.V_pad * (int64_t)sizeof(S));
+  const int t = threadIdx.x, ch = t & 31;
+  constexpr int kRowsPerPass = NTHR / 32;
+#pragma unroll 4
+  for (int row = t >> 5; row < TILE; row += kRowsPerPass) {
+    const u32x4 v = *(const u32x4*)(smem + row * (TILE * 2) + ((ch ^ (row & 31)) << 4));
+    bstore_b128(rq, (u32)((int64_t)row * a.V_pad * (int64_t)sizeof(S)) + (u32)(ch * 16), v);
+  }
 }
 
 template <typename T>
@@ -731,14 +758,18 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
   const bool edge = v0 + (((int)threadIdx.x >> 6) & 1) * WM + WM > a.V;
   if (a.softcap > 0.0f) {
     if (edge)
-      fwd_epilogue<T, true, true>(a, acc, v0, c0, ylab);
+      fwd_epilogue<T, true, true>(a, acc, v0, c0, ylab, smem);
     else
-      fwd_epilogue<T, true, false>(a, acc, v0, c0, ylab);
+      fwd_epilogue<T, true, false>(a, acc, v0, c0, ylab, smem);
   } else {
     if (edge)
-      fwd_epilogue<T, false, true>(a, acc, v0, c0, ylab);
+      fwd_epilogue<T, false, true>(a, acc, v0, c0, ylab, smem);
     else
-      fwd_epilogue<T, false, false>(a, acc, v0, c0, ylab);
+      fwd_epilogue<T, false, false>(a, acc, v0, c0, ylab, smem);
+  }
+  if constexpr (kStageQ<T>) {
+    __syncthreads();
+    fwd_store_staged<T>(a, v0, c0, smem);
   }
 }
 
