@@ -22,6 +22,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "FLCE fwd+bwd tokens/sec at H=4096,V=128256 bf16; % bf16 MFMA peak; peak bytes"
+METRIC_FWD = "FLCE forward-only tokens/sec (flce_forward, no gradients); % bf16 MFMA peak; peak bytes"
 PEAK_BF16 = 2.5e15          # dense bf16 MFMA, MI355X published
 PEAK_HBM = 8.0e12
 
@@ -36,6 +37,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4608, help="rows of the oracle's bounded sample")
     ap.add_argument("--profile-only", action="store_true", help="warmup + steps, no extras (for rocprofv3)")
+    ap.add_argument("--mode", choices=("fwd_bwd", "forward"), default="fwd_bwd",
+                    help="fwd_bwd: the fused forward + backward (default); forward: flce_forward only")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for the FETCH_SIZE/WRITE_SIZE scale)")
     return ap.parse_args()
@@ -58,7 +61,7 @@ def traffic_from_profiles(kernel: str, launches_bytes_key: str = "bytes_per_laun
     return d.get(launches_bytes_key)
 
 
-def cpu_baseline(w, X, W, y, rows: int):
+def cpu_baseline(w, X, W, y, rows: int, forward_only: bool = False):
     """The oracle as it stands, on the first `rows` rows of the same workload (bounded sample)."""
     import numpy as np
 
@@ -72,11 +75,15 @@ def cpu_baseline(w, X, W, y, rows: int):
         threads = len(os.sched_getaffinity(0))
     Xs, ys = X[:rows], y[:rows]
     t0 = time.perf_counter()
-    oracle.flce_forward_backward(Xs, W, ys, -100, w.softcap, w.reduction)
+    if forward_only:
+        oracle.flce_forward(Xs, W, ys, -100, w.softcap, w.reduction)
+    else:
+        oracle.flce_forward_backward(Xs, W, ys, -100, w.softcap, w.reduction)
     dt = time.perf_counter() - t0
     return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {rows} of {w.BT} rows of {w.name} (full H={w.H}, V={w.V}), fp64 numpy/OpenBLAS "
-                      f"forward+backward incl. widening inputs to fp64; {dt:.2f} s"}
+                      f"{'forward' if forward_only else 'forward+backward'} incl. widening inputs to fp64; "
+                      f"{dt:.2f} s"}
 
 
 def main():
@@ -108,14 +115,22 @@ def main():
     loss = torch.empty((), dtype=torch.float32, device=dev)
     gh = torch.empty_like(Xd)
     gw = torch.empty((V, H), dtype=torch.float32, device=dev)
-    ws_bytes = eng.workspace_size(BT, H, V, Xd.dtype)
+    fwd_only = args.mode == "forward"
+    if fwd_only:
+        del gh, gw
+        ws_bytes = flce.forward_workspace_size(BT, H, V, Xd.dtype, eng.handle)
+    else:
+        ws_bytes = eng.workspace_size(BT, H, V, Xd.dtype)
     torch.cuda.synchronize(dev)
     io_alloc = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def step():
-        eng.forward_backward(Xd, Wd, yd, -100, w.softcap, w.reduction, out=(loss, gh, gw), workspace=ws)
+        if fwd_only:
+            loss.copy_(eng.forward(Xd, Wd, yd, -100, w.softcap, w.reduction, workspace=ws))
+        else:
+            eng.forward_backward(Xd, Wd, yd, -100, w.softcap, w.reduction, out=(loss, gh, gw), workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -157,7 +172,7 @@ def main():
     kt = eng.profile_end(stream)
     print(f"# kernel ms/launch: " + ", ".join(f"{k} {v[0] / max(v[1], 1):.3f}x{v[1] // args.steps}"
                                             for k, v in kt.items() if v[1]), file=sys.stderr, flush=True)
-    gemm = {k: kt[k] for k in ("fwd", "dx", "dw")}
+    gemm = {k: kt[k] for k in (("fwd",) if fwd_only else ("fwd", "dx", "dw"))}
     dom = max(gemm, key=lambda k: gemm[k][0])
     dom_ms = gemm[dom][0] / gemm[dom][1]
     flops_per_launch = 2.0 * chunk_rows * H * V  # one GEMM of a full chunk: 2*C*H*V
@@ -166,9 +181,9 @@ def main():
     achieved = flops_per_launch / (dom_ms * 1e-3)
 
     tokens_per_s = BT / (ms_med * 1e-3)
-    step_flops = 6.0 * BT * H * V
+    step_flops = (2.0 if fwd_only else 6.0) * BT * H * V
     out = {
-        "metric": METRIC,
+        "metric": METRIC_FWD if fwd_only else METRIC,
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -189,15 +204,16 @@ def main():
         "peak_bytes": {"workspace": ws_bytes, "max_allocated_beyond_io": int(peak_extra),
                        "inputs_outputs": int(io_alloc - base_alloc),
                        "full_bf16_logits_not_allocated": BT * V * 2},
+        "mode": args.mode,
         "kernels_ms_per_launch": {k: round(v[0] / v[1], 4) for k, v in kt.items() if v[1]},
         "roofline": {"kernel": f"k_{dom}", "bound": "mfma", "achieved": round(achieved / 1e12, 2),
                      "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
-                     "traffic": traffic_from_profiles(dom),
+                     "traffic": None if fwd_only else traffic_from_profiles(dom),
                      "flops_per_launch": flops_per_launch},
     }
     if not args.no_cpu_baseline:
         print(f"# timing the oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, X, W, y, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(w, X, W, y, args.cpu_rows, fwd_only)
     print(json.dumps(out), flush=True)
 
 

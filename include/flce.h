@@ -48,8 +48,9 @@ typedef struct flce_ctx* flce_handle;
 /* Element type of hidden, W and grad_hidden. grad_W is always fp32 (it is the accumulator). */
 typedef enum { FLCE_BF16 = 0, FLCE_FP32 = 1 } flce_dtype;
 
-/* Loss reduction. Per-row output (reduction 'none') is not part of this boundary. */
-typedef enum { FLCE_MEAN = 1, FLCE_SUM = 2 } flce_reduction;
+/* Loss reduction. FLCE_NONE (per-row losses) is offered by flce_forward only: the fused forward +
+ * backward assumes a scalar upstream gradient. */
+typedef enum { FLCE_NONE = 0, FLCE_MEAN = 1, FLCE_SUM = 2 } flce_reduction;
 
 /* Return codes. */
 enum {
@@ -97,7 +98,8 @@ int flce_chunk_plan(flce_handle h, int64_t BT, int64_t* n_chunks, int64_t* chunk
  *   BT >= 0, 0 < H <= 65536 with H % 8 == 0, 0 < V <= 2^20 (larger sizes: FLCE_ERR_UNSUPPORTED)
  *   dtype        FLCE_BF16 or FLCE_FP32
  *   softcap      0 = off, > 0 = cap; negative or NaN is FLCE_ERR_INVALID_ARG
- *   reduction    FLCE_MEAN or FLCE_SUM (dLoss/dloss = 1 is assumed; scale the grads for other upstream grads)
+ *   reduction    FLCE_MEAN or FLCE_SUM (dLoss/dloss = 1 is assumed; scale the grads for other upstream
+ *                grads); FLCE_NONE is FLCE_ERR_UNSUPPORTED here (see flce_forward)
  *   loss         device, 1 float (written)
  *   grad_hidden  device, [BT][H] of dtype (overwritten)
  *   grad_W       device, [V][H] fp32 (overwritten)
@@ -113,19 +115,46 @@ int flce_forward_backward(flce_handle h,
                           float* loss, void* grad_hidden, float* grad_W,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* Synchronise `stream` and report the status word of the last flce_forward_backward on it:
+/* Bytes of device workspace flce_forward needs (host-only arithmetic; h may be NULL). The forward
+ * path keeps no logits: the workspace holds the per-(row, 128-wide V segment) statistics of one
+ * chunk, per-row label data and one chunk of hidden transposed. Returns FLCE_OK or
+ * FLCE_ERR_INVALID_ARG / FLCE_ERR_UNSUPPORTED for sizes flce_forward rejects. */
+int flce_forward_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, size_t* bytes);
+
+/* Forward only (evaluation, per-row verification): the loss of the same model as
+ * flce_forward_backward without any gradient, and optionally the per-row terms.
+ *   hidden, W, labels, BT, H, V, dtype, ignore_index, softcap   as for flce_forward_backward
+ *   reduction    FLCE_MEAN or FLCE_SUM (loss required), or FLCE_NONE (loss_rows required)
+ *   loss         device, 1 float (written for MEAN/SUM; may be NULL for NONE)
+ *   loss_rows    device, [BT] float or NULL (required for FLCE_NONE when BT > 0): row t gets
+ *                lse_t - s_t[label_t] (the NLL term of the
+ *                PR #126348 description), 0 where the label is ignore_index or out of range
+ *   lse_rows     device, [BT] float or NULL: row t gets lse_t = log sum_v exp(s_tv), for every row
+ *   workspace    device, >= flce_forward_workspace_size bytes, 256-byte aligned; contents are scratch
+ *   stream       a hipStream_t (NULL = the null stream)
+ * The loss and the per-row terms are bitwise those of flce_forward_backward on the same inputs.
+ * Labels outside [0, V) that are not ignore_index are flagged as for flce_forward_backward. Never
+ * allocates or synchronises. Returns FLCE_OK or an error code before enqueueing. */
+int flce_forward(flce_handle h,
+                 const void* hidden, const void* W, const int64_t* labels,
+                 int64_t BT, int64_t H, int64_t V, int dtype,
+                 int64_t ignore_index, float softcap, int reduction,
+                 float* loss, float* loss_rows, float* lse_rows,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Synchronise `stream` and report the status word of the last flce_forward_backward or flce_forward on it:
  * FLCE_OK, or FLCE_ERR_LABEL_RANGE if some label was outside [0, V) and not ignore_index. */
 int flce_status(flce_handle h, void* stream);
 
 /* Kernel timing (diagnostics). Between flce_profile_begin and flce_profile_end, every kernel that
- * flce_forward_backward enqueues on the handle is bracketed by a pair of HIP events recorded on the
+ * flce_forward_backward or flce_forward enqueues on the handle is bracketed by a pair of HIP events recorded on the
  * same stream, for at most max_launches launches. flce_profile_end synchronises `stream`, writes for
  * each kernel kind k (FLCE_K_*) the summed duration in ms_out[k] and the launch count in count_out[k]
  * (arrays of FLCE_K_COUNT entries, host memory), and releases the events. Events are created in
  * flce_profile_begin, never inside flce_forward_backward. Returns FLCE_OK, FLCE_ERR_INVALID_ARG or
  * FLCE_ERR_HIP. */
 enum { FLCE_K_PREPASS = 0, FLCE_K_FWD = 1, FLCE_K_MERGE = 2, FLCE_K_DX = 3, FLCE_K_DX_REDUCE = 4,
-       FLCE_K_DW = 5, FLCE_K_FINALIZE = 6, FLCE_K_TRANSPOSE = 7, FLCE_K_COUNT = 8 };
+       FLCE_K_DW = 5, FLCE_K_FINALIZE = 6, FLCE_K_TRANSPOSE = 7, FLCE_K_ROWS = 8, FLCE_K_COUNT = 9 };
 int flce_profile_begin(flce_handle h, int max_launches);
 int flce_profile_end(flce_handle h, void* stream, double* ms_out, int64_t* count_out);
 

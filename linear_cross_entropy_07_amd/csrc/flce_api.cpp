@@ -84,7 +84,9 @@ struct Layout {
   int64_t chunk_rows;
 };
 
-Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu) {
+// Workspace carving. The forward-only path (backward = false) needs no q/dZ chunk and no split-K
+// partials.
+Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu, bool backward = true) {
   Layout L{};
   int64_t n, rows;
   plan(BT, cmax, &n, &rows);
@@ -98,9 +100,9 @@ Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu
     return o;
   };
   L.chunk_rows = rows;
-  L.splits = rows > 0 ? dx_splits(rows, H, V_pad, dtype, ncu) : 1;
+  L.splits = backward && rows > 0 ? dx_splits(rows, H, V_pad, dtype, ncu) : 1;
   L.off_params = take(sizeof(flce::DevParams));
-  L.off_e = take((size_t)rows * V_pad * esz);
+  L.off_e = take(backward ? (size_t)rows * V_pad * esz : 0);
   L.off_m = take((size_t)rows * nseg * 4);
   L.off_s = take((size_t)rows * nseg * 4);
   L.off_y = take((size_t)BT * 4);
@@ -137,6 +139,59 @@ struct DeviceGuard {
     if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
   }
 };
+
+// One call's problem description, workspace views and launch bookkeeping. Each launch is
+// optionally bracketed by a pre-created event pair on the call's stream (kernel timing diagnostics).
+struct Call {
+  flce_ctx* h;
+  hipStream_t stream;
+  flce::Problem p;
+  flce::Work w;
+  template <class F>
+  bool run(int kind, F&& launch) {
+    const size_t k = h->prof_kinds.size();
+    const bool rec = h->prof_on && 2 * (k + 1) <= h->prof_events.size();
+    if (rec && hipEventRecord(h->prof_events[2 * k], stream) != hipSuccess) return false;
+    if (launch() != hipSuccess) return false;
+    if (rec) {
+      if (hipEventRecord(h->prof_events[2 * k + 1], stream) != hipSuccess) return false;
+      h->prof_kinds.push_back(kind);
+    }
+    return true;
+  }
+};
+
+Call make_call(flce_ctx* h, const Layout& L, int64_t BT, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+               float softcap, int reduction, void* workspace, void* stream) {
+  Call c;
+  c.h = h;
+  c.stream = (hipStream_t)stream;
+  flce::Problem& p = c.p;
+  p.BT = BT;
+  p.H = H;
+  p.V = V;
+  p.V_pad = round_up(V, flce::kTile);
+  p.nseg = p.V_pad / flce::kSeg;
+  p.dtype = dtype;
+  p.ignore_index = ignore_index;
+  p.softcap = softcap;
+  p.reduction = reduction;
+  p.ncu = h->ncu;
+  char* base = (char*)workspace;
+  flce::Work& w = c.w;
+  w.ws_e = base + L.off_e;
+  w.seg_m = (float*)(base + L.off_m);
+  w.seg_s = (float*)(base + L.off_s);
+  w.y32 = (int*)(base + L.off_y);
+  w.s_label = (float*)(base + L.off_sl);
+  w.og = (float*)(base + L.off_og);
+  w.loss_row = (float*)(base + L.off_loss);
+  w.dx_part = L.splits > 1 ? (float*)(base + L.off_part) : nullptr;
+  w.params = (flce::DevParams*)(base + L.off_params);
+  w.xt = base + L.off_xt;
+  w.chunk_cap = L.chunk_rows;
+  return c;
+}
 
 }  // namespace
 
@@ -207,6 +262,7 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
   if (!h) return FLCE_ERR_INVALID_ARG;
   int rc = check_sizes(BT, H, V, dtype);
   if (rc != FLCE_OK) return rc;
+  if (reduction == FLCE_NONE) return FLCE_ERR_UNSUPPORTED;
   if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
   if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_INVALID_ARG;
   if (!W || !loss || !grad_W || !workspace) return FLCE_ERR_INVALID_ARG;
@@ -220,49 +276,13 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
 
   DeviceGuard g(h->device);
   if (!g.ok) return FLCE_ERR_HIP;
-  hipStream_t stream = (hipStream_t)stream_ptr;
-
-  flce::Problem p;
-  p.BT = BT;
-  p.H = H;
-  p.V = V;
-  p.V_pad = round_up(V, flce::kTile);
-  p.nseg = p.V_pad / flce::kSeg;
-  p.dtype = dtype;
-  p.ignore_index = ignore_index;
-  p.softcap = softcap;
-  p.reduction = reduction;
-  p.ncu = h->ncu;
-
-  char* base = (char*)workspace;
-  flce::Work w;
-  w.ws_e = base + L.off_e;
-  w.seg_m = (float*)(base + L.off_m);
-  w.seg_s = (float*)(base + L.off_s);
-  w.y32 = (int*)(base + L.off_y);
-  w.s_label = (float*)(base + L.off_sl);
-  w.og = (float*)(base + L.off_og);
-  w.loss_row = (float*)(base + L.off_loss);
-  w.dx_part = L.splits > 1 ? (float*)(base + L.off_part) : nullptr;
-  w.params = (flce::DevParams*)(base + L.off_params);
-  w.xt = base + L.off_xt;
-  w.chunk_cap = L.chunk_rows;
-
-  // Each launch is optionally bracketed by a pre-created event pair (kernel timing diagnostics).
-  auto run = [&](int kind, auto&& launch) -> bool {
-    const size_t k = h->prof_kinds.size();
-    const bool rec = h->prof_on && 2 * (k + 1) <= h->prof_events.size();
-    if (rec && hipEventRecord(h->prof_events[2 * k], stream) != hipSuccess) return false;
-    if (launch() != hipSuccess) return false;
-    if (rec) {
-      if (hipEventRecord(h->prof_events[2 * k + 1], stream) != hipSuccess) return false;
-      h->prof_kinds.push_back(kind);
-    }
-    return true;
-  };
-#define FLCE_LAUNCH(kind, expr)                                  \
-  do {                                                           \
-    if (!run(kind, [&]() { return (expr); })) return FLCE_ERR_HIP; \
+  Call call = make_call(h, L, BT, H, V, dtype, ignore_index, softcap, reduction, workspace, stream_ptr);
+  const hipStream_t stream = call.stream;
+  const flce::Problem& p = call.p;
+  const flce::Work& w = call.w;
+#define FLCE_LAUNCH(kind, expr)                                        \
+  do {                                                                 \
+    if (!call.run(kind, [&]() { return (expr); })) return FLCE_ERR_HIP; \
   } while (0)
 
   FLCE_LAUNCH(FLCE_K_PREPASS, flce::launch_prepass(p, labels, w, h->d_status, stream));
@@ -277,7 +297,7 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
     const int64_t row0 = ci * crows;
     const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
     FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
-    FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, stream));
+    FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, true, stream));
     FLCE_LAUNCH(FLCE_K_MERGE, flce::launch_merge(p, w, row0, rows, stream));
     int splits = L.splits > 1 ? dx_splits(rows, H, p.V_pad, dtype, h->ncu) : 1;
     if (splits > L.splits) splits = L.splits;
@@ -287,6 +307,60 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
     FLCE_LAUNCH(FLCE_K_DW, flce::launch_dw(p, hidden, w, grad_W, row0, rows, ci > 0, stream));
   }
   FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
+#undef FLCE_LAUNCH
+  return FLCE_OK;
+}
+
+int flce_forward_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, size_t* bytes) {
+  if (!bytes) return FLCE_ERR_INVALID_ARG;
+  const int rc = check_sizes(BT, H, V, dtype);
+  if (rc != FLCE_OK) return rc;
+  *bytes = layout(BT, H, V, dtype, chunk_max_of(h), ncu_of(h), false).total;
+  return FLCE_OK;
+}
+
+int flce_forward(flce_handle h, const void* hidden, const void* W, const int64_t* labels, int64_t BT, int64_t H,
+                 int64_t V, int dtype, int64_t ignore_index, float softcap, int reduction, float* loss,
+                 float* loss_rows, float* lse_rows, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  if (!h) return FLCE_ERR_INVALID_ARG;
+  int rc = check_sizes(BT, H, V, dtype);
+  if (rc != FLCE_OK) return rc;
+  if (reduction != FLCE_NONE && reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
+  if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_INVALID_ARG;
+  if (!W || !workspace) return FLCE_ERR_INVALID_ARG;
+  if (reduction == FLCE_NONE ? (BT > 0 && !loss_rows) : !loss) return FLCE_ERR_INVALID_ARG;
+  if (BT > 0 && (!hidden || !labels)) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || !aligned(workspace, 256) || !aligned(loss, 4) || !aligned(loss_rows, 4) ||
+      !aligned(lse_rows, 4))
+    return FLCE_ERR_INVALID_ARG;
+  if (BT > 0 && (!aligned(hidden, 16) || !aligned(labels, 8))) return FLCE_ERR_INVALID_ARG;
+  const Layout L = layout(BT, H, V, dtype, h->chunk_rows_max, h->ncu, false);
+  if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+
+  DeviceGuard g(h->device);
+  if (!g.ok) return FLCE_ERR_HIP;
+  // per-row terms need no scale; the pre-pass's 1/N only matters for the reduced mean
+  const int red = reduction == FLCE_NONE ? FLCE_SUM : reduction;
+  Call call = make_call(h, L, BT, H, V, dtype, ignore_index, softcap, red, workspace, stream_ptr);
+  const hipStream_t stream = call.stream;
+  const flce::Problem& p = call.p;
+  const flce::Work& w = call.w;
+#define FLCE_LAUNCH(kind, expr)                                        \
+  do {                                                                 \
+    if (!call.run(kind, [&]() { return (expr); })) return FLCE_ERR_HIP; \
+  } while (0)
+
+  FLCE_LAUNCH(FLCE_K_PREPASS, flce::launch_prepass(p, labels, w, h->d_status, stream));
+  int64_t n_chunks, crows;
+  plan(BT, h->chunk_rows_max, &n_chunks, &crows);
+  for (int64_t ci = 0; ci < n_chunks && BT > 0; ++ci) {
+    const int64_t row0 = ci * crows;
+    const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
+    FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
+    FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, false, stream));
+    FLCE_LAUNCH(FLCE_K_ROWS, flce::launch_rows(p, w, row0, rows, loss_rows, lse_rows, stream));
+  }
+  if (reduction != FLCE_NONE) FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
 #undef FLCE_LAUNCH
   return FLCE_OK;
 }

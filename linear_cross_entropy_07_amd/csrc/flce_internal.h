@@ -58,7 +58,9 @@ hipError_t launch_prepass(const Problem& p, const int64_t* labels, const Work& w
 hipError_t launch_transpose(const Problem& p, const void* hidden, const Work& w, int64_t row0, int64_t rows,
                             hipStream_t stream);
 hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t row0, int64_t rows,
-                      hipStream_t stream);
+                      bool store_q, hipStream_t stream);
+hipError_t launch_rows(const Problem& p, const Work& w, int64_t row0, int64_t rows, float* loss_rows,
+                       float* lse_rows, hipStream_t stream);
 hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream);
 hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_hidden, int64_t row0,
                      int64_t rows, int splits, hipStream_t stream);

@@ -580,7 +580,7 @@ __device__ __forceinline__ u32 qlds(int cl, int vl) {  // byte address of q(cl, 
   return (u32)(cl * (TILE * 2) + (((vl >> 3) ^ (cl & 31)) << 4) + ((vl & 7) << 1));
 }
 
-template <typename T, bool CAP, bool EDGE, int J0, int JG>
+template <typename T, bool CAP, bool EDGE, bool STORE_Q, int J0, int JG>
 __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc)[TBM][TBN], int v0, int c0,
                                                   const int (&ylab)[TBN], char* smem) {
   using S = typename Traits<T>::S;
@@ -655,7 +655,9 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
           }
         }
         const u32 qoff = qrow + (u32)((32 * i + 8 * g) * sizeof(S));
-        if constexpr (kStageQ<T>) {
+        if constexpr (!STORE_Q) {
+          (void)qoff;
+        } else if constexpr (kStageQ<T>) {
           f16x4 h{(S)q[0], (S)q[1], (S)q[2], (S)q[3]};
           *(u32x2*)(smem + qlds(c - c0, wm * WM + 32 * i + 8 * g + 4 * half)) = __builtin_bit_cast(u32x2, h);
         } else if constexpr (sizeof(S) == 2) {
@@ -709,12 +711,12 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
   }
 }
 
-template <typename T, bool CAP, bool EDGE>
+template <typename T, bool CAP, bool EDGE, bool STORE_Q>
 __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16 (&acc)[TBM][TBN], int v0, int c0,
                                              const int (&ylab)[TBN], char* smem) {
   // two row blocks at a time: enough independent work, few enough live values to stay in registers
-  fwd_epilogue_part<T, CAP, EDGE, 0, 2>(a, acc, v0, c0, ylab, smem);
-  if constexpr (TBN > 2) fwd_epilogue_part<T, CAP, EDGE, 2, 2>(a, acc, v0, c0, ylab, smem);
+  fwd_epilogue_part<T, CAP, EDGE, STORE_Q, 0, 2>(a, acc, v0, c0, ylab, smem);
+  if constexpr (TBN > 2) fwd_epilogue_part<T, CAP, EDGE, STORE_Q, 2, 2>(a, acc, v0, c0, ylab, smem);
 }
 
 // Staged q tile -> workspace: 32 threads per 512-byte row, each one 16-byte chunk; rows past the
@@ -733,7 +735,9 @@ __device__ __forceinline__ void fwd_store_staged(const FwdArgs& a, int v0, int c
   }
 }
 
-template <typename T>
+// STORE_Q = false is the forward-only path: the row statistics and label logits are produced, the
+// q tile is not stored.
+template <typename T, bool STORE_Q>
 __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes];
 
@@ -758,16 +762,16 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
   const bool edge = v0 + (((int)threadIdx.x >> 6) & 1) * WM + WM > a.V;
   if (a.softcap > 0.0f) {
     if (edge)
-      fwd_epilogue<T, true, true>(a, acc, v0, c0, ylab, smem);
+      fwd_epilogue<T, true, true, STORE_Q>(a, acc, v0, c0, ylab, smem);
     else
-      fwd_epilogue<T, true, false>(a, acc, v0, c0, ylab, smem);
+      fwd_epilogue<T, true, false, STORE_Q>(a, acc, v0, c0, ylab, smem);
   } else {
     if (edge)
-      fwd_epilogue<T, false, true>(a, acc, v0, c0, ylab, smem);
+      fwd_epilogue<T, false, true, STORE_Q>(a, acc, v0, c0, ylab, smem);
     else
-      fwd_epilogue<T, false, false>(a, acc, v0, c0, ylab, smem);
+      fwd_epilogue<T, false, false, STORE_Q>(a, acc, v0, c0, ylab, smem);
   }
-  if constexpr (kStageQ<T>) {
+  if constexpr (STORE_Q && kStageQ<T>) {
     __syncthreads();
     fwd_store_staged<T>(a, v0, c0, smem);
   }
@@ -968,20 +972,14 @@ __global__ __launch_bounds__(1024) void k_prepass(const int64_t* labels, int64_t
 // then one sweep over the row turning q into dZ = q * g * exp(m_seg - lse) - [v == y] * og, written
 // in place in the operand type of the backward GEMMs. This is where the softmax is rebuilt from the
 // logits-derived q and the small per-row max/sum statistics.
-template <typename T>
-__global__ __launch_bounds__(256) void k_merge_dlogits(void* ws, const float* seg_m, const float* seg_s,
-                                                       int nseg, int64_t V_pad, const int* y32,
-                                                       const float* s_label, const float* og,
-                                                       const DevParams* prm, float* loss_row) {
-  using S = typename Traits<T>::S;
-  constexpr int KV = Traits<T>::KV;
-  extern __shared__ float sc_seg[];  // [nseg]: g * exp(m_seg - lse)
+// Per-row log-sum-exp from the per-(row, 128-wide segment) statistics of the logits epilogue, in a
+// fixed order (max over the segments, then the rescaled sum), and the row's loss term (0 on rows that
+// do not count). One 256-thread block per row; every thread returns the row's lse.
+__device__ __forceinline__ float row_lse(const float* m, const float* sp, int nseg, int c, const int* y32,
+                                         const float* s_label, float* loss_row, float* lse_out) {
   __shared__ float red[4];
   __shared__ float s_lse;
-  const int c = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float* m = seg_m + (int64_t)c * nseg;
-  const float* sp = seg_s + (int64_t)c * nseg;
   float M = kNegInf;
   for (int j = threadIdx.x; j < nseg; j += 256) M = fmaxf(M, m[j]);
   M = wave_max(M);
@@ -998,11 +996,25 @@ __global__ __launch_bounds__(256) void k_merge_dlogits(void* ws, const float* se
     const float lse = M + __logf((red[0] + red[1]) + (red[2] + red[3]));
     s_lse = lse;
     loss_row[c] = y32[c] >= 0 ? lse - s_label[c] : 0.0f;
+    if (lse_out) lse_out[c] = lse;
   }
   __syncthreads();
+  return s_lse;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_merge_dlogits(void* ws, const float* seg_m, const float* seg_s,
+                                                       int nseg, int64_t V_pad, const int* y32,
+                                                       const float* s_label, const float* og,
+                                                       const DevParams* prm, float* loss_row) {
+  using S = typename Traits<T>::S;
+  constexpr int KV = Traits<T>::KV;
+  extern __shared__ float sc_seg[];  // [nseg]: g * exp(m_seg - lse)
+  const int c = blockIdx.x;
+  const float* m = seg_m + (int64_t)c * nseg;
+  const float lse = row_lse(m, seg_s + (int64_t)c * nseg, nseg, c, y32, s_label, loss_row, nullptr);
   const int y = y32[c];
   const float g = y >= 0 ? prm->ginv : 0.0f;
-  const float lse = s_lse;
   for (int j = threadIdx.x; j < nseg; j += 256) sc_seg[j] = g * ex2((m[j] - lse) * kLog2e);
   __syncthreads();
   const float oc = og[c];
@@ -1027,6 +1039,18 @@ __global__ __launch_bounds__(256) void k_merge_dlogits(void* ws, const float* se
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pack(f, (T*)nullptr)), rr, q * 16, 0, 0);
     }
   }
+}
+
+// Forward-only path: per-row lse and loss term of one chunk (rows row0 .. of the call), optionally
+// copied to caller buffers indexed by the call's row.
+__global__ __launch_bounds__(256) void k_rows(const float* seg_m, const float* seg_s, int nseg,
+                                              const int* y32, const float* s_label, float* loss_row,
+                                              float* loss_out, float* lse_out) {
+  const int c = blockIdx.x;
+  const float lse = row_lse(seg_m + (int64_t)c * nseg, seg_s + (int64_t)c * nseg, nseg, c, y32, s_label,
+                            loss_row, lse_out);
+  (void)lse;
+  if (threadIdx.x == 0 && loss_out) loss_out[c] = loss_row[c];
 }
 
 // Fixed-order loss reduction (one block).
@@ -1075,7 +1099,7 @@ hipError_t launch_transpose(const Problem& p, const void* hidden, const Work& w,
 }
 
 hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t row0, int64_t rows,
-                      hipStream_t stream) {
+                      bool store_q, hipStream_t stream) {
   FwdArgs a;
   a.XT = w.xt;
   a.ldt = w.chunk_cap;
@@ -1094,10 +1118,17 @@ hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t ro
   a.rows = (int)rows;
   a.softcap = p.softcap;
   const unsigned grid = (unsigned)((p.V_pad / TILE) * ((rows + TILE - 1) / TILE));
-  if (p.dtype == 0)
-    k_fwd<__bf16><<<grid, NTHR, 0, stream>>>(a);
-  else
-    k_fwd<float><<<grid, NTHR, 0, stream>>>(a);
+  if (p.dtype == 0) {
+    if (store_q)
+      k_fwd<__bf16, true><<<grid, NTHR, 0, stream>>>(a);
+    else
+      k_fwd<__bf16, false><<<grid, NTHR, 0, stream>>>(a);
+  } else {
+    if (store_q)
+      k_fwd<float, true><<<grid, NTHR, 0, stream>>>(a);
+    else
+      k_fwd<float, false><<<grid, NTHR, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -1110,6 +1141,14 @@ hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t r
     k_merge_dlogits<float><<<(unsigned)rows, 256, (size_t)p.nseg * 4, stream>>>(w.ws_e, w.seg_m, w.seg_s, (int)p.nseg, p.V_pad,
                                                              w.y32 + row0, w.s_label + row0, w.og + row0,
                                                              w.params, w.loss_row + row0);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows(const Problem& p, const Work& w, int64_t row0, int64_t rows, float* loss_rows,
+                       float* lse_rows, hipStream_t stream) {
+  k_rows<<<(unsigned)rows, 256, 0, stream>>>(w.seg_m, w.seg_s, (int)p.nseg, w.y32 + row0, w.s_label + row0,
+                                             w.loss_row + row0, loss_rows ? loss_rows + row0 : nullptr,
+                                             lse_rows ? lse_rows + row0 : nullptr);
   return hipGetLastError();
 }
 

@@ -17,8 +17,9 @@ import torch
 from . import build_lib
 
 FLCE_BF16, FLCE_FP32 = 0, 1
-FLCE_MEAN, FLCE_SUM = 1, 2
+FLCE_NONE, FLCE_MEAN, FLCE_SUM = 0, 1, 2
 _REDUCTIONS = {"mean": FLCE_MEAN, "sum": FLCE_SUM}
+_FWD_REDUCTIONS = {"none": FLCE_NONE, "mean": FLCE_MEAN, "sum": FLCE_SUM}
 _DTYPES = {torch.bfloat16: FLCE_BF16, torch.float32: FLCE_FP32}
 
 ERRORS = {0: "FLCE_OK", -1: "FLCE_ERR_INVALID_ARG", -2: "FLCE_ERR_UNSUPPORTED",
@@ -63,13 +64,17 @@ def lib() -> ctypes.CDLL:
             L.flce_chunk_plan.argtypes = [vp, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
             L.flce_forward_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, ctypes.c_float,
                                                 i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            L.flce_forward_workspace_size.argtypes = [vp, i64, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
+            L.flce_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, ctypes.c_float, i32,
+                                       vp, vp, vp, vp, ctypes.c_size_t, vp]
             L.flce_status.argtypes = [vp, vp]
             L.flce_profile_begin.argtypes = [vp, i32]
             L.flce_profile_end.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
             L.flce_error_string.argtypes = [i32]
             L.flce_error_string.restype = ctypes.c_char_p
             for f in ("flce_create", "flce_destroy", "flce_workspace_size", "flce_chunk_plan",
-                      "flce_forward_backward", "flce_status", "flce_profile_begin", "flce_profile_end"):
+                      "flce_forward_backward", "flce_forward_workspace_size", "flce_forward", "flce_status",
+                      "flce_profile_begin", "flce_profile_end"):
                 getattr(L, f).restype = i32
             _LIB = L
     return _LIB
@@ -84,6 +89,13 @@ def workspace_size(BT: int, H: int, V: int, dtype=torch.bfloat16, handle=None) -
     out = ctypes.c_size_t()
     _check(lib().flce_workspace_size(handle, BT, H, V, _DTYPES[dtype], ctypes.byref(out)),
            "flce_workspace_size")
+    return out.value
+
+
+def forward_workspace_size(BT: int, H: int, V: int, dtype=torch.bfloat16, handle=None) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().flce_forward_workspace_size(handle, BT, H, V, _DTYPES[dtype], ctypes.byref(out)),
+           "flce_forward_workspace_size")
     return out.value
 
 
@@ -137,10 +149,7 @@ class FLCE:
             self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
         return self._ws
 
-    def forward_backward(self, hidden: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
-                         ignore_index: int = -100, softcap: float = 0.0, reduction: str = "mean",
-                         out=None, workspace: torch.Tensor | None = None, stream=None):
-        """Run the fused forward + backward; returns (loss [0-dim fp32], grad_hidden, grad_W fp32)."""
+    def _check_inputs(self, hidden: torch.Tensor, W: torch.Tensor, labels: torch.Tensor):
         if hidden.dim() != 2 or W.dim() != 2 or labels.dim() != 1:
             raise ValueError("hidden [BT,H], W [V,H], labels [BT] expected")
         BT, H = hidden.shape
@@ -157,6 +166,13 @@ class FLCE:
                 raise ValueError(f"{name} is on {t.device}, handle is on {self.device}")
             if not t.is_contiguous():
                 raise ValueError(f"{name} must be contiguous")
+        return BT, H, V
+
+    def forward_backward(self, hidden: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
+                         ignore_index: int = -100, softcap: float = 0.0, reduction: str = "mean",
+                         out=None, workspace: torch.Tensor | None = None, stream=None):
+        """Run the fused forward + backward; returns (loss [0-dim fp32], grad_hidden, grad_W fp32)."""
+        BT, H, V = self._check_inputs(hidden, W, labels)
         if reduction not in _REDUCTIONS:
             raise ValueError("reduction must be 'mean' or 'sum'")
         dt = _DTYPES[hidden.dtype]
@@ -179,7 +195,33 @@ class FLCE:
         _check(rc, "flce_forward_backward")
         return loss, gh, gw
 
-    KERNELS = ("prepass", "fwd", "merge", "dx", "dx_reduce", "dw", "finalize", "transpose")
+    def forward(self, hidden: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,
+                softcap: float = 0.0, reduction: str = "mean", return_lse: bool = False,
+                workspace: torch.Tensor | None = None, stream=None):
+        """Forward only. Returns the loss (0-dim fp32) for 'mean'/'sum', or the per-row loss terms
+        [BT] fp32 for 'none'; with return_lse also the per-row log-sum-exp [BT] fp32."""
+        BT, H, V = self._check_inputs(hidden, W, labels)
+        if reduction not in _FWD_REDUCTIONS:
+            raise ValueError("reduction must be 'none', 'mean' or 'sum'")
+        dt = _DTYPES[hidden.dtype]
+        need = forward_workspace_size(BT, H, V, hidden.dtype, self._h)
+        if workspace is None:
+            workspace = self.workspace(need)
+        loss = torch.empty((), dtype=torch.float32, device=self.device) if reduction != "none" else None
+        rows = torch.empty(BT, dtype=torch.float32, device=self.device) if reduction == "none" else None
+        lse = torch.empty(BT, dtype=torch.float32, device=self.device) if return_lse else None
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        rc = lib().flce_forward(
+            self._h, hidden.data_ptr(), W.data_ptr(), labels.data_ptr(), BT, H, V, dt, int(ignore_index),
+            float(softcap), _FWD_REDUCTIONS[reduction], ptr(loss), ptr(rows), ptr(lse),
+            workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+        _check(rc, "flce_forward")
+        out = loss if reduction != "none" else rows
+        return (out, lse) if return_lse else out
+
+    KERNELS = ("prepass", "fwd", "merge", "dx", "dx_reduce", "dw", "finalize", "transpose", "rows")
 
     def profile_begin(self, max_launches: int = 4096):
         """Bracket every following kernel launch with HIP events on its stream (diagnostics)."""

@@ -11,5 +11,6 @@ from .flce_oracle import (  # noqa: F401
     row_logsumexp,
     valid_mask,
     flce_forward_backward,
+    flce_forward,
     flce_rows,
 )

@@ -165,6 +165,33 @@ def flce_forward_backward(X, W, y, ignore_index: int = -100, softcap: float = 0.
     return loss, dX, dW
 
 
+def flce_forward(X, W, y, ignore_index: int = -100, softcap: float = 0.0, reduction: str = "mean"):
+    """Forward only: the NLL of the PR description without any gradient.
+
+    Steps 1-5 of the module docstring on fully materialised float64 logits. Returns (out, lse):
+    out is the loss (a float) for 'mean' and 'sum', or the per-row terms l_t [BT] (lse_t - s_{t,y_t},
+    0 on ignored rows) for 'none'; lse [BT] is the row log-sum-exp of every row, ignored rows
+    included.
+    """
+    X = _f64(X)
+    W = _f64(W)
+    y = _labels(y)
+    _check(X, W, y, softcap, "mean" if reduction == "none" else reduction)
+    V = W.shape[0]
+    valid = valid_mask(y, V, ignore_index)
+    S = apply_softcap(logits(X, W), softcap)
+    _, lse = row_logsumexp(S)
+    y_safe = np.where(valid, y, 0)
+    loss_rows = np.where(valid, lse - S[np.arange(X.shape[0]), y_safe], 0.0)
+    if reduction == "none":
+        return loss_rows, lse
+    total = float(loss_rows.sum())
+    N = int(valid.sum())
+    if reduction == "mean":
+        return (total / N if N > 0 else 0.0), lse
+    return total, lse
+
+
 def flce_rows(X, W, y, rows, n_valid: int, ignore_index: int = -100, softcap: float = 0.0,
               reduction: str = "mean"):
     """Per-row results for a subset of the rows of a larger call.

@@ -79,13 +79,45 @@ def test_forward_backward_rejects_before_any_device_call():
     assert _fb(h=fake, BT=-1) == -1
     assert _fb(h=fake, H=12) == -2
     assert _fb(h=fake, dtype=3) == -1
-    assert _fb(h=fake, red=0) == -1
+    assert _fb(h=fake, red=0) == -2                  # 'none' is offered by flce_forward only
     assert _fb(h=fake, red=3) == -1
     assert _fb(h=fake, softcap=-1.0) == -1
     assert _fb(h=fake, softcap=float("nan")) == -1
     assert _fb(h=fake, softcap=float("inf")) == -1
     assert _fb(h=fake, ptr=0) == -1              # null pointers
     assert _fb(h=fake, ptr=264) == -1            # misaligned workspace (needs 256)
+
+
+def _fw(h=NULL, BT=4, H=64, V=10, dtype=0, softcap=0.0, red=1, loss=256, rows=256, lse=0, ptr=256,
+        ws=256, ws_bytes=1 << 30):
+    p = ctypes.c_void_p(ptr)
+    v = lambda a: ctypes.c_void_p(a) if a else NULL  # noqa: E731
+    return L.flce_forward(h, p, p, p, BT, H, V, dtype, -100, softcap, red, v(loss), v(rows), v(lse),
+                          v(ws), ws_bytes, NULL)
+
+
+def test_forward_rejects_before_any_device_call():
+    assert _fw(h=NULL) == -1
+    fake = ctypes.c_void_p(1)                    # never dereferenced: argument checks come first
+    assert _fw(h=fake, BT=-1) == -1
+    assert _fw(h=fake, H=12) == -2
+    assert _fw(h=fake, red=3) == -1
+    assert _fw(h=fake, red=0, rows=0) == -1      # 'none' needs the per-row output
+    assert _fw(h=fake, red=1, loss=0) == -1      # 'mean' needs the scalar loss
+    assert _fw(h=fake, softcap=-2.0) == -1
+    assert _fw(h=fake, rows=258) == -1           # misaligned per-row output
+    assert _fw(h=fake, ws=0) == -1
+    assert _fw(h=fake, ws=264) == -1
+
+
+def test_forward_workspace_keeps_no_logits():
+    H, V = 4096, 128256
+    fwd = flce.forward_workspace_size(8192, H, V)
+    full = flce.workspace_size(8192, H, V)
+    # no 16-bit logits chunk: segment statistics + hidden^T of one chunk + per-row data
+    assert fwd < full - 4096 * V * 2 + 1
+    assert fwd < 4096 * (V // 128) * 8 + 4096 * H * 2 + 8192 * 16 + 4096
+    assert flce.forward_workspace_size(33768, H, V) < fwd + 64 * 33768
 
 
 def test_create_without_gpu_fails_cleanly():

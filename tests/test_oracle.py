@@ -167,6 +167,43 @@ def test_matches_torch_cross_entropy(softcap, reduction, shape):
     assert _rel(dW, tdW) < 1e-12
 
 
+# ---------------------------------------------------------------- forward-only oracle
+
+@pytest.mark.parametrize("softcap", [0.0, 4.0])
+@pytest.mark.parametrize("shape", [(256, 64, 1000), (7, 8, 3)])
+def test_forward_rows_match_torch(softcap, shape):
+    """Per-row NLL and lse against torch float64 cross_entropy(reduction='none') and logsumexp."""
+    BT, H, V = shape
+    rng = np.random.default_rng(16)
+    X, W, y = _rand_case(rng, BT, H, V, ignore=max(1, BT // 10), w_scale=4.0)
+    rows, lse = oracle.flce_forward(X, W, y, IGN, softcap, "none")
+    z = torch.nn.functional.linear(torch.tensor(X), torch.tensor(W))
+    if softcap > 0:
+        z = softcap * torch.tanh(z / softcap)
+    t_rows = torch.nn.functional.cross_entropy(z, torch.tensor(y), ignore_index=IGN, reduction="none").numpy()
+    t_lse = torch.logsumexp(z, dim=1).numpy()
+    np.testing.assert_allclose(rows, t_rows, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, t_lse, rtol=1e-12, atol=0)
+    assert np.all(rows[y == IGN] == 0.0)
+    for red in ("mean", "sum"):
+        loss, lse2 = oracle.flce_forward(X, W, y, IGN, softcap, red)
+        tl = torch.nn.functional.cross_entropy(z, torch.tensor(y), ignore_index=IGN, reduction=red).item()
+        assert abs(loss - tl) <= 1e-12 * abs(tl)
+        np.testing.assert_array_equal(lse2, lse)
+
+
+def test_forward_zero_weight_closed_form():
+    """W = 0: every row's lse is ln V, every valid row's term is ln V, ignored rows give 0."""
+    rng = np.random.default_rng(17)
+    X, _, y = _rand_case(rng, 33, 8, 21, ignore=4)
+    W = np.zeros((21, 8))
+    rows, lse = oracle.flce_forward(X, W, y, IGN, 0.0, "none")
+    np.testing.assert_allclose(lse, math.log(21), rtol=1e-15)
+    np.testing.assert_allclose(rows, np.where(y == IGN, 0.0, math.log(21)), rtol=1e-15)
+    loss, _ = oracle.flce_forward(X, W, y, IGN, 0.0, "mean")
+    assert abs(loss - math.log(21)) < 1e-14
+
+
 # ---------------------------------------------------------------- invariants and metamorphic relations
 
 @pytest.mark.parametrize("softcap", [0.0, 3.0])
