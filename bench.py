@@ -175,8 +175,8 @@ def main():
     gemm = {k: kt[k] for k in (("fwd",) if fwd_only else ("fwd", "dx", "dw"))}
     dom = max(gemm, key=lambda k: gemm[k][0])
     dom_ms = gemm[dom][0] / gemm[dom][1]
-    flops_per_launch = 2.0 * chunk_rows * H * V  # one GEMM of a full chunk: 2*C*H*V
-    # the last chunk may be shorter: average algorithmic flops over the launches actually made
+    # one GEMM launch per chunk; the last chunk may be shorter, so average the algorithmic flops
+    # 2*C*H*V over the launches actually made
     flops_per_launch = 2.0 * BT * H * V / n_chunks
     achieved = flops_per_launch / (dom_ms * 1e-3)
 
@@ -208,7 +208,7 @@ def main():
         "kernels_ms_per_launch": {k: round(v[0] / v[1], 4) for k, v in kt.items() if v[1]},
         "roofline": {"kernel": f"k_{dom}", "bound": "mfma", "achieved": round(achieved / 1e12, 2),
                      "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
-                     "traffic": None if fwd_only else traffic_from_profiles(dom),
+                     "traffic": traffic_from_profiles("fwd_noq" if fwd_only else dom),
                      "flops_per_launch": flops_per_launch},
     }
     if not args.no_cpu_baseline:
