@@ -142,6 +142,63 @@ int flce_forward(flce_handle h,
                  float* loss, float* loss_rows, float* lse_rows,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Rows given as a batch of sequences (the *_rows entry points). hidden and grad_hidden hold B
+ * sequences of T positions, each position a row of H contiguous elements, at arbitrary
+ * non-negative element strides; labels hold B x T int64 values at their own strides. With
+ * shift = 1, position t < T-1 of sequence b is scored against the label at position t+1 and
+ * position T-1 is not a row: the next-token shift of a causal LM, which torchtune issue #1228
+ * ("[FEATURE REQUEST] Compile model+loss_fn together") shows being done with sliced .contiguous()
+ * copies of the logits and labels. Here no copy is made: rows are addressed where they lie.
+ * Row r = b * (T - shift) + t, so BT = B * (T - shift); loss_rows / lse_rows are indexed by r. */
+typedef struct {
+  int64_t batch;                 /* B >= 0 */
+  int64_t seq;                   /* T >= 0 positions per sequence */
+  int64_t shift;                 /* 0 or 1 */
+  int64_t hidden_stride[2];      /* elements from (b, t) to (b+1, t) and to (b, t+1); multiples of
+                                    8 (FLCE_BF16) or 4 (FLCE_FP32) elements, so rows stay 16-byte aligned */
+  int64_t grad_hidden_stride[2]; /* the same for grad_hidden; its B x T rows must not overlap */
+  int64_t label_stride[2];       /* elements from (b, t) to (b+1, t) and to (b, t+1) of labels */
+} flce_rows;
+
+/* Flags of flce_forward_backward_rows. */
+enum { FLCE_ACCUMULATE_GRAD_HIDDEN = 1, FLCE_ACCUMULATE_GRAD_W = 2 };
+
+/* Bytes of device workspace flce_forward_backward_rows needs (host-only arithmetic; h may be NULL).
+ * Equal to flce_workspace_size for BT = B * (T - shift) when the hidden rows lie in the plain
+ * [BT][H] layout; otherwise one chunk of gathered hidden rows ([chunk_rows][H] of dtype) more.
+ * Returns FLCE_OK, FLCE_ERR_INVALID_ARG or FLCE_ERR_UNSUPPORTED. */
+int flce_workspace_size_rows(flce_handle h, const flce_rows* rows, int64_t H, int64_t V, int dtype,
+                             size_t* bytes);
+
+/* flce_forward_backward over rows described by `rows` (see flce_rows), with two more options:
+ *   grad_scale   multiplies grad_hidden and grad_W (not the loss): the upstream gradient of the
+ *                loss, e.g. 1 / gradient-accumulation steps as in the training loop of the
+ *                torchtune issue #1228 discussion; finite, else FLCE_ERR_INVALID_ARG
+ *   flags        FLCE_ACCUMULATE_GRAD_HIDDEN: grad_hidden rows get += instead of =
+ *                FLCE_ACCUMULATE_GRAD_W: grad_W gets += instead of =; other bits FLCE_ERR_INVALID_ARG
+ *   grad_hidden  device, B x T rows at grad_hidden_stride (written): the rows of the call get their
+ *                gradient; with shift = 1 the last position of each sequence gets 0 (or is left as it
+ *                is with FLCE_ACCUMULATE_GRAD_HIDDEN)
+ * Everything else as for flce_forward_backward (BT there is B * (T - shift) here). With B = 1,
+ * T = BT, shift = 0, hidden/grad strides {0, H}, label strides {0, 1}, grad_scale = 1 and no flags
+ * it computes exactly what flce_forward_backward computes. */
+int flce_forward_backward_rows(flce_handle h,
+                               const void* hidden, const void* W, const int64_t* labels,
+                               const flce_rows* rows, int64_t H, int64_t V, int dtype,
+                               int64_t ignore_index, float softcap, int reduction,
+                               float grad_scale, int flags,
+                               float* loss, void* grad_hidden, float* grad_W,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* flce_forward over rows described by `rows` (grad_hidden_stride is not used). The workspace is
+ * flce_forward_workspace_size for BT = B * (T - shift). */
+int flce_forward_rows(flce_handle h,
+                      const void* hidden, const void* W, const int64_t* labels,
+                      const flce_rows* rows, int64_t H, int64_t V, int dtype,
+                      int64_t ignore_index, float softcap, int reduction,
+                      float* loss, float* loss_rows, float* lse_rows,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Synchronise `stream` and report the status word of the last flce_forward_backward or flce_forward on it:
  * FLCE_OK, or FLCE_ERR_LABEL_RANGE if some label was outside [0, V) and not ignore_index. */
 int flce_status(flce_handle h, void* stream);

@@ -13,6 +13,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "flce.h"
@@ -79,14 +80,16 @@ int dx_splits(int64_t rows, int64_t H, int64_t V_pad, int dtype, int ncu) {
 }
 
 struct Layout {
-  size_t off_e, off_m, off_s, off_y, off_sl, off_og, off_loss, off_part, off_xt, off_params, total;
+  size_t off_e, off_m, off_s, off_y, off_sl, off_og, off_loss, off_part, off_xt, off_xs, off_params, total;
   int splits;
   int64_t chunk_rows;
 };
 
 // Workspace carving. The forward-only path (backward = false) needs no q/dZ chunk and no split-K
-// partials.
-Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu, bool backward = true) {
+// partials; a gathered copy of the chunk's hidden rows (xstage) is needed only by the backward of
+// rows that are not in the plain [BT][H] layout.
+Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu, bool backward = true,
+              bool xstage = false) {
   Layout L{};
   int64_t n, rows;
   plan(BT, cmax, &n, &rows);
@@ -111,6 +114,7 @@ Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu
   L.off_loss = take((size_t)BT * 4);
   L.off_part = take(L.splits > 1 ? (size_t)L.splits * rows * H * 4 : 0);
   L.off_xt = take((size_t)rows * H * esz);
+  L.off_xs = take(backward && xstage ? (size_t)rows * H * esz : 0);
   L.total = off;
   return L;
 }
@@ -121,6 +125,73 @@ int check_sizes(int64_t BT, int64_t H, int64_t V, int dtype) {
   if (BT < 0 || H <= 0 || V <= 0) return FLCE_ERR_INVALID_ARG;
   if (dtype != FLCE_BF16 && dtype != FLCE_FP32) return FLCE_ERR_INVALID_ARG;
   if (H % 8 != 0 || H > kMaxH || V > kMaxV || BT > kMaxBT) return FLCE_ERR_UNSUPPORTED;
+  return FLCE_OK;
+}
+
+// Rows of one call: where row r's hidden, grad_hidden and label live.
+struct Rows {
+  int64_t B = 0, T = 0, shift = 0, BT = 0;
+  flce::RowMap hmap{}, gmap{}, lmap{};
+  bool dense = true;  // hidden rows in the plain [BT][H] layout
+};
+
+// The plain layout: hidden and grad_hidden [BT][H], labels [BT].
+Rows plain_rows(int64_t BT, int64_t H) {
+  Rows r;
+  r.B = BT;
+  r.T = 1;
+  r.BT = BT;
+  r.hmap = flce::RowMap{H, 0, 0, 1};
+  r.gmap = r.hmap;
+  r.lmap = flce::RowMap{1, 0, 0, 1};
+  return r;
+}
+
+// True if rows (b, t) of extents (n0, n1) with element strides (s0, s1) and `width` elements each
+// never share an element (the two strides, ordered, must each step past everything inside).
+bool no_overlap(int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_t width) {
+  if (n0 <= 1) s0 = 0, n0 = 1;
+  if (n1 <= 1) s1 = 0, n1 = 1;
+  if (n0 == 1 && n1 == 1) return true;
+  if (n0 == 1) return s1 >= width;
+  if (n1 == 1) return s0 >= width;
+  if (s0 > s1) {
+    std::swap(s0, s1);
+    std::swap(n0, n1);
+  }
+  return s0 >= width && s1 >= n0 * s0;
+}
+
+// Validates a flce_rows description (see include/flce.h) and derives the row maps.
+int check_rows(const flce_rows* d, int64_t H, int dtype, bool grads, Rows* out) {
+  if (!d) return FLCE_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->seq < 0 || (d->shift != 0 && d->shift != 1)) return FLCE_ERR_INVALID_ARG;
+  for (int i = 0; i < 2; ++i)
+    if (d->hidden_stride[i] < 0 || d->label_stride[i] < 0 || (grads && d->grad_hidden_stride[i] < 0))
+      return FLCE_ERR_INVALID_ARG;
+  const int64_t per = d->seq > d->shift ? d->seq - d->shift : 0;
+  if (d->batch > 0 && per > 0 && d->batch > kMaxBT / per) return FLCE_ERR_UNSUPPORTED;
+  // 16-byte aligned rows: element strides of hidden and grad_hidden are multiples of 16 bytes
+  const int64_t al = dtype == FLCE_BF16 ? 8 : 4;
+  for (int i = 0; i < 2; ++i)
+    if (d->hidden_stride[i] % al != 0 || (grads && d->grad_hidden_stride[i] % al != 0))
+      return FLCE_ERR_INVALID_ARG;
+  // every grad_hidden row is written (rows of the call, and the skipped last positions when the
+  // labels are shifted), so no two of them may share an element
+  if (grads && !no_overlap(d->batch, d->grad_hidden_stride[0], d->seq, d->grad_hidden_stride[1], H))
+    return FLCE_ERR_INVALID_ARG;
+  Rows r;
+  r.B = d->batch;
+  r.T = d->seq;
+  r.shift = d->shift;
+  r.BT = d->batch * per;
+  const uint32_t up = (uint32_t)(per > 0 ? per : 1);
+  r.hmap = flce::RowMap{d->hidden_stride[0], d->hidden_stride[1], 0, up};
+  r.gmap = flce::RowMap{d->grad_hidden_stride[0], d->grad_hidden_stride[1], 0, up};
+  r.lmap = flce::RowMap{d->label_stride[0], d->label_stride[1], d->shift * d->label_stride[1], up};
+  // plain [BT][H] rows: consecutive positions H apart, consecutive sequences per * H apart
+  r.dense = (per <= 1 || d->hidden_stride[1] == H) && (d->batch <= 1 || d->hidden_stride[0] == per * H);
+  *out = r;
   return FLCE_OK;
 }
 
@@ -161,13 +232,21 @@ struct Call {
   }
 };
 
-Call make_call(flce_ctx* h, const Layout& L, int64_t BT, int64_t H, int64_t V, int dtype, int64_t ignore_index,
-               float softcap, int reduction, void* workspace, void* stream) {
+Call make_call(flce_ctx* h, const Layout& L, const Rows& R, int64_t H, int64_t V, int dtype,
+               int64_t ignore_index, float softcap, int reduction, float grad_scale, int flags, void* workspace,
+               void* stream) {
   Call c;
   c.h = h;
   c.stream = (hipStream_t)stream;
   flce::Problem& p = c.p;
-  p.BT = BT;
+  p.BT = R.BT;
+  p.hmap = R.hmap;
+  p.gmap = R.gmap;
+  p.lmap = R.lmap;
+  p.hidden_dense = R.dense;
+  p.grad_scale = grad_scale;
+  p.acc_gh = (flags & FLCE_ACCUMULATE_GRAD_HIDDEN) != 0;
+  p.acc_gw = (flags & FLCE_ACCUMULATE_GRAD_W) != 0;
   p.H = H;
   p.V = V;
   p.V_pad = round_up(V, flce::kTile);
@@ -189,9 +268,113 @@ Call make_call(flce_ctx* h, const Layout& L, int64_t BT, int64_t H, int64_t V, i
   w.dx_part = L.splits > 1 ? (float*)(base + L.off_part) : nullptr;
   w.params = (flce::DevParams*)(base + L.off_params);
   w.xt = base + L.off_xt;
+  w.xs = L.off_xs != L.total ? base + L.off_xs : nullptr;
   w.chunk_cap = L.chunk_rows;
   return c;
 }
+
+#define FLCE_LAUNCH(kind, expr)                                        \
+  do {                                                                 \
+    if (!call.run(kind, [&]() { return (expr); })) return FLCE_ERR_HIP; \
+  } while (0)
+
+// The fused forward + backward over the rows R (sizes already checked).
+int run_fused(flce_ctx* h, const void* hidden, const void* W, const int64_t* labels, const Rows& R, int64_t H,
+              int64_t V, int dtype, int64_t ignore_index, float softcap, int reduction, float grad_scale,
+              int flags, float* loss, void* grad_hidden, float* grad_W, void* workspace, size_t workspace_bytes,
+              void* stream_ptr) {
+  const int64_t BT = R.BT;
+  if (reduction == FLCE_NONE) return FLCE_ERR_UNSUPPORTED;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
+  if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_INVALID_ARG;
+  if (!W || !loss || !grad_W || !workspace) return FLCE_ERR_INVALID_ARG;
+  // grad_hidden is written on every row of the call and on the skipped last positions
+  const bool gh_rows = BT > 0 || (R.shift == 1 && R.B > 0 && R.T > 0);
+  if ((BT > 0 && (!hidden || !labels)) || (gh_rows && !grad_hidden)) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || !aligned(loss, 4) || !aligned(grad_W, 16) || !aligned(workspace, 256))
+    return FLCE_ERR_INVALID_ARG;
+  if (BT > 0 && (!aligned(hidden, 16) || !aligned(labels, 8))) return FLCE_ERR_INVALID_ARG;
+  if (gh_rows && !aligned(grad_hidden, 16)) return FLCE_ERR_INVALID_ARG;
+  const Layout L = layout(BT, H, V, dtype, h->chunk_rows_max, h->ncu, true, !R.dense);
+  if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+
+  DeviceGuard g(h->device);
+  if (!g.ok) return FLCE_ERR_HIP;
+  Call call = make_call(h, L, R, H, V, dtype, ignore_index, softcap, reduction, grad_scale, flags, workspace,
+                        stream_ptr);
+  const hipStream_t stream = call.stream;
+  const flce::Problem& p = call.p;
+  const flce::Work& w = call.w;
+
+  FLCE_LAUNCH(FLCE_K_PREPASS, flce::launch_prepass(p, labels, w, h->d_status, stream));
+  // the last position of each sequence is no row when labels are shifted: its gradient is zero
+  if (R.shift == 1 && R.T > 0 && !p.acc_gh)
+    FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_zero_rows(p, grad_hidden, R.B, (R.T - 1) * R.gmap.st, stream));
+  if (BT == 0) {
+    if (!p.acc_gw) FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_zero_f32(grad_W, V * H, stream));
+    FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
+    return FLCE_OK;
+  }
+  int64_t n_chunks, crows;
+  plan(BT, h->chunk_rows_max, &n_chunks, &crows);
+  for (int64_t ci = 0; ci < n_chunks; ++ci) {
+    const int64_t row0 = ci * crows;
+    const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
+    FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
+    FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, true, stream));
+    FLCE_LAUNCH(FLCE_K_MERGE, flce::launch_merge(p, w, row0, rows, stream));
+    int splits = L.splits > 1 ? dx_splits(rows, H, p.V_pad, dtype, h->ncu) : 1;
+    if (splits > L.splits) splits = L.splits;
+    FLCE_LAUNCH(FLCE_K_DX, flce::launch_dx(p, W, w, grad_hidden, row0, rows, splits, stream));
+    if (splits > 1)
+      FLCE_LAUNCH(FLCE_K_DX_REDUCE, flce::launch_dx_reduce(p, w, grad_hidden, row0, rows, splits, stream));
+    FLCE_LAUNCH(FLCE_K_DW, flce::launch_dw(p, hidden, w, grad_W, row0, rows, ci > 0 || p.acc_gw, stream));
+  }
+  FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
+  return FLCE_OK;
+}
+
+// The forward alone over the rows R (sizes already checked).
+int run_forward(flce_ctx* h, const void* hidden, const void* W, const int64_t* labels, const Rows& R, int64_t H,
+                int64_t V, int dtype, int64_t ignore_index, float softcap, int reduction, float* loss,
+                float* loss_rows, float* lse_rows, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  const int64_t BT = R.BT;
+  if (reduction != FLCE_NONE && reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
+  if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_INVALID_ARG;
+  if (!W || !workspace) return FLCE_ERR_INVALID_ARG;
+  if (reduction == FLCE_NONE ? (BT > 0 && !loss_rows) : !loss) return FLCE_ERR_INVALID_ARG;
+  if (BT > 0 && (!hidden || !labels)) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || !aligned(workspace, 256) || !aligned(loss, 4) || !aligned(loss_rows, 4) ||
+      !aligned(lse_rows, 4))
+    return FLCE_ERR_INVALID_ARG;
+  if (BT > 0 && (!aligned(hidden, 16) || !aligned(labels, 8))) return FLCE_ERR_INVALID_ARG;
+  const Layout L = layout(BT, H, V, dtype, h->chunk_rows_max, h->ncu, false);
+  if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+
+  DeviceGuard g(h->device);
+  if (!g.ok) return FLCE_ERR_HIP;
+  // per-row terms need no scale; the pre-pass's 1/N only matters for the reduced mean
+  const int red = reduction == FLCE_NONE ? FLCE_SUM : reduction;
+  Call call = make_call(h, L, R, H, V, dtype, ignore_index, softcap, red, 1.0f, 0, workspace, stream_ptr);
+  const hipStream_t stream = call.stream;
+  flce::Problem& p = call.p;
+  p.hidden_dense = true;  // no grad_W product: the transpose alone reads the mapped rows
+  const flce::Work& w = call.w;
+
+  FLCE_LAUNCH(FLCE_K_PREPASS, flce::launch_prepass(p, labels, w, h->d_status, stream));
+  int64_t n_chunks, crows;
+  plan(BT, h->chunk_rows_max, &n_chunks, &crows);
+  for (int64_t ci = 0; ci < n_chunks && BT > 0; ++ci) {
+    const int64_t row0 = ci * crows;
+    const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
+    FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
+    FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, false, stream));
+    FLCE_LAUNCH(FLCE_K_ROWS, flce::launch_rows(p, w, row0, rows, loss_rows, lse_rows, stream));
+  }
+  if (reduction != FLCE_NONE) FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
+  return FLCE_OK;
+}
+#undef FLCE_LAUNCH
 
 }  // namespace
 
@@ -260,55 +443,37 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
                           float softcap, int reduction, float* loss, void* grad_hidden, float* grad_W,
                           void* workspace, size_t workspace_bytes, void* stream_ptr) {
   if (!h) return FLCE_ERR_INVALID_ARG;
-  int rc = check_sizes(BT, H, V, dtype);
+  const int rc = check_sizes(BT, H, V, dtype);
   if (rc != FLCE_OK) return rc;
-  if (reduction == FLCE_NONE) return FLCE_ERR_UNSUPPORTED;
-  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
-  if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_INVALID_ARG;
-  if (!W || !loss || !grad_W || !workspace) return FLCE_ERR_INVALID_ARG;
-  if (BT > 0 && (!hidden || !labels || !grad_hidden)) return FLCE_ERR_INVALID_ARG;
-  if (!aligned(W, 16) || !aligned(loss, 4) || !aligned(grad_W, 16) || !aligned(workspace, 256))
-    return FLCE_ERR_INVALID_ARG;
-  if (BT > 0 && (!aligned(hidden, 16) || !aligned(labels, 8) || !aligned(grad_hidden, 16)))
-    return FLCE_ERR_INVALID_ARG;
-  const Layout L = layout(BT, H, V, dtype, h->chunk_rows_max, h->ncu);
-  if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  return run_fused(h, hidden, W, labels, plain_rows(BT, H), H, V, dtype, ignore_index, softcap, reduction, 1.0f,
+                   0, loss, grad_hidden, grad_W, workspace, workspace_bytes, stream_ptr);
+}
 
-  DeviceGuard g(h->device);
-  if (!g.ok) return FLCE_ERR_HIP;
-  Call call = make_call(h, L, BT, H, V, dtype, ignore_index, softcap, reduction, workspace, stream_ptr);
-  const hipStream_t stream = call.stream;
-  const flce::Problem& p = call.p;
-  const flce::Work& w = call.w;
-#define FLCE_LAUNCH(kind, expr)                                        \
-  do {                                                                 \
-    if (!call.run(kind, [&]() { return (expr); })) return FLCE_ERR_HIP; \
-  } while (0)
-
-  FLCE_LAUNCH(FLCE_K_PREPASS, flce::launch_prepass(p, labels, w, h->d_status, stream));
-  if (BT == 0) {
-    FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_zero_f32(grad_W, V * H, stream));
-    FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
-    return FLCE_OK;
-  }
-  int64_t n_chunks, crows;
-  plan(BT, h->chunk_rows_max, &n_chunks, &crows);
-  for (int64_t ci = 0; ci < n_chunks; ++ci) {
-    const int64_t row0 = ci * crows;
-    const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
-    FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
-    FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, true, stream));
-    FLCE_LAUNCH(FLCE_K_MERGE, flce::launch_merge(p, w, row0, rows, stream));
-    int splits = L.splits > 1 ? dx_splits(rows, H, p.V_pad, dtype, h->ncu) : 1;
-    if (splits > L.splits) splits = L.splits;
-    FLCE_LAUNCH(FLCE_K_DX, flce::launch_dx(p, W, w, grad_hidden, row0, rows, splits, stream));
-    if (splits > 1)
-      FLCE_LAUNCH(FLCE_K_DX_REDUCE, flce::launch_dx_reduce(p, w, grad_hidden, row0, rows, splits, stream));
-    FLCE_LAUNCH(FLCE_K_DW, flce::launch_dw(p, hidden, w, grad_W, row0, rows, ci > 0, stream));
-  }
-  FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
-#undef FLCE_LAUNCH
+int flce_workspace_size_rows(flce_handle h, const flce_rows* rows, int64_t H, int64_t V, int dtype,
+                             size_t* bytes) {
+  if (!bytes || !rows) return FLCE_ERR_INVALID_ARG;
+  Rows R;
+  int rc = check_rows(rows, H, dtype, true, &R);
+  if (rc == FLCE_OK) rc = check_sizes(R.BT, H, V, dtype);
+  if (rc != FLCE_OK) return rc;
+  *bytes = layout(R.BT, H, V, dtype, chunk_max_of(h), ncu_of(h), true, !R.dense).total;
   return FLCE_OK;
+}
+
+int flce_forward_backward_rows(flce_handle h, const void* hidden, const void* W, const int64_t* labels,
+                               const flce_rows* rows, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                               float softcap, int reduction, float grad_scale, int flags, float* loss,
+                               void* grad_hidden, float* grad_W, void* workspace, size_t workspace_bytes,
+                               void* stream_ptr) {
+  if (!h || !rows) return FLCE_ERR_INVALID_ARG;
+  Rows R;
+  int rc = check_rows(rows, H, dtype, true, &R);
+  if (rc == FLCE_OK) rc = check_sizes(R.BT, H, V, dtype);
+  if (rc != FLCE_OK) return rc;
+  if (!std::isfinite(grad_scale)) return FLCE_ERR_INVALID_ARG;
+  if (flags & ~(FLCE_ACCUMULATE_GRAD_HIDDEN | FLCE_ACCUMULATE_GRAD_W)) return FLCE_ERR_INVALID_ARG;
+  return run_fused(h, hidden, W, labels, R, H, V, dtype, ignore_index, softcap, reduction, grad_scale, flags, loss,
+                   grad_hidden, grad_W, workspace, workspace_bytes, stream_ptr);
 }
 
 int flce_forward_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, size_t* bytes) {
@@ -323,46 +488,23 @@ int flce_forward(flce_handle h, const void* hidden, const void* W, const int64_t
                  int64_t V, int dtype, int64_t ignore_index, float softcap, int reduction, float* loss,
                  float* loss_rows, float* lse_rows, void* workspace, size_t workspace_bytes, void* stream_ptr) {
   if (!h) return FLCE_ERR_INVALID_ARG;
-  int rc = check_sizes(BT, H, V, dtype);
+  const int rc = check_sizes(BT, H, V, dtype);
   if (rc != FLCE_OK) return rc;
-  if (reduction != FLCE_NONE && reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
-  if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_INVALID_ARG;
-  if (!W || !workspace) return FLCE_ERR_INVALID_ARG;
-  if (reduction == FLCE_NONE ? (BT > 0 && !loss_rows) : !loss) return FLCE_ERR_INVALID_ARG;
-  if (BT > 0 && (!hidden || !labels)) return FLCE_ERR_INVALID_ARG;
-  if (!aligned(W, 16) || !aligned(workspace, 256) || !aligned(loss, 4) || !aligned(loss_rows, 4) ||
-      !aligned(lse_rows, 4))
-    return FLCE_ERR_INVALID_ARG;
-  if (BT > 0 && (!aligned(hidden, 16) || !aligned(labels, 8))) return FLCE_ERR_INVALID_ARG;
-  const Layout L = layout(BT, H, V, dtype, h->chunk_rows_max, h->ncu, false);
-  if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  return run_forward(h, hidden, W, labels, plain_rows(BT, H), H, V, dtype, ignore_index, softcap, reduction, loss,
+                     loss_rows, lse_rows, workspace, workspace_bytes, stream_ptr);
+}
 
-  DeviceGuard g(h->device);
-  if (!g.ok) return FLCE_ERR_HIP;
-  // per-row terms need no scale; the pre-pass's 1/N only matters for the reduced mean
-  const int red = reduction == FLCE_NONE ? FLCE_SUM : reduction;
-  Call call = make_call(h, L, BT, H, V, dtype, ignore_index, softcap, red, workspace, stream_ptr);
-  const hipStream_t stream = call.stream;
-  const flce::Problem& p = call.p;
-  const flce::Work& w = call.w;
-#define FLCE_LAUNCH(kind, expr)                                        \
-  do {                                                                 \
-    if (!call.run(kind, [&]() { return (expr); })) return FLCE_ERR_HIP; \
-  } while (0)
-
-  FLCE_LAUNCH(FLCE_K_PREPASS, flce::launch_prepass(p, labels, w, h->d_status, stream));
-  int64_t n_chunks, crows;
-  plan(BT, h->chunk_rows_max, &n_chunks, &crows);
-  for (int64_t ci = 0; ci < n_chunks && BT > 0; ++ci) {
-    const int64_t row0 = ci * crows;
-    const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
-    FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
-    FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, false, stream));
-    FLCE_LAUNCH(FLCE_K_ROWS, flce::launch_rows(p, w, row0, rows, loss_rows, lse_rows, stream));
-  }
-  if (reduction != FLCE_NONE) FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
-#undef FLCE_LAUNCH
-  return FLCE_OK;
+int flce_forward_rows(flce_handle h, const void* hidden, const void* W, const int64_t* labels, const flce_rows* rows,
+                      int64_t H, int64_t V, int dtype, int64_t ignore_index, float softcap, int reduction,
+                      float* loss, float* loss_rows, float* lse_rows, void* workspace, size_t workspace_bytes,
+                      void* stream_ptr) {
+  if (!h || !rows) return FLCE_ERR_INVALID_ARG;
+  Rows R;
+  int rc = check_rows(rows, H, dtype, false, &R);
+  if (rc == FLCE_OK) rc = check_sizes(R.BT, H, V, dtype);
+  if (rc != FLCE_OK) return rc;
+  return run_forward(h, hidden, W, labels, R, H, V, dtype, ignore_index, softcap, reduction, loss, loss_rows,
+                     lse_rows, workspace, workspace_bytes, stream_ptr);
 }
 
 int flce_status(flce_handle h, void* stream) {

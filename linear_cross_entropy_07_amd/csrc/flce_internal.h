@@ -20,10 +20,22 @@ constexpr int kRowAlign = 256;  // chunk sizes are multiples of this
 constexpr int kStepBytes = FLCE_STEP_BYTES;  // bytes of K per GEMM pipeline step (64 or 128)
 constexpr int kPipeStages = FLCE_STAGES;     // LDS stages of the GEMM pipeline
 
+// Row r of a call -> element offset of its first element in a tensor of sequences: r = b * per + t
+// (per = rows per sequence), offset = b * sb + t * st + base. The plain [BT][ld] layout is
+// {sb = ld, st = 0, base = 0, per = 1}. Row indices and per fit in 31 bits.
+struct RowMap {
+  int64_t sb, st, base;
+  uint32_t per;
+  __host__ __device__ __forceinline__ int64_t operator()(int64_t r) const {
+    const uint32_t b = (uint32_t)r / per, t = (uint32_t)r - b * per;
+    return (int64_t)b * sb + (int64_t)t * st + base;
+  }
+};
+
 // Per-call device parameters written by the label pre-pass and read by later kernels.
 struct DevParams {
   int n_valid;   // N = number of rows whose label is in [0, V)
-  float ginv;    // 1/N (mean, N > 0), 0 (mean, N == 0), 1 (sum)
+  float ginv;    // grad_scale * (1/N (mean, N > 0), 0 (mean, N == 0), 1 (sum))
   int status;    // bit 0: a label outside [0, V) that is not ignore_index was seen
   int pad;
 };
@@ -39,6 +51,7 @@ struct Work {
   float* loss_row;     // [BT]
   float* dx_part;      // [splits][chunk_rows][H] fp32 split-K partials of grad_hidden (may be null)
   void* xt;            // [H][chunk_cap] the current chunk of hidden, transposed
+  void* xs;            // [chunk_cap][H] the current chunk of hidden, gathered (only for mapped rows)
   int64_t chunk_cap;   // row capacity of one chunk (a multiple of 256)
   DevParams* params;   // in the workspace
 };
@@ -50,6 +63,12 @@ struct Problem {
   float softcap;
   int reduction;       // 1 mean, 2 sum
   int ncu;             // compute units of the device (sizes persistent grids)
+  RowMap hmap;         // rows of hidden (elements)
+  RowMap gmap;         // rows of grad_hidden (elements)
+  RowMap lmap;         // labels (elements)
+  bool hidden_dense;   // hmap is the plain [BT][H] layout: the grad_W product reads hidden directly
+  float grad_scale;    // multiplies both gradients
+  bool acc_gh, acc_gw; // add into grad_hidden / grad_W instead of overwriting
 };
 
 // Launchers (all enqueue on `stream`, return hipError_t of the launch).
@@ -64,6 +83,9 @@ hipError_t launch_rows(const Problem& p, const Work& w, int64_t row0, int64_t ro
 hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream);
 hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_hidden, int64_t row0,
                      int64_t rows, int splits, hipStream_t stream);
+// grad_hidden rows that are no rows of the call (the last position of each sequence when labels are
+// shifted): zero-filled. B sequences, element offset `off` of the row in sequence 0.
+hipError_t launch_zero_rows(const Problem& p, void* grad_hidden, int64_t B, int64_t off, hipStream_t stream);
 hipError_t launch_dx_reduce(const Problem& p, const Work& w, void* grad_hidden, int64_t row0, int64_t rows,
                             int splits, hipStream_t stream);
 hipError_t launch_dw(const Problem& p, const void* hidden, const Work& w, float* grad_W, int64_t row0,

@@ -90,6 +90,11 @@ __device__ __forceinline__ void unpack(u32x4 v, float (&f)[8], _Float16*) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
 }
+__device__ __forceinline__ void unpack(u32x4 v, float (&f)[8], __bf16*) {
+  const f32x8 h = __builtin_convertvector(__builtin_bit_cast(bf16x8, v), f32x8);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = h[i];
+}
 __device__ __forceinline__ void unpack(u32x4 v, float (&f)[4], float*) {
   const f32x4 h = __builtin_bit_cast(f32x4, v);
 #pragma unroll
@@ -508,10 +513,12 @@ struct FwdArgs {
 struct DxArgs {
   const void* W;
   const void* ws;     // dZ of the chunk, [rows][V_pad]
-  void* out;          // grad_hidden, chunk row 0 (splits == 1)
+  void* out;          // grad_hidden (splits == 1): row r of the call starts at element gmap(r)
+  RowMap gmap;
+  int64_t row0;       // call row of chunk row 0
   float* part;        // [splits][rows][H] (splits > 1)
   int64_t H, V, V_pad;
-  int rows, splits, ksteps_per_split;
+  int rows, splits, ksteps_per_split, accumulate;
 };
 
 struct DwArgs {
@@ -778,6 +785,64 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
 }
 
 // ---- grad_hidden = dZ . W ---------------------------------------------------------------------
+// The fp32 tile goes through the (then idle) LDS ring in passes of kDxPassRows rows, one wave row-half
+// (WM rows) per pass, and leaves as 16-byte pieces of whole caller rows: each row is placed by the row
+// map (sequences with strides, shifted labels), and with `accumulate` added to what the row holds
+// (one rounding to the output type, after the add).
+constexpr int kDxRowBytes = TILE * 4;
+constexpr int kDxPassRows = WM;
+static_assert(kDxPassRows * kDxRowBytes <= kStages * kStageBytes, "a pass fits the LDS ring");
+template <typename T>
+__device__ __forceinline__ void dx_store_tile(const DxArgs& a, const f32x16 (&acc)[TBM][TBN], int c0, int h0,
+                                              int vrows, char* smem) {
+  constexpr int OV = 16 / (int)sizeof(T);  // output elements per 16-byte store
+  constexpr int TPR = TILE / OV;           // threads per row
+  constexpr int RPI = NTHR / TPR;          // rows per read-out iteration
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1, half = lane >> 5;
+  const int ch = (int)threadIdx.x % TPR, h = h0 + ch * OV;
+#pragma unroll
+  for (int pass = 0; pass < TILE / kDxPassRows; ++pass) {
+    if (wm == pass) {
+#pragma unroll
+      for (int i = 0; i < TBM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+#pragma unroll
+          for (int j = 0; j < TBN; ++j) {
+            const int cl = wn * WN + 32 * j + (lane & 31);
+            *(float*)(smem + rl * kDxRowBytes + cl * 4) = acc[i][j][r];
+          }
+        }
+    }
+    __syncthreads();
+    for (int rl = (int)threadIdx.x / TPR; rl < kDxPassRows; rl += RPI) {
+      const int c = pass * kDxPassRows + rl;
+      if (c < vrows && h < a.H) {
+        const float* src = (const float*)(smem + rl * kDxRowBytes) + ch * OV;
+        float f[OV];
+#pragma unroll
+        for (int e = 0; e < OV; e += 4) {
+          const f32x4 v = *(const f32x4*)(src + e);
+          f[e] = v[0];
+          f[e + 1] = v[1];
+          f[e + 2] = v[2];
+          f[e + 3] = v[3];
+        }
+        T* dst = (T*)a.out + a.gmap(a.row0 + c0 + c) + h;
+        if (a.accumulate) {
+          float o[OV];
+          unpack(*(const u32x4*)dst, o, (T*)nullptr);
+#pragma unroll
+          for (int e = 0; e < OV; ++e) f[e] += o[e];
+        }
+        *(u32x4*)dst = pack(f, (T*)nullptr);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes];
@@ -800,26 +865,10 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
   f32x16 acc[TBM][TBN];
   gemm_core<T, kSchedDx>(la, lb, kb, ke, smem, acc);
 
-  // row-major [rows][H] output tile at (c0, h0); rows past the chunk and columns past H are dropped
+  // output tile (c0, h0); rows past the chunk and columns past H are dropped
   const int vrows = min(TILE, a.rows - c0), ncols = (int)min<int64_t>(TILE, a.H - h0);
   if (a.splits == 1) {
-    const rsrc_t ro = make_rsrc((T*)a.out + (int64_t)c0 * a.H + h0, ((int64_t)vrows * a.H - h0) * (int64_t)sizeof(T));
-    const AccAddr<sizeof(T)> ad((int)a.H, ncols);
-#pragma unroll
-    for (int i = 0; i < TBM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const u32 so = ad.row(i, r);
-#pragma unroll
-        for (int j = 0; j < TBN; ++j) {
-          if constexpr (sizeof(T) == 2)
-            bstore_b16(ro, ad.col[j], so, __builtin_bit_cast(unsigned short, (T)acc[i][j][r]));
-          else
-            bstore_f32(ro, ad.col[j], so, acc[i][j][r]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    dx_store_tile<T>(a, acc, c0, h0, vrows, smem);
   } else {
     const rsrc_t ro = make_rsrc(a.part + ((int64_t)split * a.rows + c0) * a.H + h0, ((int64_t)vrows * a.H - h0) * 4);
     const AccAddr<4> ad((int)a.H, ncols);
@@ -834,14 +883,22 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
   }
 }
 
-// Fixed-order sum of the split-K partials of grad_hidden.
+// Fixed-order sum of the split-K partials of grad_hidden, placed by the row map (and added to what the
+// row holds with `accumulate`). Blocks: x over H, y over chunk rows (grid-stride).
 template <typename T>
-__global__ __launch_bounds__(256) void k_dx_reduce(const float* part, int splits, int64_t n, T* out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  float s = 0.0f;
-  for (int k = 0; k < splits; ++k) s += part[(int64_t)k * n + i];
-  out[i] = (T)s;
+__global__ __launch_bounds__(256) void k_dx_reduce(const float* part, int splits, int rows, int64_t H, T* out,
+                                                   RowMap gmap, int64_t row0, int accumulate) {
+  const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (h >= H) return;
+  const int64_t n = (int64_t)rows * H;
+  for (int c = blockIdx.y; c < rows; c += gridDim.y) {
+    const int64_t i = (int64_t)c * H + h;
+    float s = 0.0f;
+    for (int k = 0; k < splits; ++k) s += part[(int64_t)k * n + i];
+    T* dst = out + gmap(row0 + c) + h;
+    if (accumulate) s += (float)*dst;
+    *dst = (T)s;
+  }
 }
 
 // ---- grad_W (+)= dZ^T . X -----------------------------------------------------------------------
@@ -903,15 +960,24 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
 }
 
 // ---- hidden chunk transpose: [rows][H] -> [H][ldt] through a 64 x 64 LDS tile ------------------
+// Row r of the chunk is call row row0 + r, found in hidden by the row map; with Xs the chunk is also
+// gathered into a plain [rows][H] copy (for the grad_W product when the rows are mapped).
 template <typename T>
-__global__ __launch_bounds__(256) void k_transpose(const T* X, int rows, int H, T* XT, int64_t ldt) {
+__global__ __launch_bounds__(256) void k_transpose(const T* X, RowMap hmap, int64_t row0, int rows, int H, T* XT,
+                                                   int64_t ldt, T* Xs) {
   __shared__ T tile[64][65];
+  __shared__ int64_t roff[64];
   const int r0 = blockIdx.y * 64, h0 = blockIdx.x * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  if (threadIdx.x < 64) roff[tx] = r0 + tx < rows ? hmap(row0 + r0 + tx) : 0;
+  __syncthreads();
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int r = r0 + ty + 4 * k, h = h0 + tx;
-    tile[ty + 4 * k][tx] = (r < rows && h < H) ? X[(int64_t)r * H + h] : (T)0.0f;
+    const bool in = r < rows && h < H;
+    const T v = in ? X[roff[ty + 4 * k] + h] : (T)0.0f;
+    tile[ty + 4 * k][tx] = v;
+    if (Xs && in) Xs[(int64_t)r * H + h] = v;
   }
   __syncthreads();
 #pragma unroll
@@ -934,14 +1000,14 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Label pre-pass: one block. y32 = label or -1 (ignored or out of range), N, 1/N, status.
-__global__ __launch_bounds__(1024) void k_prepass(const int64_t* labels, int64_t BT, int64_t V,
-                                                  int64_t ignore_index, int reduction, int* y32,
-                                                  DevParams* prm, int* status_out) {
+__global__ __launch_bounds__(1024) void k_prepass(const int64_t* labels, RowMap lmap, int64_t BT, int64_t V,
+                                                  int64_t ignore_index, int reduction, float grad_scale,
+                                                  int* y32, DevParams* prm, int* status_out) {
   __shared__ int s_cnt[1024];
   __shared__ int s_bad[1024];
   int cnt = 0, bad = 0;
   for (int64_t t = threadIdx.x; t < BT; t += 1024) {
-    const int64_t y = labels[t];
+    const int64_t y = labels[lmap(t)];
     const bool counted = y != ignore_index;
     const bool out = counted && (y < 0 || y >= V);
     const bool ok = counted && !out;
@@ -962,7 +1028,7 @@ __global__ __launch_bounds__(1024) void k_prepass(const int64_t* labels, int64_t
   if (threadIdx.x == 0) {
     const int n = s_cnt[0];
     prm->n_valid = n;
-    prm->ginv = reduction == 1 ? (n > 0 ? 1.0f / (float)n : 0.0f) : 1.0f;
+    prm->ginv = grad_scale * (reduction == 1 ? (n > 0 ? 1.0f / (float)n : 0.0f) : 1.0f);
     prm->status = s_bad[0];
     *status_out = s_bad[0];
   }
@@ -1076,25 +1142,35 @@ __global__ __launch_bounds__(256) void k_zero(float* p, int64_t n) {
   if (i < n) p[i] = 0.0f;
 }
 
+// Rows b * sb + off (b < B) of H elements set to zero. Blocks: x over H, y over b (grid-stride).
+template <typename T>
+__global__ __launch_bounds__(256) void k_zero_rows(T* p, int64_t B, int64_t sb, int64_t off, int64_t H) {
+  const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (h >= H) return;
+  for (int64_t b = blockIdx.y; b < B; b += gridDim.y) p[b * sb + off + h] = (T)0.0f;
+}
+
 }  // namespace
 
 // ---- launchers ------------------------------------------------------------------------------
 hipError_t launch_prepass(const Problem& p, const int64_t* labels, const Work& w, int* status_out,
                           hipStream_t stream) {
-  k_prepass<<<1, 1024, 0, stream>>>(labels, p.BT, p.V, p.ignore_index, p.reduction, w.y32, w.params,
-                                    status_out);
+  k_prepass<<<1, 1024, 0, stream>>>(labels, p.lmap, p.BT, p.V, p.ignore_index, p.reduction, p.grad_scale,
+                                    w.y32, w.params, status_out);
   return hipGetLastError();
 }
 
 hipError_t launch_transpose(const Problem& p, const void* hidden, const Work& w, int64_t row0, int64_t rows,
                             hipStream_t stream) {
   const dim3 grid((unsigned)((p.H + 63) / 64), (unsigned)((rows + 63) / 64));
+  if (!p.hidden_dense && !w.xs) return hipErrorInvalidValue;
+  void* xs = p.hidden_dense ? nullptr : w.xs;
   if (p.dtype == 0)
-    k_transpose<__bf16><<<grid, 256, 0, stream>>>((const __bf16*)hidden + row0 * p.H, (int)rows, (int)p.H,
-                                                  (__bf16*)w.xt, w.chunk_cap);
+    k_transpose<__bf16><<<grid, 256, 0, stream>>>((const __bf16*)hidden, p.hmap, row0, (int)rows, (int)p.H,
+                                                  (__bf16*)w.xt, w.chunk_cap, (__bf16*)xs);
   else
-    k_transpose<float><<<grid, 256, 0, stream>>>((const float*)hidden + row0 * p.H, (int)rows, (int)p.H,
-                                                 (float*)w.xt, w.chunk_cap);
+    k_transpose<float><<<grid, 256, 0, stream>>>((const float*)hidden, p.hmap, row0, (int)rows, (int)p.H,
+                                                 (float*)w.xt, w.chunk_cap, (float*)xs);
   return hipGetLastError();
 }
 
@@ -1156,10 +1232,14 @@ hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_
                      int64_t rows, int splits, hipStream_t stream) {
   const size_t esz = p.dtype == 0 ? 2 : 4;
   const int nk = (int)(p.V_pad * (p.dtype == 0 ? 2 : 4) / kStepBytes);
+  (void)esz;
   DxArgs a;
   a.W = W;
   a.ws = w.ws_e;
-  a.out = (char*)grad_hidden + row0 * p.H * esz;
+  a.out = grad_hidden;
+  a.gmap = p.gmap;
+  a.row0 = row0;
+  a.accumulate = p.acc_gh ? 1 : 0;
   a.part = w.dx_part;
   a.H = p.H;
   a.V = p.V;
@@ -1177,22 +1257,34 @@ hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_
 
 hipError_t launch_dx_reduce(const Problem& p, const Work& w, void* grad_hidden, int64_t row0, int64_t rows,
                             int splits, hipStream_t stream) {
-  const size_t esz = p.dtype == 0 ? 2 : 4;
-  void* out = (char*)grad_hidden + row0 * p.H * esz;
-  const int64_t n = rows * p.H;
-  const unsigned g2 = (unsigned)((n + 255) / 256);
+  const dim3 grid((unsigned)((p.H + 255) / 256), (unsigned)(rows < 65535 ? rows : 65535));
+  const int acc = p.acc_gh ? 1 : 0;
   if (p.dtype == 0)
-    k_dx_reduce<__bf16><<<g2, 256, 0, stream>>>(w.dx_part, splits, n, (__bf16*)out);
+    k_dx_reduce<__bf16><<<grid, 256, 0, stream>>>(w.dx_part, splits, (int)rows, p.H, (__bf16*)grad_hidden, p.gmap,
+                                                  row0, acc);
   else
-    k_dx_reduce<float><<<g2, 256, 0, stream>>>(w.dx_part, splits, n, (float*)out);
+    k_dx_reduce<float><<<grid, 256, 0, stream>>>(w.dx_part, splits, (int)rows, p.H, (float*)grad_hidden, p.gmap,
+                                                 row0, acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_rows(const Problem& p, void* grad_hidden, int64_t B, int64_t off, hipStream_t stream) {
+  if (B <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((p.H + 255) / 256), (unsigned)(B < 65535 ? B : 65535));
+  if (p.dtype == 0)
+    k_zero_rows<__bf16><<<grid, 256, 0, stream>>>((__bf16*)grad_hidden, B, p.gmap.sb, off, p.H);
+  else
+    k_zero_rows<float><<<grid, 256, 0, stream>>>((float*)grad_hidden, B, p.gmap.sb, off, p.H);
   return hipGetLastError();
 }
 
 hipError_t launch_dw(const Problem& p, const void* hidden, const Work& w, float* grad_W, int64_t row0,
                      int64_t rows, bool accumulate, hipStream_t stream) {
   const size_t esz = p.dtype == 0 ? 2 : 4;
+  if (!p.hidden_dense && !w.xs) return hipErrorInvalidValue;
   DwArgs a;
-  a.X = (const char*)hidden + row0 * p.H * esz;
+  // rows in the plain layout are read where they are; mapped rows from the chunk's gathered copy
+  a.X = p.hidden_dense ? (const void*)((const char*)hidden + row0 * p.H * esz) : (const void*)w.xs;
   a.ws = w.ws_e;
   a.dW = grad_W;
   a.H = p.H;

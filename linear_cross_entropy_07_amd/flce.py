@@ -39,6 +39,17 @@ class _Config(ctypes.Structure):
     _fields_ = [("chunk_rows_max", ctypes.c_int64), ("reserved", ctypes.c_int64 * 3)]
 
 
+class Rows(ctypes.Structure):
+    """flce_rows: B sequences of T positions at element strides; shift = 1 scores position t
+    against the label at t + 1 and leaves the last position out."""
+    _fields_ = [("batch", ctypes.c_int64), ("seq", ctypes.c_int64), ("shift", ctypes.c_int64),
+                ("hidden_stride", ctypes.c_int64 * 2), ("grad_hidden_stride", ctypes.c_int64 * 2),
+                ("label_stride", ctypes.c_int64 * 2)]
+
+
+FLCE_ACCUMULATE_GRAD_HIDDEN, FLCE_ACCUMULATE_GRAD_W = 1, 2
+
+
 _LIB = None
 _LOCK = threading.Lock()
 
@@ -67,6 +78,12 @@ def lib() -> ctypes.CDLL:
             L.flce_forward_workspace_size.argtypes = [vp, i64, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
             L.flce_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, ctypes.c_float, i32,
                                        vp, vp, vp, vp, ctypes.c_size_t, vp]
+            rp = ctypes.POINTER(Rows)
+            L.flce_workspace_size_rows.argtypes = [vp, rp, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
+            L.flce_forward_backward_rows.argtypes = [vp, vp, vp, vp, rp, i64, i64, i32, i64, ctypes.c_float, i32,
+                                                     ctypes.c_float, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            L.flce_forward_rows.argtypes = [vp, vp, vp, vp, rp, i64, i64, i32, i64, ctypes.c_float, i32,
+                                            vp, vp, vp, vp, ctypes.c_size_t, vp]
             L.flce_status.argtypes = [vp, vp]
             L.flce_profile_begin.argtypes = [vp, i32]
             L.flce_profile_end.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
@@ -74,6 +91,7 @@ def lib() -> ctypes.CDLL:
             L.flce_error_string.restype = ctypes.c_char_p
             for f in ("flce_create", "flce_destroy", "flce_workspace_size", "flce_chunk_plan",
                       "flce_forward_backward", "flce_forward_workspace_size", "flce_forward", "flce_status",
+                      "flce_workspace_size_rows", "flce_forward_backward_rows", "flce_forward_rows",
                       "flce_profile_begin", "flce_profile_end"):
                 getattr(L, f).restype = i32
             _LIB = L
@@ -96,6 +114,13 @@ def forward_workspace_size(BT: int, H: int, V: int, dtype=torch.bfloat16, handle
     out = ctypes.c_size_t()
     _check(lib().flce_forward_workspace_size(handle, BT, H, V, _DTYPES[dtype], ctypes.byref(out)),
            "flce_forward_workspace_size")
+    return out.value
+
+
+def workspace_size_rows(rows: Rows, H: int, V: int, dtype=torch.bfloat16, handle=None) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().flce_workspace_size_rows(handle, ctypes.byref(rows), H, V, _DTYPES[dtype], ctypes.byref(out)),
+           "flce_workspace_size_rows")
     return out.value
 
 
@@ -219,6 +244,100 @@ class FLCE:
             workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
         _check(rc, "flce_forward")
         out = loss if reduction != "none" else rows
+        return (out, lse) if return_lse else out
+
+    def _seq_rows(self, hidden: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, shift: bool,
+                  grad_hidden: torch.Tensor | None = None) -> tuple:
+        if hidden.dim() != 3 or W.dim() != 2 or labels.dim() != 2:
+            raise ValueError("hidden [B,T,H], W [V,H], labels [B,T] expected")
+        B, T, H = hidden.shape
+        V = W.shape[0]
+        if W.shape[1] != H or tuple(labels.shape) != (B, T):
+            raise ValueError(f"shape mismatch: hidden {tuple(hidden.shape)}, W {tuple(W.shape)}, "
+                             f"labels {tuple(labels.shape)}")
+        if hidden.dtype != W.dtype or hidden.dtype not in _DTYPES:
+            raise TypeError("hidden and W must both be bfloat16 or both float32")
+        if labels.dtype != torch.int64:
+            raise TypeError("labels must be int64")
+        for name, t in (("hidden", hidden), ("W", W), ("labels", labels), ("grad_hidden", grad_hidden)):
+            if t is not None and t.device != self.device:
+                raise ValueError(f"{name} is on {t.device}, handle is on {self.device}")
+        if not W.is_contiguous():
+            raise ValueError("W must be contiguous")
+        if hidden.stride(2) != 1 or (grad_hidden is not None and grad_hidden.stride(2) != 1):
+            raise ValueError("hidden and grad_hidden rows must be contiguous (unit stride along H)")
+        if grad_hidden is not None and (tuple(grad_hidden.shape) != (B, T, H) or grad_hidden.dtype != hidden.dtype):
+            raise ValueError("grad_hidden must match hidden's shape and dtype")
+        g = grad_hidden if grad_hidden is not None else hidden
+        r = Rows(B, T, 1 if shift else 0, (ctypes.c_int64 * 2)(hidden.stride(0), hidden.stride(1)),
+                 (ctypes.c_int64 * 2)(g.stride(0), g.stride(1)),
+                 (ctypes.c_int64 * 2)(labels.stride(0), labels.stride(1)))
+        return r, B, T, H, V
+
+    def forward_backward_seq(self, hidden: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, shift: bool = True,
+                             ignore_index: int = -100, softcap: float = 0.0, reduction: str = "mean",
+                             grad_scale: float = 1.0, grad_hidden: torch.Tensor | None = None,
+                             grad_W: torch.Tensor | None = None, accumulate_grad_hidden: bool = False,
+                             accumulate_grad_W: bool = False, loss: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None, stream=None):
+        """Fused forward + backward over a batch of sequences hidden [B,T,H] (any strides with H
+        contiguous) and labels [B,T]; with shift, position t is scored against label t+1 and the
+        last position gets no gradient of its own. Gradients are multiplied by grad_scale and
+        written into (or, with the accumulate flags, added to) grad_hidden [B,T,H] and grad_W
+        [V,H] fp32, allocated when not given. Returns (loss, grad_hidden, grad_W)."""
+        if reduction not in _REDUCTIONS:
+            raise ValueError("reduction must be 'mean' or 'sum'")
+        if accumulate_grad_hidden and grad_hidden is None or accumulate_grad_W and grad_W is None:
+            raise ValueError("accumulating needs the gradient tensor to add to")
+        if grad_hidden is None:
+            grad_hidden = torch.empty(hidden.shape, dtype=hidden.dtype, device=self.device)
+        rows, B, T, H, V = self._seq_rows(hidden, W, labels, shift, grad_hidden)
+        if grad_W is None:
+            grad_W = torch.empty((V, H), dtype=torch.float32, device=self.device)
+        if tuple(grad_W.shape) != (V, H) or grad_W.dtype != torch.float32 or not grad_W.is_contiguous() \
+                or grad_W.device != self.device:
+            raise ValueError("grad_W must be a contiguous [V,H] float32 tensor on the handle's device")
+        if loss is None:
+            loss = torch.empty((), dtype=torch.float32, device=self.device)
+        flags = (FLCE_ACCUMULATE_GRAD_HIDDEN if accumulate_grad_hidden else 0) | \
+                (FLCE_ACCUMULATE_GRAD_W if accumulate_grad_W else 0)
+        need = workspace_size_rows(rows, H, V, hidden.dtype, self._h)
+        if workspace is None:
+            workspace = self.workspace(need)
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        rc = lib().flce_forward_backward_rows(
+            self._h, hidden.data_ptr(), W.data_ptr(), labels.data_ptr(), ctypes.byref(rows), H, V,
+            _DTYPES[hidden.dtype], int(ignore_index), float(softcap), _REDUCTIONS[reduction], float(grad_scale),
+            flags, loss.data_ptr(), grad_hidden.data_ptr(), grad_W.data_ptr(), workspace.data_ptr(),
+            workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+        _check(rc, "flce_forward_backward_rows")
+        return loss, grad_hidden, grad_W
+
+    def forward_seq(self, hidden: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, shift: bool = True,
+                    ignore_index: int = -100, softcap: float = 0.0, reduction: str = "mean",
+                    return_lse: bool = False, workspace: torch.Tensor | None = None, stream=None):
+        """Forward only over a batch of sequences (as forward_backward_seq). Returns the loss, or
+        for 'none' the per-row terms [B, T - shift]; with return_lse also lse [B, T - shift]."""
+        if reduction not in _FWD_REDUCTIONS:
+            raise ValueError("reduction must be 'none', 'mean' or 'sum'")
+        rows, B, T, H, V = self._seq_rows(hidden, W, labels, shift)
+        P = max(T - rows.shift, 0)
+        need = forward_workspace_size(B * P, H, V, hidden.dtype, self._h)
+        if workspace is None:
+            workspace = self.workspace(need)
+        loss = torch.empty((), dtype=torch.float32, device=self.device) if reduction != "none" else None
+        per = torch.empty((B, P), dtype=torch.float32, device=self.device) if reduction == "none" else None
+        lse = torch.empty((B, P), dtype=torch.float32, device=self.device) if return_lse else None
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        rc = lib().flce_forward_rows(
+            self._h, hidden.data_ptr(), W.data_ptr(), labels.data_ptr(), ctypes.byref(rows), H, V,
+            _DTYPES[hidden.dtype], int(ignore_index), float(softcap), _FWD_REDUCTIONS[reduction], ptr(loss),
+            ptr(per), ptr(lse), workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+        _check(rc, "flce_forward_rows")
+        out = loss if reduction != "none" else per
         return (out, lse) if return_lse else out
 
     KERNELS = ("prepass", "fwd", "merge", "dx", "dx_reduce", "dw", "finalize", "transpose", "rows")

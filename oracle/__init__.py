@@ -13,4 +13,5 @@ from .flce_oracle import (  # noqa: F401
     flce_forward_backward,
     flce_forward,
     flce_rows,
+    flce_sequences,
 )

@@ -52,6 +52,7 @@ __all__ = [
     "valid_mask",
     "flce_forward_backward",
     "flce_rows",
+    "flce_sequences",
 ]
 
 
@@ -209,3 +210,36 @@ def flce_rows(X, W, y, rows, n_valid: int, ignore_index: int = -100, softcap: fl
     t = _row_terms(Xr, Wf, yr, ignore_index, softcap, reduction, n_valid)
     return dict(lse=t["lse"], loss_rows=t["loss_rows"], dX=t["dZ"] @ Wf, valid=t["valid"],
                 s_label=t["s_label"])
+
+
+def flce_sequences(X3, W, Y2, shift: int = 1, ignore_index: int = -100, softcap: float = 0.0,
+                   reduction: str = "mean", grad_scale: float = 1.0, dX_init=None, dW_init=None):
+    """The same loss over a batch of sequences, with the next-token shift done by indexing.
+
+    X3: [B, T, H], Y2: [B, T]. With shift = 1 the position t < T-1 of sequence b is scored against
+    the label at (b, t+1) and the last position is not scored: the shift that the training loop in
+    torchtune issue #1228 ("[FEATURE REQUEST] Compile model+loss_fn together") makes by slicing the
+    logits and labels; shift = 0 scores every position against its own label. The gradients are
+    multiplied by grad_scale (the upstream gradient of the loss, e.g. the loss / accumulation-steps
+    division of that loop) and added to dX_init / dW_init when given. The last positions get no
+    gradient of their own (0 + dX_init there).
+
+    Returns (loss, dX3 [B, T, H] f64, dW [V, H] f64, loss_rows [B * (T - shift)], lse [B * (T - shift)]),
+    rows numbered b * (T - shift) + t.
+    """
+    X3 = _f64(X3)
+    W = _f64(W)
+    if hasattr(Y2, "detach"):
+        Y2 = Y2.detach().cpu().numpy()
+    Y2 = np.asarray(Y2, dtype=np.int64)
+    if X3.ndim != 3 or Y2.shape != X3.shape[:2] or shift not in (0, 1):
+        raise ValueError(f"bad shapes X{X3.shape} Y{Y2.shape} or shift {shift}")
+    B, T, H = X3.shape
+    P = max(T - shift, 0)
+    X = X3[:, :P, :].reshape(B * P, H)
+    y = Y2[:, shift:shift + P].reshape(B * P)
+    loss, dX, dW, t = flce_forward_backward(X, W, y, ignore_index, softcap, reduction, return_details=True)
+    dX3 = np.zeros((B, T, H)) if dX_init is None else _f64(dX_init).copy()
+    dX3[:, :P, :] += grad_scale * dX.reshape(B, P, H)
+    dW_out = grad_scale * dW if dW_init is None else _f64(dW_init) + grad_scale * dW
+    return loss, dX3, dW_out, t["loss_rows"], t["lse"]

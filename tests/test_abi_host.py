@@ -135,3 +135,57 @@ def test_config_validation():
     assert L.flce_create(ctypes.byref(h), 0, ctypes.byref(cfg)) == -1
     cfg = flce._Config(-5, (ctypes.c_int64 * 3)(0, 0, 0))
     assert L.flce_create(ctypes.byref(h), 0, ctypes.byref(cfg)) == -1
+
+
+def _rows(B=2, T=5, shift=1, hs=(5 * 64, 64), gs=(5 * 64, 64), ls=(5, 1)):
+    return flce.Rows(B, T, shift, (ctypes.c_int64 * 2)(*hs), (ctypes.c_int64 * 2)(*gs), (ctypes.c_int64 * 2)(*ls))
+
+
+def test_rows_workspace_size():
+    H, V = 4096, 128256
+    # hidden rows already in the plain [BT][H] layout (B = 1, shift = 1): same as the plain call
+    dense = _rows(B=1, T=8193, hs=(8193 * H, H), gs=(8193 * H, H), ls=(8193, 1))
+    assert flce.workspace_size_rows(dense, H, V) == flce.workspace_size(8192, H, V)
+    # [8, 1025, H] with the shift: rows are not in the plain layout, one gathered chunk more
+    shifted = _rows(B=8, T=1025, hs=(1025 * H, H), gs=(1025 * H, H), ls=(1025, 1))
+    n, c = flce.chunk_plan(8192)
+    assert flce.workspace_size_rows(shifted, H, V) == flce.workspace_size(8192, H, V) + c * H * 2
+    # no shift, contiguous [B, T, H]: plain again
+    plain = _rows(B=8, T=1024, shift=0, hs=(1024 * H, H), gs=(1024 * H, H), ls=(1024, 1))
+    assert flce.workspace_size_rows(plain, H, V) == flce.workspace_size(8192, H, V)
+
+
+def test_rows_validation():
+    out = ctypes.c_size_t()
+    ws = lambda r, H=64: L.flce_workspace_size_rows(NULL, ctypes.byref(r), H, 10, 0, ctypes.byref(out))  # noqa: E731
+    assert ws(_rows()) == 0
+    assert L.flce_workspace_size_rows(NULL, None, 64, 10, 0, ctypes.byref(out)) == -1
+    assert ws(_rows(B=-1)) == -1
+    assert ws(_rows(shift=2)) == -1
+    assert ws(_rows(hs=(5 * 64, 60))) == -1          # rows would not be 16-byte aligned (bf16)
+    assert ws(_rows(gs=(5 * 64, -64))) == -1         # negative stride
+    assert ws(_rows(gs=(64, 64))) == -1              # grad_hidden rows overlap
+    assert ws(_rows(gs=(64, 2 * 64))) == 0           # sequence-inner layout [T][B][H] is fine
+    assert ws(_rows(hs=(0, 0))) == 0                 # hidden rows may repeat (read only)
+    assert ws(_rows(B=1 << 20, T=1 << 12, hs=(0, 64), gs=(1 << 18, 64))) == -2   # BT above 2^31 - 1
+
+
+def _fbr(h, rows, scale=1.0, flags=0, red=1, ptr=256):
+    p = ctypes.c_void_p(ptr)
+    return L.flce_forward_backward_rows(h, p, p, p, ctypes.byref(rows), 64, 10, 0, -100, 0.0, red, scale, flags,
+                                        p, p, p, p, 1 << 30, NULL)
+
+
+def test_rows_entry_points_reject_before_any_device_call():
+    fake = ctypes.c_void_p(1)
+    assert _fbr(NULL, _rows()) == -1
+    assert _fbr(fake, _rows(shift=3)) == -1
+    assert _fbr(fake, _rows(), scale=float("nan")) == -1
+    assert _fbr(fake, _rows(), scale=float("inf")) == -1
+    assert _fbr(fake, _rows(), flags=4) == -1
+    assert _fbr(fake, _rows(), red=0) == -2
+    assert _fbr(fake, _rows(), ptr=264) == -1
+    p = ctypes.c_void_p(256)
+    assert L.flce_forward_rows(fake, p, p, p, None, 64, 10, 0, -100, 0.0, 1, p, p, p, p, 1 << 30, NULL) == -1
+    assert L.flce_forward_rows(fake, p, p, p, ctypes.byref(_rows(ls=(-1, 1))), 64, 10, 0, -100, 0.0, 1,
+                               p, p, p, p, 1 << 30, NULL) == -1

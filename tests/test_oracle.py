@@ -360,3 +360,100 @@ def test_pins_catch_planted_mistakes(monkeypatch, mutation):
 
         monkeypatch.setattr(O, "_row_terms", patched)
     assert not _pins_pass()
+
+
+# ---------------------------------------------------------------- batches of sequences (label shift)
+
+def _torch_sequences(X3, W, Y2, shift, softcap, reduction, grad_scale, dX0, dW0):
+    """Independent implementation: the training-loop form, with torch float64 autograd. The logits
+    of all positions are formed, sliced to the first T-1 positions and the labels to the last T-1
+    (shift), cross_entropy is taken, and loss * grad_scale is back-propagated into grads that
+    already hold dX0 / dW0."""
+    Xt = torch.tensor(X3, dtype=torch.float64, requires_grad=True)
+    Wt = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    Xt.grad = torch.tensor(dX0, dtype=torch.float64)
+    Wt.grad = torch.tensor(dW0, dtype=torch.float64)
+    z = torch.nn.functional.linear(Xt, Wt)  # [B, T, V]
+    if softcap > 0:
+        z = softcap * torch.tanh(z / softcap)
+    yt = torch.tensor(Y2, dtype=torch.int64)
+    if shift:
+        z, yt = z[:, :-1, :], yt[:, 1:]
+    loss = torch.nn.functional.cross_entropy(z.reshape(-1, z.shape[-1]), yt.reshape(-1), ignore_index=IGN,
+                                             reduction=reduction)
+    (loss * grad_scale).backward()
+    return loss.item(), Xt.grad.numpy(), Wt.grad.numpy()
+
+
+def _seq_case(rng, B, T, H, V, ignore):
+    X3 = rng.standard_normal((B, T, H))
+    W = rng.standard_normal((V, H)) * 3.0 / math.sqrt(H)
+    Y2 = rng.integers(0, V, size=(B, T))
+    flat = Y2.reshape(-1)
+    flat[rng.permutation(B * T)[:ignore]] = IGN
+    return X3, W, flat.reshape(B, T)
+
+
+@pytest.mark.parametrize("shift", [1, 0])
+@pytest.mark.parametrize("softcap", [0.0, 3.0])
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_sequences_match_torch_training_loop(shift, softcap, reduction):
+    rng = np.random.default_rng(30)
+    X3, W, Y2 = _seq_case(rng, 3, 11, 16, 37, ignore=5)
+    dX0 = rng.standard_normal(X3.shape)
+    dW0 = rng.standard_normal(W.shape)
+    for scale, init in ((1.0, False), (0.25, True), (-2.0, True)):
+        loss, dX, dW, rows, lse = oracle.flce_sequences(X3, W, Y2, shift, IGN, softcap, reduction, scale,
+                                                        dX0 if init else None, dW0 if init else None)
+        tl, tdX, tdW = _torch_sequences(X3, W, Y2, shift, softcap, reduction, scale,
+                                        dX0 if init else np.zeros_like(X3), dW0 if init else np.zeros_like(W))
+        assert abs(loss - tl) <= 1e-12 * abs(tl)
+        assert _rel(dX, tdX) < 1e-12 and _rel(dW, tdW) < 1e-12
+        assert rows.shape == (3 * (11 - shift),) and lse.shape == rows.shape
+    # the last position of each sequence gets no gradient of its own under the shift
+    _, dX, _, _, _ = oracle.flce_sequences(X3, W, Y2, shift, IGN, softcap, reduction)
+    if shift:
+        assert np.all(dX[:, -1, :] == 0.0)
+
+
+def test_sequences_rows_are_the_shifted_pairs():
+    """Row b*(T-1)+t of the shifted form is the pair (hidden (b, t), label (b, t+1)) of the plain form."""
+    rng = np.random.default_rng(31)
+    X3, W, Y2 = _seq_case(rng, 2, 6, 8, 13, ignore=2)
+    _, _, _, rows, lse = oracle.flce_sequences(X3, W, Y2, 1, IGN, 0.0, "mean")
+    X = X3[:, :-1, :].reshape(-1, 8)
+    y = Y2[:, 1:].reshape(-1)
+    r2, l2 = oracle.flce_forward(X, W, y, IGN, 0.0, "none")
+    np.testing.assert_array_equal(rows, r2)
+    np.testing.assert_array_equal(lse, l2)
+
+
+@pytest.mark.parametrize("mutation", ["shift_backwards", "no_shift", "scale_on_loss", "init_dropped"])
+def test_sequence_pin_catches_planted_mistakes(monkeypatch, mutation):
+    """A plausible mistake in the sequence form must fail the training-loop comparison."""
+    rng = np.random.default_rng(32)
+    X3, W, Y2 = _seq_case(rng, 2, 7, 8, 11, ignore=1)
+    dX0, dW0 = rng.standard_normal(X3.shape), rng.standard_normal(W.shape)
+    real = O.flce_forward_backward
+
+    def wrong_rows(X, W_, y, *a, **k):
+        # the oracle flattens positions 0..T-2 with labels 1..T-1; re-pair them wrongly
+        y = np.asarray(y).reshape(2, 6)
+        if mutation == "shift_backwards":
+            y = np.concatenate([Y2[:, :1], Y2[:, :5]], axis=1)
+        elif mutation == "no_shift":
+            y = Y2[:, :6]
+        return real(X, W_, y.reshape(-1), *a, **k)
+
+    scale = 0.5
+    if mutation in ("shift_backwards", "no_shift"):
+        monkeypatch.setattr(O, "flce_forward_backward", wrong_rows)
+        got = O.flce_sequences(X3, W, Y2, 1, IGN, 0.0, "mean", scale, dX0, dW0)
+    elif mutation == "scale_on_loss":
+        got = list(O.flce_sequences(X3, W, Y2, 1, IGN, 0.0, "mean", 1.0, dX0, dW0))
+        got[0] *= scale
+    else:
+        got = O.flce_sequences(X3, W, Y2, 1, IGN, 0.0, "mean", scale)
+    tl, tdX, tdW = _torch_sequences(X3, W, Y2, 1, 0.0, "mean", scale, dX0, dW0)
+    ok = abs(got[0] - tl) <= 1e-12 * abs(tl) and _rel(got[1], tdX) < 1e-12 and _rel(got[2], tdW) < 1e-12
+    assert not ok
