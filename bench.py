@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--profile-only", action="store_true", help="warmup + steps, no extras (for rocprofv3)")
     ap.add_argument("--mode", choices=("fwd_bwd", "forward"), default="fwd_bwd",
                     help="fwd_bwd: the fused forward + backward (default); forward: flce_forward only")
+    ap.add_argument("--sequences", type=int, default=0,
+                    help="B > 0: lay the BT rows out as B sequences of BT/B + 1 positions, hidden [B, T+1, H], "
+                         "with the next-token label shift done by the library (the *_rows entry points)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for the FETCH_SIZE/WRITE_SIZE scale)")
     return ap.parse_args()
@@ -105,13 +108,21 @@ def main():
     torch.cuda.set_device(dev)
     w = inputs.WORKLOADS[args.workload]
     print(f"# generating {w.name}: BT={w.BT} H={w.H} V={w.V} {w.dtype}", file=sys.stderr, flush=True)
-    X, W, y = inputs.make_inputs(w, seed=0)
-    eng = flce.FLCE(dev, chunk_rows_max=args.chunk)
     BT, H, V = w.BT, w.H, w.V
+    nseq = args.sequences
+    if nseq:
+        if BT % nseq:
+            raise SystemExit("--sequences must divide BT")
+        X, W, y = inputs.make_inputs(w, seed=0, BT=BT + nseq)  # B sequences of BT/B + 1 positions
+    else:
+        X, W, y = inputs.make_inputs(w, seed=0)
+    eng = flce.FLCE(dev, chunk_rows_max=args.chunk)
     n_chunks, chunk_rows = eng.chunk_plan(BT)
 
     base_alloc = torch.cuda.memory_allocated(dev)
     Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
+    if nseq:
+        Xd, yd = Xd.reshape(nseq, BT // nseq + 1, H), yd.reshape(nseq, BT // nseq + 1)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     gh = torch.empty_like(Xd)
     gw = torch.empty((V, H), dtype=torch.float32, device=dev)
@@ -119,6 +130,8 @@ def main():
     if fwd_only:
         del gh, gw
         ws_bytes = flce.forward_workspace_size(BT, H, V, Xd.dtype, eng.handle)
+    elif nseq:
+        ws_bytes = flce.workspace_size_rows(eng._seq_rows(Xd, Wd, yd, True, gh)[0], H, V, Xd.dtype, eng.handle)
     else:
         ws_bytes = eng.workspace_size(BT, H, V, Xd.dtype)
     torch.cuda.synchronize(dev)
@@ -127,8 +140,13 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def step():
-        if fwd_only:
+        if fwd_only and nseq:
+            loss.copy_(eng.forward_seq(Xd, Wd, yd, True, -100, w.softcap, w.reduction, workspace=ws))
+        elif fwd_only:
             loss.copy_(eng.forward(Xd, Wd, yd, -100, w.softcap, w.reduction, workspace=ws))
+        elif nseq:
+            eng.forward_backward_seq(Xd, Wd, yd, True, -100, w.softcap, w.reduction, 1.0, gh, gw, loss=loss,
+                                     workspace=ws)
         else:
             eng.forward_backward(Xd, Wd, yd, -100, w.softcap, w.reduction, out=(loss, gh, gw), workspace=ws)
 
@@ -197,7 +215,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "BT": BT, "H": H, "V": V, "softcap": w.softcap,
                    "labels": w.labels, "ignore_frac": w.ignore_frac, "reduction": w.reduction,
-                   "chunk_rows": chunk_rows, "n_chunks": n_chunks, "parallelism": "single GPU"},
+                   "chunk_rows": chunk_rows, "n_chunks": n_chunks, "parallelism": "single GPU",
+                   "layout": (f"{nseq} sequences [B, T+1, H] = {list(Xd.shape)}, labels shifted by the library"
+                              if nseq else "plain [BT, H]")},
         "mfma_frac_step": round(step_flops / (ms_med * 1e-3) / PEAK_BF16, 4),
         "ms_p10_p90": [round(per[len(per) // 10], 4), round(per[(9 * len(per)) // 10], 4)],
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
