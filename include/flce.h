@@ -27,10 +27,12 @@
  *   - Pointers named "device" are HIP device pointers on the handle's device; "host" pointers are
  *     ordinary host memory. The caller owns every buffer passed in; the library never frees them.
  *   - Row-major, contiguous, densely packed: hidden and grad_hidden are [BT][H], W and grad_W are
- *     [V][H], labels is [BT]. Device pointers must be 16-byte aligned.
+ *     [V][H], labels is [BT]. Device pointers must be 16-byte aligned (labels: 8-byte). The *_rows
+ *     entry points take hidden, grad_hidden and labels as batches of sequences at given strides
+ *     (see flce_rows).
  *   - Errors are reported synchronously by the return code before anything is enqueued; the
- *     outputs are then untouched. flce_forward_backward never allocates, never synchronises and
- *     enqueues all its work on `stream`.
+ *     outputs are then untouched. The compute entry points never allocate, never synchronise and
+ *     enqueue all their work on `stream`.
  *   - A handle may be used by one stream at a time (it holds a small device status word).
  */
 #ifndef FLCE_H
