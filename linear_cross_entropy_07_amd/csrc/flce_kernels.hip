@@ -637,6 +637,7 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
   for (int j = J0; j < J0 + JG; ++j) {
     const int c = c0 + wn * WN + 32 * j + (lane & 31);
     const float ms = mx[j] == kNegInf ? 0.0f : mx[j];
+    const float msl = -ms * kLog2e;
     const u32 qrow = (u32)(((int64_t)(c - c0) * a.V_pad + wm * WM + 4 * half) * (int64_t)sizeof(S));
     float sum4[TBM];
 #pragma unroll
@@ -648,7 +649,7 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const float s = acc[i][j][4 * g + rr];
-          float e = ex2((s - ms) * kLog2e);  // exactly 1 at the segment max
+          float e = ex2(fmaf(s, kLog2e, msl));  // 2^((s - ms) log2 e); 1 (to rounding) at the max
           if constexpr (EDGE) {
             const int v = vw + 32 * i + 8 * g + 4 * half + rr;
             e = v < a.V ? e : 0.0f;
