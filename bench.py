@@ -52,14 +52,15 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str, launches_bytes_key: str = "bytes_per_launch"):
-    """HBM bytes per launch measured by rocprofv3 counters for this exact kernel source, else None."""
+def traffic_from_profiles(kernel: str, workload: str, launches_bytes_key: str = "bytes_per_launch"):
+    """HBM bytes per launch measured by rocprofv3 counters for this exact kernel source and workload,
+    else None."""
     p = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     try:
         d = json.load(open(p))
     except (OSError, ValueError):
         return None
-    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+    if d.get("kernel_source_sha256_16") != kernel_source_hash() or d.get("workload") != workload:
         return None
     return d.get(launches_bytes_key)
 
@@ -228,7 +229,7 @@ def main():
         "kernels_ms_per_launch": {k: round(v[0] / v[1], 4) for k, v in kt.items() if v[1]},
         "roofline": {"kernel": f"k_{dom}", "bound": "mfma", "achieved": round(achieved / 1e12, 2),
                      "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
-                     "traffic": traffic_from_profiles("fwd_noq" if fwd_only else dom),
+                     "traffic": traffic_from_profiles("fwd_noq" if fwd_only else dom, w.name) if not nseq else None,
                      "flops_per_launch": flops_per_launch},
     }
     if not args.no_cpu_baseline:

@@ -13,7 +13,9 @@ weight is used):
     saving softmax output";
   * llama3_8b_head / ragged: H = 4096, V = 128256 and the ragged B*T protocol from
     the benchmark comment in "Torch compiled FLCE is 2x faster than the current FLCE";
-  * gemma2_head: a softcapped Gemma2-style head (softcap mentioned in the same thread).
+  * gemma2_head: a softcapped Gemma2-style head (softcap mentioned in the same thread);
+  * llama3_8b_head_vshard8: one GPU's share of the Llama head split by vocabulary over 8 GPUs
+    (V = 128256 / 8 = 16032 rows of W), at its real shape.
 """
 from __future__ import annotations
 
@@ -45,6 +47,8 @@ WORKLOADS = {
     "llama3_8b_head": Workload("llama3_8b_head", 8192, 4096, 128256, "bf16", 0.0, 0.05, "zipf1.1", True, 0.02),
     "gemma2_head": Workload("gemma2_head", 8192, 3584, 256000, "bf16", 30.0, 0.05, "uniform", False, 0.02),
     "ragged": Workload("ragged", 0, 4096, 128256, "bf16", 0.0, 0.05, "uniform", False, 0.02),
+    "llama3_8b_head_vshard8": Workload("llama3_8b_head_vshard8", 8192, 4096, 16032, "bf16", 0.0, 0.05, "zipf1.1",
+                                       True, 0.02),
 }
 
 

@@ -79,7 +79,7 @@ def _fullsize_check(X, W, y, softcap, label):
     assert torch.isfinite(gw).all() and torch.isfinite(gh.float()).all()
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_head", "gemma2_head", "gpt2_head"])
+@pytest.mark.parametrize("name", ["llama3_8b_head", "gemma2_head", "gpt2_head", "llama3_8b_head_vshard8"])
 def test_fullsize_workload(name):
     w = inputs.WORKLOADS[name]
     X, W, y = inputs.make_inputs(w, seed=0)
