@@ -71,12 +71,22 @@ def cpu_baseline(w, X, W, y, rows: int, forward_only: bool = False):
 
     import oracle
 
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info
+                                 if i.get("user_api") == "blas"})) or blas
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:  # pragma: no cover
+        pass
     Xs, ys = X[:rows], y[:rows]
     t0 = time.perf_counter()
     if forward_only:
@@ -84,7 +94,7 @@ def cpu_baseline(w, X, W, y, rows: int, forward_only: bool = False):
     else:
         oracle.flce_forward_backward(Xs, W, ys, -100, w.softcap, w.reduction)
     dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu": cpu, "blas": blas,
             "sample": f"first {rows} of {w.BT} rows of {w.name} (full H={w.H}, V={w.V}), fp64 numpy/OpenBLAS "
                       f"{'forward' if forward_only else 'forward+backward'} incl. widening inputs to fp64; "
                       f"{dt:.2f} s"}
@@ -222,7 +232,7 @@ def main():
         "mfma_frac_step": round(step_flops / (ms_med * 1e-3) / PEAK_BF16, 4),
         "ms_p10_p90": [round(per[len(per) // 10], 4), round(per[(9 * len(per)) // 10], 4)],
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "peak_bytes": {"workspace": ws_bytes, "max_allocated_beyond_io": int(peak_extra),
+        "peak_bytes": {"workspace": ws_bytes, "handle_device_bytes": 256, "max_allocated_beyond_io": int(peak_extra),
                        "inputs_outputs": int(io_alloc - base_alloc),
                        "full_bf16_logits_not_allocated": BT * V * 2},
         "mode": args.mode,
