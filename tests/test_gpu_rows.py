@@ -1,8 +1,9 @@
 """GPU parity of the sequence entry points (flce_forward_backward_rows, flce_forward_rows) against
 the CPU float64 oracle: hidden [B,T,H] at arbitrary strides, labels [B,T] at their own strides, the
 next-token label shift done by addressing, a gradient scale, and accumulation into existing
-gradients. Shapes span several tiles and chunks with ragged tails; V = 300 takes the grad_hidden
-epilogue of whole tiles, V = 3001 the split-K reduction."""
+gradients. Shapes span several tiles and chunks with ragged tails; V = 300 (bf16) and V = 250 (fp32)
+take the grad_hidden epilogue of whole tiles, V = 3001 (bf16) and V = 1000 (fp32) the split-K
+reduction."""
 import numpy as np
 import pytest
 import torch
@@ -138,11 +139,13 @@ def test_accumulate_and_grad_scale_bf16(acc, V):
     _check(eng(256), X3, W, Y2, "bf16", grad_scale=0.25, layout="padded", acc_gh=acc[0], acc_gw=acc[1], seed=1)
 
 
+@pytest.mark.parametrize("V", [1000, 250])
 @pytest.mark.parametrize("layout", ["contiguous", "seq_major"])
 @pytest.mark.parametrize("reduction", ["mean", "sum"])
-def test_fp32_shifted(layout, reduction):
-    X3, W, Y2 = _seq_inputs(4, 100, 96, 1000, "fp32", seed=43)
-    announce("rows: fp32", layout, reduction, "chunk 256")
+def test_fp32_shifted(layout, reduction, V):
+    """V = 250 keeps K = V too short to split: the fp32 grad_hidden tile epilogue; V = 1000 splits K."""
+    X3, W, Y2 = _seq_inputs(4, 100, 96, V, "fp32", seed=43)
+    announce("rows: fp32", layout, reduction, V, "chunk 256")
     _check(eng(256), X3, W, Y2, "fp32", softcap=3.0, reduction=reduction, grad_scale=-1.5, layout=layout,
            labels_layout="strided", acc_gh=True, acc_gw=True, seed=2)
 
