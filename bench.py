@@ -181,6 +181,9 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # per-kernel durations: the library brackets each of its launches with a HIP event pair on the
+    # launch stream (events created here, before the timed region)
+    eng.profile_begin(max_launches=64 * args.steps)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -189,16 +192,10 @@ def main():
         ev[i][1].record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
+    kt = eng.profile_end(stream)
     per = sorted(a.elapsed_time(b) for a, b in ev)
     ms_med = statistics.median(per)
     peak_extra = torch.cuda.max_memory_allocated(dev) - io_alloc
-
-    # per-kernel durations: HIP events bracketing each launch on the launch stream, over a second
-    # timed pass of the same steps
-    eng.profile_begin(max_launches=64 * args.steps)
-    for _ in range(args.steps):
-        step()
-    kt = eng.profile_end(stream)
     print(f"# kernel ms/launch: " + ", ".join(f"{k} {v[0] / max(v[1], 1):.3f}x{v[1] // args.steps}"
                                             for k, v in kt.items() if v[1]), file=sys.stderr, flush=True)
     gemm = {k: kt[k] for k in (("fwd",) if fwd_only else ("fwd", "dx", "dw"))}
