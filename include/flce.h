@@ -58,7 +58,7 @@ typedef enum { FLCE_NONE = 0, FLCE_MEAN = 1, FLCE_SUM = 2 } flce_reduction;
 enum {
   FLCE_OK = 0,
   FLCE_ERR_INVALID_ARG = -1,        /* null pointer, bad size, bad enum, misaligned pointer, bad softcap */
-  FLCE_ERR_UNSUPPORTED = -2,        /* a valid request this build does not implement (e.g. H % 8 != 0) */
+  FLCE_ERR_UNSUPPORTED = -2,        /* a valid request this library does not implement (e.g. H % 8 != 0) */
   FLCE_ERR_WORKSPACE_TOO_SMALL = -3,/* workspace_bytes < flce_workspace_size(...) */
   FLCE_ERR_HIP = -4,                /* a HIP runtime call or kernel launch failed */
   FLCE_ERR_LABEL_RANGE = -5         /* (flce_status) a label outside [0, V) that is not ignore_index */
