@@ -100,6 +100,68 @@ def cpu_baseline(w, X, W, y, rows: int, forward_only: bool = False):
                       f"{dt:.2f} s"}
 
 
+def ragged_sweep(args, dev):
+    """The ragged B*T protocol: one handle, one code object, calls whose B*T changes every time.
+    Hidden rows and labels of every call are the first B*T rows of one draw of the largest call."""
+    import torch
+
+    from linear_cross_entropy_07_amd import flce, inputs
+
+    w = inputs.WORKLOADS["ragged"]
+    bts = inputs.ragged_bt_list(0, 20)
+    print(f"# generating the ragged sweep: {len(bts)} calls, B*T {min(bts)}..{max(bts)}", file=sys.stderr,
+          flush=True)
+    X, W, y = inputs.make_ragged_call(max(bts), seed=100)
+    eng = flce.FLCE(dev, chunk_rows_max=args.chunk)
+    H, V = w.H, w.V
+    Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    gh = torch.empty_like(Xd)
+    gw = torch.empty((V, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(eng.workspace_size(bt, H, V) for bt in bts), dtype=torch.uint8, device=dev)
+    reps = max(1, args.steps // 10)
+
+    def call(bt):
+        eng.forward_backward(Xd[:bt], Wd, yd[:bt], -100, 0.0, "mean", out=(loss, gh[:bt], gw), workspace=ws)
+
+    for bt in bts[: args.warmup]:
+        call(bt)
+    stream = torch.cuda.current_stream(dev)
+    per_call = []
+    eng.profile_begin(max_launches=64 * reps * len(bts))
+    for bt in bts:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            call(bt)
+            b.record(stream)
+        torch.cuda.synchronize(dev)
+        per_call.append((bt, statistics.median(a.elapsed_time(b) for a, b in ev)))
+    kt = eng.profile_end(stream)
+    tot_bt = sum(bt for bt, _ in per_call)
+    tot_ms = sum(ms for _, ms in per_call)
+    flops = sum(6.0 * bt * H * V for bt, _ in per_call)
+    # roofline of the slowest GEMM kernel over the sweep: its flops (2*BT*H*V per call) / its time
+    gemm = {k: kt[k][0] / reps for k in ("fwd", "dx", "dw")}
+    dom = max(gemm, key=gemm.get)
+    achieved = (flops / 3.0) / (gemm[dom] * 1e-3)
+    out = {
+        "metric": "FLCE fwd+bwd tokens/sec over the ragged B*T sweep (sum of B*T / sum of call times)",
+        "value": round(tot_bt / (tot_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": reps,
+        "warmup": args.warmup, "ms_per_step": round(tot_ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "ragged", "H": H, "V": V, "calls": len(bts), "BT": [bt for bt, _ in per_call],
+                   "parallelism": "single GPU", "layout": "plain [BT, H]"},
+        "mfma_frac_sweep": round(flops / (tot_ms * 1e-3) / PEAK_BF16, 4),
+        "ms_per_call": [round(ms, 3) for _, ms in per_call],
+        "kernels_ms_per_sweep": {k: round(v[0] / reps, 3) for k, v in kt.items() if v[1]},
+        "roofline": {"kernel": f"k_{dom}", "bound": "mfma", "achieved": round(achieved / 1e12, 2),
+                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -118,6 +180,8 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     w = inputs.WORKLOADS[args.workload]
+    if w.name == "ragged":
+        return ragged_sweep(args, dev)
     print(f"# generating {w.name}: BT={w.BT} H={w.H} V={w.V} {w.dtype}", file=sys.stderr, flush=True)
     BT, H, V = w.BT, w.H, w.V
     nseq = args.sequences
