@@ -158,7 +158,8 @@ typedef struct {
   int64_t shift;                 /* 0 or 1 */
   int64_t hidden_stride[2];      /* elements from (b, t) to (b+1, t) and to (b, t+1); multiples of
                                     8 (FLCE_BF16) or 4 (FLCE_FP32) elements, so rows stay 16-byte aligned */
-  int64_t grad_hidden_stride[2]; /* the same for grad_hidden; its B x T rows must not overlap */
+  int64_t grad_hidden_stride[2]; /* the same for grad_hidden; its B x T rows must be disjoint, with
+                                    the larger stride stepping past the whole span of the smaller */
   int64_t label_stride[2];       /* elements from (b, t) to (b+1, t) and to (b, t+1) of labels */
 } flce_rows;
 

@@ -148,7 +148,9 @@ Rows plain_rows(int64_t BT, int64_t H) {
 }
 
 // True if rows (b, t) of extents (n0, n1) with element strides (s0, s1) and `width` elements each
-// never share an element (the two strides, ordered, must each step past everything inside).
+// never share an element: with the strides ordered (s0 <= s1), the inner stride steps past a row
+// and the outer stride steps past the whole inner span, s1 >= (n0 - 1) * s0 + width (checked
+// without overflow).
 bool no_overlap(int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_t width) {
   if (n0 <= 1) s0 = 0, n0 = 1;
   if (n1 <= 1) s1 = 0, n1 = 1;
@@ -159,7 +161,7 @@ bool no_overlap(int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_t width) {
     std::swap(s0, s1);
     std::swap(n0, n1);
   }
-  return s0 >= width && s1 >= n0 * s0;
+  return s0 >= width && s1 >= width && (s1 - width) / s0 >= n0 - 1;
 }
 
 // Validates a flce_rows description (see include/flce.h) and derives the row maps.

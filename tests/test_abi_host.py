@@ -189,3 +189,24 @@ def test_rows_entry_points_reject_before_any_device_call():
     assert L.flce_forward_rows(fake, p, p, p, None, 64, 10, 0, -100, 0.0, 1, p, p, p, p, 1 << 30, NULL) == -1
     assert L.flce_forward_rows(fake, p, p, p, ctypes.byref(_rows(ls=(-1, 1))), 64, 10, 0, -100, 0.0, 1,
                                p, p, p, p, 1 << 30, NULL) == -1
+
+
+def test_rows_overlap_rule_never_accepts_overlapping_grad_rows():
+    """flce_workspace_size_rows accepts a grad_hidden layout only if its B x T rows are disjoint
+    (checked by enumerating the elements of small layouts)."""
+    import itertools
+
+    H = 8
+    out = ctypes.c_size_t()
+    accepted = 0
+    for B, T in itertools.product(range(1, 4), repeat=2):
+        for k0, k1 in itertools.product(range(0, 10), repeat=2):
+            s0, s1 = 8 * k0, 8 * k1
+            r = _rows(B=B, T=T, shift=0, hs=(s0, s1), gs=(s0, s1), ls=(T, 1))
+            rc = L.flce_workspace_size_rows(NULL, ctypes.byref(r), H, 10, 0, ctypes.byref(out))
+            assert rc in (0, -1)
+            if rc == 0:
+                accepted += 1
+                cells = [b * s0 + t * s1 + e for b in range(B) for t in range(T) for e in range(H)]
+                assert len(cells) == len(set(cells)), (B, T, s0, s1)
+    assert accepted > 100
