@@ -41,6 +41,26 @@ def build(verbose: bool = False) -> str:
     return DEFAULT_LIB
 
 
+EXAMPLE_SRC = os.path.join(PKG, "examples", "flce_from_c.c")
+EXAMPLE_BIN = os.path.join(PKG, "examples", "flce_from_c")
+
+
+def build_c_example(verbose: bool = False) -> str:
+    """Compile the plain C99 caller of the library (gcc; HIP runtime C API for device memory)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-O2", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", INCLUDE, EXAMPLE_SRC,
+           "-L", PKG, "-lflce", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/..", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", EXAMPLE_BIN + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{res.stderr[-8000:]}")
+    os.replace(EXAMPLE_BIN + ".tmp", EXAMPLE_BIN)
+    return EXAMPLE_BIN
+
+
 def ensure_built() -> str:
     """Return the library path, building it only if no library exists yet."""
     if not os.path.exists(LIB):

@@ -210,3 +210,18 @@ def test_rows_overlap_rule_never_accepts_overlapping_grad_rows():
                 cells = [b * s0 + t * s1 + e for b in range(B) for t in range(T) for e in range(H)]
                 assert len(cells) == len(set(cells)), (B, T, s0, s1)
     assert accepted > 100
+
+
+@pytest.mark.parametrize("compiler,std", [("gcc", "-std=c99"), ("g++", "-std=c++17")])
+def test_header_compiles_as_c_and_cpp(tmp_path, compiler, std):
+    """include/flce.h is a C header: it compiles on its own as C99 and as C++ (no HIP or torch types)."""
+    import shutil
+    import subprocess
+
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not found")
+    src = tmp_path / ("t.c" if compiler == "gcc" else "t.cpp")
+    src.write_text('#include "flce.h"\nint main(void) { flce_handle h = 0; return flce_destroy(h); }\n')
+    res = subprocess.run([compiler, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I",
+                          build_lib.INCLUDE, str(src)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
