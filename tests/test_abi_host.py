@@ -225,3 +225,16 @@ def test_header_compiles_as_c_and_cpp(tmp_path, compiler, std):
     res = subprocess.run([compiler, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I",
                           build_lib.INCLUDE, str(src)], capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
+
+
+def test_chunk_plan_invariants_random_bt():
+    """For any B*T up to 2^31 - 1: n chunks of C rows cover it with a non-empty last chunk, C is a
+    multiple of 256 and at most the 4096-row default, and n is the fewest chunks of that size."""
+    import numpy as np
+
+    rng = np.random.default_rng(5)
+    for bt in [1, 255, 256, 257, 4095, 4096, 4097, 2**31 - 1] + rng.integers(1, 2**31 - 1, size=200).tolist():
+        n, c = flce.chunk_plan(int(bt))
+        assert c % 256 == 0 and 0 < c <= 4096
+        assert (n - 1) * c < bt <= n * c
+        assert n == -(-bt // 4096)
