@@ -55,7 +55,7 @@ def kernel_source_hash() -> str:
 def traffic_from_profiles(kernel: str, workload: str, launches_bytes_key: str = "bytes_per_launch"):
     """HBM bytes per launch measured by rocprofv3 counters for this exact kernel source and workload,
     else None."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}_{kernel}.json")
     try:
         d = json.load(open(p))
     except (OSError, ValueError):
