@@ -23,6 +23,8 @@ if ROOT not in sys.path:
 
 METRIC = "FLCE fwd+bwd tokens/sec at H=4096,V=128256 bf16; % bf16 MFMA peak; peak bytes"
 METRIC_FWD = "FLCE forward-only tokens/sec (flce_forward, no gradients); % bf16 MFMA peak; peak bytes"
+METRIC_RECOMPUTE = ("FLCE fwd+bwd tokens/sec, recompute mode (flce_forward_backward_recompute); "
+                    "% bf16 MFMA peak of the 6*BT*H*V algorithmic flops; peak bytes")
 PEAK_BF16 = 2.5e15          # dense bf16 MFMA, MI355X published
 PEAK_HBM = 8.0e12
 
@@ -37,8 +39,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4608, help="rows of the oracle's bounded sample")
     ap.add_argument("--profile-only", action="store_true", help="warmup + steps, no extras (for rocprofv3)")
-    ap.add_argument("--mode", choices=("fwd_bwd", "forward"), default="fwd_bwd",
-                    help="fwd_bwd: the fused forward + backward (default); forward: flce_forward only")
+    ap.add_argument("--mode", choices=("fwd_bwd", "forward", "recompute"), default="fwd_bwd",
+                    help="fwd_bwd: the fused forward + backward (default); forward: flce_forward only; "
+                         "recompute: flce_forward_backward_recompute (logits formed twice, one vocabulary "
+                         "slice kept)")
+    ap.add_argument("--vslice", type=int, default=0, help="vocabulary slice of the recompute mode (0 = 8192)")
     ap.add_argument("--sequences", type=int, default=0,
                     help="B > 0: lay the BT rows out as B sequences of BT/B + 1 positions, hidden [B, T+1, H], "
                          "with the next-token label shift done by the library (the *_rows entry points)")
@@ -202,7 +207,12 @@ def main():
     gh = torch.empty_like(Xd)
     gw = torch.empty((V, H), dtype=torch.float32, device=dev)
     fwd_only = args.mode == "forward"
-    if fwd_only:
+    recompute = args.mode == "recompute"
+    if recompute and nseq:
+        raise SystemExit("--mode recompute takes the plain [BT, H] layout")
+    if recompute:
+        ws_bytes = flce.recompute_workspace_size(BT, H, V, Xd.dtype, args.vslice, eng.handle)
+    elif fwd_only:
         del gh, gw
         ws_bytes = flce.forward_workspace_size(BT, H, V, Xd.dtype, eng.handle)
     elif nseq:
@@ -219,6 +229,9 @@ def main():
             loss.copy_(eng.forward_seq(Xd, Wd, yd, True, -100, w.softcap, w.reduction, workspace=ws))
         elif fwd_only:
             loss.copy_(eng.forward(Xd, Wd, yd, -100, w.softcap, w.reduction, workspace=ws))
+        elif recompute:
+            eng.forward_backward_recompute(Xd, Wd, yd, -100, w.softcap, w.reduction, args.vslice,
+                                           out=(loss, gh, gw), workspace=ws)
         elif nseq:
             eng.forward_backward_seq(Xd, Wd, yd, True, -100, w.softcap, w.reduction, 1.0, gh, gw, loss=loss,
                                      workspace=ws)
@@ -247,7 +260,9 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     # per-kernel durations: the library brackets each of its launches with a HIP event pair on the
     # launch stream (events created here, before the timed region)
-    eng.profile_begin(max_launches=64 * args.steps)
+    vs_eff = min(-(-(args.vslice or 8192) // 256) * 256, -(-V // 256) * 256)
+    launches_per_step = 8 + n_chunks * (8 + (4 * -(-V // vs_eff) if recompute else 8))
+    eng.profile_begin(max_launches=launches_per_step * args.steps)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -257,6 +272,8 @@ def main():
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     kt = eng.profile_end(stream)
+    if kt["finalize"][1] != args.steps:  # the last launch of every step was recorded
+        raise SystemExit("kernel profile incomplete: more launches per step than events")
     per = sorted(a.elapsed_time(b) for a, b in ev)
     ms_med = statistics.median(per)
     peak_extra = torch.cuda.max_memory_allocated(dev) - io_alloc
@@ -265,15 +282,18 @@ def main():
     gemm = {k: kt[k] for k in (("fwd",) if fwd_only else ("fwd", "dx", "dw"))}
     dom = max(gemm, key=lambda k: gemm[k][0])
     dom_ms = gemm[dom][0] / gemm[dom][1]
-    # one GEMM launch per chunk; the last chunk may be shorter, so average the algorithmic flops
-    # 2*C*H*V over the launches actually made
-    flops_per_launch = 2.0 * BT * H * V / n_chunks
+    # each product does 2*BT*H*V flop per step (the logits product twice in the recompute mode),
+    # over one launch per chunk (per chunk and vocabulary slice in the recompute mode); the last
+    # chunk may be shorter, so the flops are averaged over the launches actually made
+    step_gemm_flops = {"fwd": 2.0 * BT * H * V * (2 if recompute else 1), "dx": 2.0 * BT * H * V,
+                       "dw": 2.0 * BT * H * V}
+    flops_per_launch = step_gemm_flops[dom] * args.steps / gemm[dom][1]
     achieved = flops_per_launch / (dom_ms * 1e-3)
 
     tokens_per_s = BT / (ms_med * 1e-3)
     step_flops = (2.0 if fwd_only else 6.0) * BT * H * V
     out = {
-        "metric": METRIC_FWD if fwd_only else METRIC,
+        "metric": METRIC_FWD if fwd_only else (METRIC_RECOMPUTE if recompute else METRIC),
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -300,7 +320,8 @@ def main():
         "kernels_ms_per_launch": {k: round(v[0] / v[1], 4) for k, v in kt.items() if v[1]},
         "roofline": {"kernel": f"k_{dom}", "bound": "mfma", "achieved": round(achieved / 1e12, 2),
                      "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
-                     "traffic": traffic_from_profiles("fwd_noq" if fwd_only else dom, w.name) if not nseq else None,
+                     "traffic": (traffic_from_profiles("fwd_noq" if fwd_only else dom, w.name)
+                                 if not (nseq or recompute) else None),
                      "flops_per_launch": flops_per_launch},
     }
     if not args.no_cpu_baseline:

@@ -117,6 +117,29 @@ int flce_forward_backward(flce_handle h,
                           float* loss, void* grad_hidden, float* grad_W,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* The recompute mode: the result of flce_forward_backward with less workspace and more work. The
+ * PR #126348 description rebuilds the softmax in the backward pass from the softmax input and the
+ * per-row max/sum; here the softmax input itself is rebuilt too. Per chunk of rows, a forward pass
+ * over the whole vocabulary gives each row's log-sum-exp. Then, per vocabulary slice of v_slice
+ * columns, the logits are computed again and turned into dZ against that lse. That dZ is used at
+ * once for the slice's rows of grad_W and for an fp32 running sum of grad_hidden. The logits GEMM runs
+ * twice: 8 * BT * H * V flop instead of 6. The workspace holds one [chunk_rows][v_slice] 16-bit slice
+ * instead of a [chunk_rows][V] one.
+ *   v_slice      vocabulary columns per slice: 0 = 8192; rounded up to a multiple of 256; at most V
+ *                rounded up; negative is FLCE_ERR_INVALID_ARG
+ * Everything else as for flce_forward_backward. The loss and grad_W are bitwise those of
+ * flce_forward_backward on the same inputs and handle; grad_hidden differs only by the order of its
+ * fp32 sums (one per slice, added in slice order). */
+int flce_recompute_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype,
+                                  int64_t v_slice, size_t* bytes);
+int flce_forward_backward_recompute(flce_handle h,
+                                    const void* hidden, const void* W, const int64_t* labels,
+                                    int64_t BT, int64_t H, int64_t V, int dtype,
+                                    int64_t ignore_index, float softcap, int reduction,
+                                    int64_t v_slice,
+                                    float* loss, void* grad_hidden, float* grad_W,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace flce_forward needs (host-only arithmetic; h may be NULL). The forward
  * path keeps no logits: the workspace holds the per-(row, 128-wide V segment) statistics of one
  * chunk, per-row label data and one chunk of hidden transposed. Returns FLCE_OK or

@@ -80,7 +80,7 @@ int dx_splits(int64_t rows, int64_t H, int64_t V_pad, int dtype, int ncu) {
 }
 
 struct Layout {
-  size_t off_e, off_m, off_s, off_y, off_sl, off_og, off_loss, off_part, off_xt, off_xs, off_params, total;
+  size_t off_e, off_m, off_s, off_y, off_sl, off_og, off_loss, off_part, off_xt, off_xs, off_lse, off_params, total;
   int splits;
   int64_t chunk_rows;
 };
@@ -115,6 +115,53 @@ Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu
   L.off_part = take(L.splits > 1 ? (size_t)L.splits * rows * H * 4 : 0);
   L.off_xt = take((size_t)rows * H * esz);
   L.off_xs = take(backward && xstage ? (size_t)rows * H * esz : 0);
+  L.off_lse = take(0);
+  L.total = off;
+  return L;
+}
+
+constexpr int64_t kDefaultVSlice = 8192;
+
+// Width of the vocabulary slices of the recompute mode: a multiple of the tile width, at most V
+// rounded up (0 selects the default).
+int64_t vslice_of(int64_t vs, int64_t V) {
+  if (vs <= 0) vs = kDefaultVSlice;
+  vs = round_up(vs, flce::kTile);
+  const int64_t vmax = round_up(V, flce::kTile);
+  return vs < vmax ? vs : vmax;
+}
+
+// Workspace of the recompute mode. Per chunk of C rows: q/dZ of one vocabulary slice
+// [C][slice], the statistics of the whole vocabulary [C][V_pad/128] (pass 1), the fp32 grad_hidden
+// accumulator [C][H] and hidden^T [H][C]; per row: labels, label logit, one-hot coefficient, loss
+// term and lse. No buffer spans the whole vocabulary for more than its 128-wide segment statistics.
+Layout layout_recompute(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int64_t vs) {
+  Layout L{};
+  int64_t n, rows;
+  plan(BT, cmax, &n, &rows);
+  const int64_t V_pad = round_up(V, flce::kTile);
+  const int64_t nseg = V_pad / flce::kSeg;
+  const size_t esz = dtype == 0 ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  L.chunk_rows = rows;
+  L.splits = 1;
+  L.off_params = take(sizeof(flce::DevParams));
+  L.off_e = take((size_t)rows * vslice_of(vs, V) * esz);
+  L.off_m = take((size_t)rows * nseg * 4);
+  L.off_s = take((size_t)rows * nseg * 4);
+  L.off_y = take((size_t)BT * 4);
+  L.off_sl = take((size_t)BT * 4);
+  L.off_og = take((size_t)BT * 4);
+  L.off_loss = take((size_t)BT * 4);
+  L.off_lse = take((size_t)BT * 4);
+  L.off_part = take((size_t)rows * H * 4);
+  L.off_xt = take((size_t)rows * H * esz);
+  L.off_xs = take(0);
   L.total = off;
   return L;
 }
@@ -336,6 +383,68 @@ int run_fused(flce_ctx* h, const void* hidden, const void* W, const int64_t* lab
   return FLCE_OK;
 }
 
+// The recompute mode over the rows R (plain layout; sizes already checked). Per chunk: the forward
+// pass over the whole vocabulary gives each row's lse; then per vocabulary slice the logits are
+// formed again, turned into dZ against that lse, and used at once for the slice's grad_W rows and
+// the chunk's fp32 grad_hidden sum.
+int run_recompute(flce_ctx* h, const void* hidden, const void* W, const int64_t* labels, const Rows& R, int64_t H,
+                  int64_t V, int dtype, int64_t ignore_index, float softcap, int reduction, int64_t v_slice,
+                  float* loss, void* grad_hidden, float* grad_W, void* workspace, size_t workspace_bytes,
+                  void* stream_ptr) {
+  const int64_t BT = R.BT;
+  if (reduction == FLCE_NONE) return FLCE_ERR_UNSUPPORTED;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
+  if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_INVALID_ARG;
+  if (v_slice < 0) return FLCE_ERR_INVALID_ARG;
+  if (!W || !loss || !grad_W || !workspace) return FLCE_ERR_INVALID_ARG;
+  if (BT > 0 && (!hidden || !labels || !grad_hidden)) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || !aligned(loss, 4) || !aligned(grad_W, 16) || !aligned(workspace, 256))
+    return FLCE_ERR_INVALID_ARG;
+  if (BT > 0 && (!aligned(hidden, 16) || !aligned(labels, 8) || !aligned(grad_hidden, 16)))
+    return FLCE_ERR_INVALID_ARG;
+  const int64_t vs = vslice_of(v_slice, V);
+  const Layout L = layout_recompute(BT, H, V, dtype, h->chunk_rows_max, vs);
+  if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+
+  DeviceGuard g(h->device);
+  if (!g.ok) return FLCE_ERR_HIP;
+  Call call = make_call(h, L, R, H, V, dtype, ignore_index, softcap, reduction, 1.0f, 0, workspace, stream_ptr);
+  const hipStream_t stream = call.stream;
+  const flce::Problem& p = call.p;
+  flce::Work& w = call.w;
+  char* base = (char*)workspace;
+  w.dx_part = (float*)(base + L.off_part);
+  float* lse = (float*)(base + L.off_lse);
+
+  FLCE_LAUNCH(FLCE_K_PREPASS, flce::launch_prepass(p, labels, w, h->d_status, stream));
+  if (BT == 0) {
+    FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_zero_f32(grad_W, V * H, stream));
+    FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
+    return FLCE_OK;
+  }
+  int64_t n_chunks, crows;
+  plan(BT, h->chunk_rows_max, &n_chunks, &crows);
+  for (int64_t ci = 0; ci < n_chunks; ++ci) {
+    const int64_t row0 = ci * crows;
+    const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
+    FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
+    // pass 1: row statistics over the whole vocabulary -> lse and the loss terms
+    FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, false, stream));
+    FLCE_LAUNCH(FLCE_K_ROWS, flce::launch_rows(p, w, row0, rows, nullptr, lse, stream));
+    // pass 2: per vocabulary slice
+    for (int64_t v0 = 0, si = 0; v0 < V; v0 += vs, ++si) {
+      const flce::VSlice sl{v0, (V - v0) < vs ? (V - v0) : vs};
+      FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, true, stream, sl));
+      FLCE_LAUNCH(FLCE_K_MERGE, flce::launch_merge(p, w, row0, rows, stream, sl, lse));
+      FLCE_LAUNCH(FLCE_K_DX, flce::launch_dx(p, W, w, grad_hidden, row0, rows, 1, stream, sl, si == 0 ? 1 : 2));
+      FLCE_LAUNCH(FLCE_K_DW, flce::launch_dw(p, hidden, w, grad_W, row0, rows, ci > 0, stream, sl));
+    }
+    FLCE_LAUNCH(FLCE_K_DX_REDUCE, flce::launch_dx_reduce(p, w, grad_hidden, row0, rows, 1, stream));
+  }
+  FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
+  return FLCE_OK;
+}
+
 // The forward alone over the rows R (sizes already checked).
 int run_forward(flce_ctx* h, const void* hidden, const void* W, const int64_t* labels, const Rows& R, int64_t H,
                 int64_t V, int dtype, int64_t ignore_index, float softcap, int reduction, float* loss,
@@ -476,6 +585,26 @@ int flce_forward_backward_rows(flce_handle h, const void* hidden, const void* W,
   if (flags & ~(FLCE_ACCUMULATE_GRAD_HIDDEN | FLCE_ACCUMULATE_GRAD_W)) return FLCE_ERR_INVALID_ARG;
   return run_fused(h, hidden, W, labels, R, H, V, dtype, ignore_index, softcap, reduction, grad_scale, flags, loss,
                    grad_hidden, grad_W, workspace, workspace_bytes, stream_ptr);
+}
+
+int flce_recompute_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, int64_t v_slice,
+                                  size_t* bytes) {
+  if (!bytes || v_slice < 0) return FLCE_ERR_INVALID_ARG;
+  const int rc = check_sizes(BT, H, V, dtype);
+  if (rc != FLCE_OK) return rc;
+  *bytes = layout_recompute(BT, H, V, dtype, chunk_max_of(h), vslice_of(v_slice, V)).total;
+  return FLCE_OK;
+}
+
+int flce_forward_backward_recompute(flce_handle h, const void* hidden, const void* W, const int64_t* labels,
+                                    int64_t BT, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                                    float softcap, int reduction, int64_t v_slice, float* loss, void* grad_hidden,
+                                    float* grad_W, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  if (!h) return FLCE_ERR_INVALID_ARG;
+  const int rc = check_sizes(BT, H, V, dtype);
+  if (rc != FLCE_OK) return rc;
+  return run_recompute(h, hidden, W, labels, plain_rows(BT, H), H, V, dtype, ignore_index, softcap, reduction,
+                       v_slice, loss, grad_hidden, grad_W, workspace, workspace_bytes, stream_ptr);
 }
 
 int flce_forward_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, size_t* bytes) {

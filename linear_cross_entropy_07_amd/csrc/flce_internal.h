@@ -71,25 +71,35 @@ struct Problem {
   bool acc_gh, acc_gw; // add into grad_hidden / grad_W instead of overwriting
 };
 
+// A slice of the vocabulary: W rows v0 .. v0 + vn - 1 (vn < 0: the whole vocabulary). Slices other
+// than the last are multiples of the tile width, so tiles and 128-wide segments line up with those
+// of the whole vocabulary.
+struct VSlice {
+  int64_t v0 = 0, vn = -1;
+};
+
 // Launchers (all enqueue on `stream`, return hipError_t of the launch).
 hipError_t launch_prepass(const Problem& p, const int64_t* labels, const Work& w, int* status_out,
                           hipStream_t stream);
 hipError_t launch_transpose(const Problem& p, const void* hidden, const Work& w, int64_t row0, int64_t rows,
                             hipStream_t stream);
 hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t row0, int64_t rows,
-                      bool store_q, hipStream_t stream);
+                      bool store_q, hipStream_t stream, VSlice vs = VSlice{});
 hipError_t launch_rows(const Problem& p, const Work& w, int64_t row0, int64_t rows, float* loss_rows,
                        float* lse_rows, hipStream_t stream);
-hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream);
+// lse_in: per-row lse of the whole vocabulary (the recompute mode); null: from the chunk's statistics.
+hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream,
+                        VSlice vs = VSlice{}, const float* lse_in = nullptr);
+// part_mode: 0 the normal output, 1 write the fp32 [rows][H] partials (one split), 2 add to them.
 hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_hidden, int64_t row0,
-                     int64_t rows, int splits, hipStream_t stream);
+                     int64_t rows, int splits, hipStream_t stream, VSlice vs = VSlice{}, int part_mode = 0);
 // grad_hidden rows that are no rows of the call (the last position of each sequence when labels are
 // shifted): zero-filled. B sequences, element offset `off` of the row in sequence 0.
 hipError_t launch_zero_rows(const Problem& p, void* grad_hidden, int64_t B, int64_t off, hipStream_t stream);
 hipError_t launch_dx_reduce(const Problem& p, const Work& w, void* grad_hidden, int64_t row0, int64_t rows,
                             int splits, hipStream_t stream);
 hipError_t launch_dw(const Problem& p, const void* hidden, const Work& w, float* grad_W, int64_t row0,
-                     int64_t rows, bool accumulate, hipStream_t stream);
+                     int64_t rows, bool accumulate, hipStream_t stream, VSlice vs = VSlice{});
 hipError_t launch_finalize(const Problem& p, const Work& w, float* loss, hipStream_t stream);
 hipError_t launch_zero_f32(float* ptr, int64_t n, hipStream_t stream);
 

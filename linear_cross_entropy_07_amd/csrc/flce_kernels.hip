@@ -505,8 +505,9 @@ struct FwdArgs {
   float* s_label;     // chunk row 0
   float* og;          // chunk row 0
   const DevParams* prm;
-  int64_t H, V, V_pad;
+  int64_t H, V, V_pad;  // V columns of W starting at W's row 0 (a slice of the vocabulary: V = slice width)
   int nseg, rows;
+  int yoff;           // vocabulary index of W's row 0: labels are taken relative to it
   float softcap;
 };
 
@@ -516,9 +517,11 @@ struct DxArgs {
   void* out;          // grad_hidden (splits == 1): row r of the call starts at element gmap(r)
   RowMap gmap;
   int64_t row0;       // call row of chunk row 0
-  float* part;        // [splits][rows][H] (splits > 1)
+  float* part;        // [splits][rows][H] fp32 partials (splits > 1, or part_out)
   int64_t H, V, V_pad;
   int rows, splits, ksteps_per_split, accumulate;
+  int part_out;       // 1: write the fp32 [rows][H] partials even with one split
+  int part_acc;       // 1: add to the fp32 partials instead of writing them (one split)
 };
 
 struct DwArgs {
@@ -575,7 +578,7 @@ __device__ __forceinline__ void fwd_labels(const FwdArgs& a, int c0, int (&ylab)
   for (int j = 0; j < TBN; ++j) {
     const int c = c0 + wn * WN + 32 * j + (lane & 31);
     const int yv = __builtin_amdgcn_raw_buffer_load_b32(ry, c * 4, 0, 0);
-    ylab[j] = c < a.rows ? yv : -1;
+    ylab[j] = c < a.rows && yv >= 0 ? yv - a.yoff : -1;
   }
 }
 
@@ -868,18 +871,35 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
 
   // output tile (c0, h0); rows past the chunk and columns past H are dropped
   const int vrows = min(TILE, a.rows - c0), ncols = (int)min<int64_t>(TILE, a.H - h0);
-  if (a.splits == 1) {
+  if (a.splits == 1 && !a.part_out) {
     dx_store_tile<T>(a, acc, c0, h0, vrows, smem);
   } else {
     const rsrc_t ro = make_rsrc(a.part + ((int64_t)split * a.rows + c0) * a.H + h0, ((int64_t)vrows * a.H - h0) * 4);
     const AccAddr<4> ad((int)a.H, ncols);
+    if (a.part_acc) {
+      // running fp32 sum over the vocabulary slices of the recompute mode (one split)
 #pragma unroll
-    for (int i = 0; i < TBM; ++i) {
+      for (int i = 0; i < TBM; ++i) {
+        float old[TBN][16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+        for (int j = 0; j < TBN; ++j)
 #pragma unroll
-        for (int j = 0; j < TBN; ++j) bstore_f32(ro, ad.col[j], ad.row(i, r), acc[i][j][r]);
-      __builtin_amdgcn_sched_barrier(0);
+          for (int r = 0; r < 16; ++r) old[j][r] = bload_f32(ro, ad.col[j], ad.row(i, r));
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+          for (int j = 0; j < TBN; ++j) bstore_f32(ro, ad.col[j], ad.row(i, r), acc[i][j][r] + old[j][r]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TBM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+          for (int j = 0; j < TBN; ++j) bstore_f32(ro, ad.col[j], ad.row(i, r), acc[i][j][r]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 }
@@ -1069,19 +1089,24 @@ __device__ __forceinline__ float row_lse(const float* m, const float* sp, int ns
   return s_lse;
 }
 
+// With lse_in (the recompute mode) the row's lse comes from the forward pass over the whole
+// vocabulary, the statistics and q cover one vocabulary slice starting at index yoff, and no loss term
+// is written.
 template <typename T>
 __global__ __launch_bounds__(256) void k_merge_dlogits(void* ws, const float* seg_m, const float* seg_s,
                                                        int nseg, int64_t V_pad, const int* y32,
                                                        const float* s_label, const float* og,
-                                                       const DevParams* prm, float* loss_row) {
+                                                       const DevParams* prm, float* loss_row,
+                                                       const float* lse_in, int yoff) {
   using S = typename Traits<T>::S;
   constexpr int KV = Traits<T>::KV;
   extern __shared__ float sc_seg[];  // [nseg]: g * exp(m_seg - lse)
   const int c = blockIdx.x;
   const float* m = seg_m + (int64_t)c * nseg;
-  const float lse = row_lse(m, seg_s + (int64_t)c * nseg, nseg, c, y32, s_label, loss_row, nullptr);
-  const int y = y32[c];
-  const float g = y >= 0 ? prm->ginv : 0.0f;
+  const float lse = lse_in ? lse_in[c] : row_lse(m, seg_s + (int64_t)c * nseg, nseg, c, y32, s_label, loss_row, nullptr);
+  const int y0 = y32[c];
+  const float g = y0 >= 0 ? prm->ginv : 0.0f;
+  const int y = y0 >= 0 ? y0 - yoff : -1;  // the label's column in this slice (outside it: no match)
   for (int j = threadIdx.x; j < nseg; j += 256) sc_seg[j] = g * ex2((m[j] - lse) * kLog2e);
   __syncthreads();
   const float oc = og[c];
@@ -1176,11 +1201,14 @@ hipError_t launch_transpose(const Problem& p, const void* hidden, const Work& w,
 }
 
 hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t row0, int64_t rows,
-                      bool store_q, hipStream_t stream) {
+                      bool store_q, hipStream_t stream, VSlice vs) {
+  if (vs.vn < 0) vs = VSlice{0, p.V};
+  const int64_t V_pad = (vs.vn + TILE - 1) / TILE * TILE;
+  const size_t esz = p.dtype == 0 ? 2 : 4;
   FwdArgs a;
   a.XT = w.xt;
   a.ldt = w.chunk_cap;
-  a.W = W;
+  a.W = (const char*)W + vs.v0 * p.H * (int64_t)esz;
   a.ws = w.ws_e;
   a.seg_m = w.seg_m;
   a.seg_s = w.seg_s;
@@ -1189,12 +1217,13 @@ hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t ro
   a.og = w.og + row0;
   a.prm = w.params;
   a.H = p.H;
-  a.V = p.V;
-  a.V_pad = p.V_pad;
-  a.nseg = (int)p.nseg;
+  a.V = vs.vn;
+  a.V_pad = V_pad;
+  a.nseg = (int)(V_pad / kSeg);
   a.rows = (int)rows;
+  a.yoff = (int)vs.v0;
   a.softcap = p.softcap;
-  const unsigned grid = (unsigned)((p.V_pad / TILE) * ((rows + TILE - 1) / TILE));
+  const unsigned grid = (unsigned)((V_pad / TILE) * ((rows + TILE - 1) / TILE));
   if (p.dtype == 0) {
     if (store_q)
       k_fwd<__bf16, true><<<grid, NTHR, 0, stream>>>(a);
@@ -1209,15 +1238,19 @@ hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t ro
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream) {
+hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream,
+                        VSlice vs, const float* lse_in) {
+  if (vs.vn < 0) vs = VSlice{0, p.V};
+  const int64_t V_pad = (vs.vn + TILE - 1) / TILE * TILE, nseg = V_pad / kSeg;
+  const float* lse = lse_in ? lse_in + row0 : nullptr;
   if (p.dtype == 0)
-    k_merge_dlogits<__bf16><<<(unsigned)rows, 256, (size_t)p.nseg * 4, stream>>>(w.ws_e, w.seg_m, w.seg_s, (int)p.nseg, p.V_pad,
-                                                              w.y32 + row0, w.s_label + row0, w.og + row0,
-                                                              w.params, w.loss_row + row0);
+    k_merge_dlogits<__bf16><<<(unsigned)rows, 256, (size_t)nseg * 4, stream>>>(
+        w.ws_e, w.seg_m, w.seg_s, (int)nseg, V_pad, w.y32 + row0, w.s_label + row0, w.og + row0, w.params,
+        w.loss_row + row0, lse, (int)vs.v0);
   else
-    k_merge_dlogits<float><<<(unsigned)rows, 256, (size_t)p.nseg * 4, stream>>>(w.ws_e, w.seg_m, w.seg_s, (int)p.nseg, p.V_pad,
-                                                             w.y32 + row0, w.s_label + row0, w.og + row0,
-                                                             w.params, w.loss_row + row0);
+    k_merge_dlogits<float><<<(unsigned)rows, 256, (size_t)nseg * 4, stream>>>(
+        w.ws_e, w.seg_m, w.seg_s, (int)nseg, V_pad, w.y32 + row0, w.s_label + row0, w.og + row0, w.params,
+        w.loss_row + row0, lse, (int)vs.v0);
   return hipGetLastError();
 }
 
@@ -1230,12 +1263,14 @@ hipError_t launch_rows(const Problem& p, const Work& w, int64_t row0, int64_t ro
 }
 
 hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_hidden, int64_t row0,
-                     int64_t rows, int splits, hipStream_t stream) {
+                     int64_t rows, int splits, hipStream_t stream, VSlice vs, int part_mode) {
+  if (vs.vn < 0) vs = VSlice{0, p.V};
+  const int64_t V_pad = (vs.vn + TILE - 1) / TILE * TILE;
   const size_t esz = p.dtype == 0 ? 2 : 4;
-  const int nk = (int)(p.V_pad * (p.dtype == 0 ? 2 : 4) / kStepBytes);
-  (void)esz;
+  const int nk = (int)(V_pad * (int64_t)esz / kStepBytes);
+  if (part_mode != 0 && splits != 1) return hipErrorInvalidValue;
   DxArgs a;
-  a.W = W;
+  a.W = (const char*)W + vs.v0 * p.H * (int64_t)esz;
   a.ws = w.ws_e;
   a.out = grad_hidden;
   a.gmap = p.gmap;
@@ -1243,11 +1278,13 @@ hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_
   a.accumulate = p.acc_gh ? 1 : 0;
   a.part = w.dx_part;
   a.H = p.H;
-  a.V = p.V;
-  a.V_pad = p.V_pad;
+  a.V = vs.vn;
+  a.V_pad = V_pad;
   a.rows = (int)rows;
   a.splits = splits;
   a.ksteps_per_split = (nk + splits - 1) / splits;
+  a.part_out = part_mode != 0 ? 1 : 0;
+  a.part_acc = part_mode == 2 ? 1 : 0;
   const unsigned tiles = (unsigned)(((rows + TILE - 1) / TILE) * ((p.H + TILE - 1) / TILE));
   if (p.dtype == 0)
     k_dx<__bf16><<<tiles * splits, NTHR, 0, stream>>>(a);
@@ -1280,20 +1317,22 @@ hipError_t launch_zero_rows(const Problem& p, void* grad_hidden, int64_t B, int6
 }
 
 hipError_t launch_dw(const Problem& p, const void* hidden, const Work& w, float* grad_W, int64_t row0,
-                     int64_t rows, bool accumulate, hipStream_t stream) {
+                     int64_t rows, bool accumulate, hipStream_t stream, VSlice vs) {
+  if (vs.vn < 0) vs = VSlice{0, p.V};
+  const int64_t V_pad = (vs.vn + TILE - 1) / TILE * TILE;
   const size_t esz = p.dtype == 0 ? 2 : 4;
   if (!p.hidden_dense && !w.xs) return hipErrorInvalidValue;
   DwArgs a;
   // rows in the plain layout are read where they are; mapped rows from the chunk's gathered copy
   a.X = p.hidden_dense ? (const void*)((const char*)hidden + row0 * p.H * esz) : (const void*)w.xs;
   a.ws = w.ws_e;
-  a.dW = grad_W;
+  a.dW = grad_W + vs.v0 * p.H;
   a.H = p.H;
-  a.V = p.V;
-  a.V_pad = p.V_pad;
+  a.V = vs.vn;
+  a.V_pad = V_pad;
   a.rows = (int)rows;
   a.accumulate = accumulate ? 1 : 0;
-  const unsigned grid = (unsigned)(((p.V + TILE - 1) / TILE) * ((p.H + TILE - 1) / TILE));
+  const unsigned grid = (unsigned)(((vs.vn + TILE - 1) / TILE) * ((p.H + TILE - 1) / TILE));
   if (p.dtype == 0)
     k_dw<__bf16><<<grid, NTHR, 0, stream>>>(a);
   else

@@ -84,6 +84,9 @@ def lib() -> ctypes.CDLL:
                                                      ctypes.c_float, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
             L.flce_forward_rows.argtypes = [vp, vp, vp, vp, rp, i64, i64, i32, i64, ctypes.c_float, i32,
                                             vp, vp, vp, vp, ctypes.c_size_t, vp]
+            L.flce_recompute_workspace_size.argtypes = [vp, i64, i64, i64, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
+            L.flce_forward_backward_recompute.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, ctypes.c_float,
+                                                          i32, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
             L.flce_status.argtypes = [vp, vp]
             L.flce_profile_begin.argtypes = [vp, i32]
             L.flce_profile_end.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
@@ -92,6 +95,7 @@ def lib() -> ctypes.CDLL:
             for f in ("flce_create", "flce_destroy", "flce_workspace_size", "flce_chunk_plan",
                       "flce_forward_backward", "flce_forward_workspace_size", "flce_forward", "flce_status",
                       "flce_workspace_size_rows", "flce_forward_backward_rows", "flce_forward_rows",
+                      "flce_recompute_workspace_size", "flce_forward_backward_recompute",
                       "flce_profile_begin", "flce_profile_end"):
                 getattr(L, f).restype = i32
             _LIB = L
@@ -114,6 +118,13 @@ def forward_workspace_size(BT: int, H: int, V: int, dtype=torch.bfloat16, handle
     out = ctypes.c_size_t()
     _check(lib().flce_forward_workspace_size(handle, BT, H, V, _DTYPES[dtype], ctypes.byref(out)),
            "flce_forward_workspace_size")
+    return out.value
+
+
+def recompute_workspace_size(BT: int, H: int, V: int, dtype=torch.bfloat16, v_slice: int = 0, handle=None) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().flce_recompute_workspace_size(handle, BT, H, V, _DTYPES[dtype], v_slice, ctypes.byref(out)),
+           "flce_recompute_workspace_size")
     return out.value
 
 
@@ -218,6 +229,32 @@ class FLCE:
             gh.data_ptr(), gw.data_ptr(), workspace.data_ptr(), workspace.numel(),
             ctypes.c_void_p(stream.cuda_stream))
         _check(rc, "flce_forward_backward")
+        return loss, gh, gw
+
+    def forward_backward_recompute(self, hidden: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
+                                   ignore_index: int = -100, softcap: float = 0.0, reduction: str = "mean",
+                                   v_slice: int = 0, out=None, workspace: torch.Tensor | None = None, stream=None):
+        """The recompute mode (logits formed twice, one vocabulary slice of 16-bit values kept at a
+        time); returns (loss, grad_hidden, grad_W fp32) like forward_backward."""
+        BT, H, V = self._check_inputs(hidden, W, labels)
+        if reduction not in _REDUCTIONS:
+            raise ValueError("reduction must be 'mean' or 'sum'")
+        need = recompute_workspace_size(BT, H, V, hidden.dtype, v_slice, self._h)
+        if workspace is None:
+            workspace = self.workspace(need)
+        if out is None:
+            loss = torch.empty((), dtype=torch.float32, device=self.device)
+            gh = torch.empty_like(hidden)
+            gw = torch.empty((V, H), dtype=torch.float32, device=self.device)
+        else:
+            loss, gh, gw = out
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        rc = lib().flce_forward_backward_recompute(
+            self._h, hidden.data_ptr(), W.data_ptr(), labels.data_ptr(), BT, H, V, _DTYPES[hidden.dtype],
+            int(ignore_index), float(softcap), _REDUCTIONS[reduction], int(v_slice), loss.data_ptr(),
+            gh.data_ptr(), gw.data_ptr(), workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+        _check(rc, "flce_forward_backward_recompute")
         return loss, gh, gw
 
     def forward(self, hidden: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,

@@ -238,3 +238,31 @@ def test_chunk_plan_invariants_random_bt():
         assert c % 256 == 0 and 0 < c <= 4096
         assert (n - 1) * c < bt <= n * c
         assert n == -(-bt // 4096)
+
+
+def test_recompute_workspace_size_keeps_a_vocabulary_slice():
+    H, V = 4096, 128256
+    full = flce.workspace_size(8192, H, V)
+    ws = {vs: flce.recompute_workspace_size(8192, H, V, v_slice=vs) for vs in (0, 1024, 4096, 8192, 16384)}
+    assert ws[0] == ws[8192]                      # 0 selects 8192 columns
+    assert ws[1024] < ws[4096] < ws[8192] < ws[16384] < full
+    # one 16-bit [4096][slice] buffer instead of [4096][V]: the slice difference is exactly that
+    assert ws[16384] - ws[8192] == 4096 * 8192 * 2
+    # a slice wider than V is capped at V rounded up to the tile width
+    assert flce.recompute_workspace_size(300, 128, 1000, v_slice=1 << 20) == \
+        flce.recompute_workspace_size(300, 128, 1000, v_slice=1024)
+    out = ctypes.c_size_t()
+    assert L.flce_recompute_workspace_size(NULL, 8, 64, 10, 0, -1, ctypes.byref(out)) == -1
+
+
+def test_recompute_rejects_before_any_device_call():
+    fake = ctypes.c_void_p(1)
+    p = ctypes.c_void_p(256)
+    call = lambda h, red=1, vs=0, softcap=0.0, ptr=p: L.flce_forward_backward_recompute(  # noqa: E731
+        h, ptr, ptr, ptr, 4, 64, 10, 0, -100, softcap, red, vs, ptr, ptr, ptr, ptr, 1 << 30, NULL)
+    assert call(NULL) == -1
+    assert call(fake, red=0) == -2
+    assert call(fake, red=5) == -1
+    assert call(fake, vs=-5) == -1
+    assert call(fake, softcap=float("nan")) == -1
+    assert call(fake, ptr=ctypes.c_void_p(264)) == -1
