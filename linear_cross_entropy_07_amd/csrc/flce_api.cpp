@@ -81,6 +81,7 @@ int dx_splits(int64_t rows, int64_t H, int64_t V_pad, int dtype, int ncu) {
 
 struct Layout {
   size_t off_e, off_m, off_s, off_y, off_sl, off_og, off_loss, off_part, off_xt, off_xs, off_lse, off_params, total;
+  bool has_xs;  // the gathered-rows copy of hidden exists
   int splits;
   int64_t chunk_rows;
 };
@@ -114,7 +115,8 @@ Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu
   L.off_loss = take((size_t)BT * 4);
   L.off_part = take(L.splits > 1 ? (size_t)L.splits * rows * H * 4 : 0);
   L.off_xt = take((size_t)rows * H * esz);
-  L.off_xs = take(backward && xstage ? (size_t)rows * H * esz : 0);
+  L.has_xs = backward && xstage;
+  L.off_xs = take(L.has_xs ? (size_t)rows * H * esz : 0);
   L.off_lse = take(0);
   L.total = off;
   return L;
@@ -317,7 +319,7 @@ Call make_call(flce_ctx* h, const Layout& L, const Rows& R, int64_t H, int64_t V
   w.dx_part = L.splits > 1 ? (float*)(base + L.off_part) : nullptr;
   w.params = (flce::DevParams*)(base + L.off_params);
   w.xt = base + L.off_xt;
-  w.xs = L.off_xs != L.total ? base + L.off_xs : nullptr;
+  w.xs = L.has_xs ? base + L.off_xs : nullptr;
   w.chunk_cap = L.chunk_rows;
   return c;
 }
