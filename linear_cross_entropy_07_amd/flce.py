@@ -415,9 +415,12 @@ def engine(device=None) -> FLCE:
 
 class _FLCEFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, hidden, W, labels, ignore_index, softcap, reduction):
-        loss, gh, gw = engine(hidden.device).forward_backward(hidden, W, labels, ignore_index, softcap,
-                                                               reduction)
+    def forward(ctx, hidden, W, labels, ignore_index, softcap, reduction, shift):
+        e = engine(hidden.device)
+        if hidden.dim() == 3:
+            loss, gh, gw = e.forward_backward_seq(hidden, W, labels, shift, ignore_index, softcap, reduction)
+        else:
+            loss, gh, gw = e.forward_backward(hidden, W, labels, ignore_index, softcap, reduction)
         ctx.save_for_backward(gh, gw)
         ctx.w_dtype = W.dtype
         return loss
@@ -425,12 +428,17 @@ class _FLCEFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_out):
         gh, gw = ctx.saved_tensors
-        return gh * grad_out.to(gh.dtype), (gw * grad_out).to(ctx.w_dtype), None, None, None, None
+        return gh * grad_out.to(gh.dtype), (gw * grad_out).to(ctx.w_dtype), None, None, None, None, None
 
 
-def flce_loss(hidden, W, labels, ignore_index: int = -100, softcap: float = 0.0, reduction: str = "mean"):
+def flce_loss(hidden, W, labels, ignore_index: int = -100, softcap: float = 0.0, reduction: str = "mean",
+              shift: bool = False):
     """Loss of softmax cross-entropy over hidden @ W.T (optionally softcapped) with autograd support.
 
-    The gradients are produced in the same fused call as the loss and scaled by the upstream
-    gradient in backward (e.g. a gradient-accumulation divisor)."""
-    return _FLCEFunction.apply(hidden, W, labels, ignore_index, softcap, reduction)
+    hidden is [BT, H] with labels [BT], or [B, T, H] (any strides, H contiguous) with labels [B, T];
+    for the latter, shift=True scores position t against label t+1 and leaves the last position out
+    (its gradient is zero). The gradients are produced in the same fused call as the loss and scaled
+    by the upstream gradient in backward (e.g. a gradient-accumulation divisor)."""
+    if shift and hidden.dim() != 3:
+        raise ValueError("shift needs hidden [B, T, H] and labels [B, T]")
+    return _FLCEFunction.apply(hidden, W, labels, ignore_index, softcap, reduction, bool(shift))

@@ -223,3 +223,22 @@ def test_llama_head_sequences_equal_plain_call_bitwise():
     assert torch.equal(g1[:, :-1, :].reshape(-1, w.H), g2)
     assert torch.all(g1[:, -1, :] == 0).item()
     assert torch.equal(w1, w2)
+
+
+def test_autograd_wrapper_on_sequences():
+    """flce_loss on hidden [B,T,H] with shift: the training-loop usage (loss / accumulation steps,
+    then backward) gives the oracle's scaled gradients, zero on the last positions."""
+    from linear_cross_entropy_07_amd.flce import flce_loss
+
+    dev = device()
+    X3, W, Y2 = _seq_inputs(2, 129, 64, 300, "bf16", seed=46)
+    announce("rows: autograd wrapper, [2,129,64] shifted, loss / 4")
+    h = X3.to(dev).requires_grad_(True)
+    Wd = W.to(dev).requires_grad_(True)
+    loss = flce_loss(h, Wd, Y2.to(dev), shift=True)
+    (loss / 4).backward()
+    ol, odx, odw, _, _ = oracle.flce_sequences(X3, W, Y2, 1, IGN, 0.0, "mean", 0.25)
+    assert abs(float(loss.detach().cpu()) - ol) <= TOL["bf16"]["loss"] * ol
+    assert rel_fro(h.grad.double().cpu().numpy(), odx) <= TOL["bf16"]["grad"]
+    assert rel_fro(Wd.grad.double().cpu().numpy(), odw) <= TOL["bf16"]["grad"]
+    assert torch.all(h.grad[:, -1, :] == 0).item()
