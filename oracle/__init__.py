@@ -13,5 +13,6 @@ from .flce_oracle import (  # noqa: F401
     flce_forward_backward,
     flce_forward,
     flce_rows,
+    flce_vocab_rows,
     flce_sequences,
 )

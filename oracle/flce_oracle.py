@@ -38,8 +38,10 @@ Readings taken where the pages are silent (the same list is kept with the design
   * no intermediate is rounded to bf16: the inputs' exact values are widened to
     float64 and every step stays in float64.
 
-There is no blocking, online softmax, chunking or fusion here: rows are
-independent, and the whole [BT, V] logits matrix of the rows asked for is built.
+There is no online softmax, chunking or fusion here: rows are independent, and
+each row's whole logits vector is built. All functions but flce_vocab_rows build
+the [BT, V] logits matrix of the rows asked for at once; flce_vocab_rows, which
+must cover every row of a full-size call, builds it in blocks of rows.
 """
 from __future__ import annotations
 
@@ -52,6 +54,7 @@ __all__ = [
     "valid_mask",
     "flce_forward_backward",
     "flce_rows",
+    "flce_vocab_rows",
     "flce_sequences",
 ]
 
@@ -210,6 +213,57 @@ def flce_rows(X, W, y, rows, n_valid: int, ignore_index: int = -100, softcap: fl
     t = _row_terms(Xr, Wf, yr, ignore_index, softcap, reduction, n_valid)
     return dict(lse=t["lse"], loss_rows=t["loss_rows"], dX=t["dZ"] @ Wf, valid=t["valid"],
                 s_label=t["s_label"])
+
+
+def flce_vocab_rows(X, W, y, vrows, ignore_index: int = -100, softcap: float = 0.0,
+                    reduction: str = "mean", block_rows: int = 1024, threads: int = 0):
+    """Selected rows of dL/dW for a call of any size: dW[v, :] = sum_t dz_tv x_t for v in vrows.
+
+    Every dz_tv needs the row's lse over the whole vocabulary, so the full float64 logits row of
+    every t is built, in blocks of block_rows rows so that host memory stays bounded (rows are
+    independent; within a row nothing is streamed: max, then the sum of exponentials, as in
+    row_logsumexp). Blocks run on a thread pool (numpy releases the GIL in BLAS and ufuncs); their
+    contributions are summed in block order. Returns dict(dW=[len(vrows), H] f64, lse=[BT], N).
+    """
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+
+    Xf = _f64(X)
+    Wf = _f64(W)
+    yl = _labels(y)
+    _check(Xf, Wf, yl, softcap, reduction)
+    vrows = np.asarray(vrows, dtype=np.int64)
+    V = Wf.shape[0]
+    if vrows.size and (vrows.min() < 0 or vrows.max() >= V):
+        raise ValueError("vocabulary rows out of range")
+    valid = valid_mask(yl, V, ignore_index)
+    N = int(valid.sum())
+    if reduction == "mean":
+        g = np.where(valid, 1.0 / N, 0.0) if N > 0 else np.zeros(Xf.shape[0])
+    else:
+        g = np.where(valid, 1.0, 0.0)
+
+    def block(b0):
+        b1 = min(b0 + block_rows, Xf.shape[0])
+        S = apply_softcap(logits(Xf[b0:b1], Wf), softcap)
+        _, lse = row_logsumexp(S)
+        Sv = S[:, vrows]
+        dS = np.exp(Sv - lse[:, None])
+        onehot = (yl[b0:b1, None] == vrows[None, :]) & valid[b0:b1, None]
+        dS -= onehot
+        dS *= g[b0:b1, None]
+        dZ = dS * (1.0 - (Sv / softcap) ** 2) if softcap > 0.0 else dS
+        return lse, dZ.T @ Xf[b0:b1]
+
+    starts = list(range(0, Xf.shape[0], block_rows))
+    nthr = threads or min(len(starts), len(os.sched_getaffinity(0)), 16) or 1
+    with ThreadPoolExecutor(max_workers=nthr) as ex:
+        parts = list(ex.map(block, starts))
+    dW = np.zeros((vrows.size, Wf.shape[1]))
+    for _, d in parts:
+        dW += d
+    lse = np.concatenate([l for l, _ in parts]) if parts else np.zeros(0)
+    return dict(dW=dW, lse=lse, N=N)
 
 
 def flce_sequences(X3, W, Y2, shift: int = 1, ignore_index: int = -100, softcap: float = 0.0,

@@ -1,5 +1,6 @@
 """Full-size GPU checks at the workloads' real shapes, in the launch configuration the benchmark times
-(default chunk plan): sampled rows of grad_hidden against the oracle computed row by row, the loss of a
+(default chunk plan): sampled rows of grad_hidden against the oracle computed row by row, sampled rows
+of grad_W against the oracle (every row's lse over the whole vocabulary, in row blocks), the loss of a
 row subset against the oracle, and relations that hold at any size (loss additivity over row subsets,
 mean = sum / N, <grad_W, W> = <grad_hidden, hidden>, ignored rows exactly zero)."""
 import numpy as np
@@ -22,7 +23,20 @@ def _sample_rows(y, BT, rng, chunk=4096):
     return np.array(sorted(rows))
 
 
-def _fullsize_check(X, W, y, softcap, label):
+def _sample_vocab_rows(y, V, rng):
+    """V's first, last and middle rows, the most frequent label, a few labels and random rows; and
+    the subset of them that is no row's label (their gradient has no one-hot term)."""
+    yv = y.numpy()
+    lab = yv[yv != -100]
+    vrows = {0, V - 1, V // 2} | set(rng.choice(V, 6, replace=False).tolist())
+    if lab.size:
+        vals, counts = np.unique(lab, return_counts=True)
+        vrows |= {int(vals[np.argmax(counts)])} | set(lab[:3].tolist())
+    vrows = np.array(sorted(vrows))
+    return vrows, ~np.isin(vrows, lab)
+
+
+def _fullsize_check(X, W, y, softcap, label, vocab_rows=True):
     dev = device()
     e = flce.FLCE(dev)
     BT, H = X.shape
@@ -45,6 +59,18 @@ def _fullsize_check(X, W, y, softcap, label):
     print(f"   loss {loss:.6f}; sampled dX rows rel err {err:.2e}", flush=True)
     assert err <= tol["grad"]
     assert not np.any(got[~ref["valid"]])
+
+    # sampled grad_W rows vs the oracle, which needs the lse of every row over the whole vocabulary
+    if vocab_rows:
+        vrows, unlabelled = _sample_vocab_rows(y, W.shape[0], rng)
+        ref_w = oracle.flce_vocab_rows(X, W, y, vrows, softcap=softcap, block_rows=512)
+        got_w = gw[torch.from_numpy(vrows).to(dev)].double().cpu().numpy()
+        err_w = rel_fro(got_w, ref_w["dW"])
+        err_u = rel_fro(got_w[unlabelled], ref_w["dW"][unlabelled])
+        print(f"   sampled dW rows ({len(vrows)}) rel err {err_w:.2e}; rows that are no label "
+              f"({int(unlabelled.sum())}) {err_u:.2e}", flush=True)
+        assert err_w <= tol["grad"]
+        assert err_u <= tol["grad"]
 
     # loss of a 256-row subset (sum reduction) vs the oracle's per-row losses
     sub = np.sort(rng.choice(BT, 256, replace=False))
@@ -90,4 +116,4 @@ def test_ragged_sweep_samples():
     bts = inputs.ragged_bt_list(0, 20)
     for i in (0, 7, len(bts) - 1):
         X, W, y = inputs.make_ragged_call(bts[i], seed=100 + i)
-        _fullsize_check(X, W, y, 0.0, f"ragged call {i}")
+        _fullsize_check(X, W, y, 0.0, f"ragged call {i}", vocab_rows=(i == 0))

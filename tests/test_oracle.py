@@ -316,6 +316,41 @@ def test_flce_rows_matches_full():
     np.testing.assert_allclose(r["lse"], t["lse"][rows], rtol=1e-14)
 
 
+def _vocab_rows_case():
+    rng = np.random.default_rng(15)
+    X, W, y = _rand_case(rng, 37, 8, 29, ignore=5, w_scale=3.0)
+    y[30:36] = 3  # one vocabulary row that is the label of many rows
+    return X, W, y, [0, 3, 11, 28]
+
+
+@pytest.mark.parametrize("softcap", [0.0, 2.5])
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_vocab_rows_match_torch(softcap, reduction):
+    """Selected grad_W rows, computed in row blocks, against torch autograd and the full oracle."""
+    X, W, y, vrows = _vocab_rows_case()
+    _, _, tdW = _torch_reference(X, W, y, softcap, reduction)
+    r = oracle.flce_vocab_rows(X, W, y, vrows, softcap=softcap, reduction=reduction, block_rows=8)
+    assert _rel(r["dW"], tdW[vrows]) < 1e-12
+    full = oracle.flce_forward_backward(X, W, y, softcap=softcap, reduction=reduction, return_details=True)
+    np.testing.assert_allclose(r["dW"], full[2][vrows], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(r["lse"], full[3]["lse"], rtol=1e-14)
+    assert r["N"] == full[3]["N"]
+
+
+@pytest.mark.parametrize("mutation", ["no_softcap", "transposed_logits_use", "lse_without_max"])
+def test_vocab_rows_pin_catches_planted_mistakes(monkeypatch, mutation):
+    X, W, y, vrows = _vocab_rows_case()
+    _, _, tdW = _torch_reference(X, W, y, 2.5, "mean")
+    if mutation == "no_softcap":
+        monkeypatch.setattr(O, "apply_softcap", lambda Z, c: Z)
+    elif mutation == "transposed_logits_use":
+        monkeypatch.setattr(O, "logits", lambda X, W: (X @ W.T)[:, ::-1].copy())
+    else:
+        monkeypatch.setattr(O, "row_logsumexp", lambda S: (S.max(1), np.log(np.exp(S).sum(1)) + 0.01))
+    r = oracle.flce_vocab_rows(X, W, y, vrows, softcap=2.5, block_rows=8)
+    assert _rel(r["dW"], tdW[vrows]) > 1e-6
+
+
 # ---------------------------------------------------------------- planted mistakes must be caught
 
 def _pins_pass(monkeypatch=None):
