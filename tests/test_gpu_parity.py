@@ -107,6 +107,27 @@ def test_logit_shift_metamorphic(dtype, a):
     assert not np.any(gdx[:, H + 1:]) and not np.any(gdw[:, H + 1:])
 
 
+@pytest.mark.parametrize("shape,softcap", [((300, 64, 1 << 20), 30.0), ((300, 65536, 1000), 0.0)],
+                         ids=["V=2^20", "H=65536"])
+def test_maximum_sizes(shape, softcap):
+    """The largest vocabulary (2^20) and hidden size (65536) the library accepts, against the oracle."""
+    BT, H, V = shape
+    w = inputs.custom(BT=BT, H=H, V=V, dtype="bf16", ignore_frac=0.1, w_std=0.05, name="max_size")
+    announce(w, softcap)
+    X, W, y = inputs.make_inputs(w, seed=14)
+    check_against_oracle(run_gpu(eng(), X, W, y, softcap=softcap), X, W, y, "bf16", softcap=softcap)
+    # one more row or column than that is refused before anything runs
+    dev = device()
+    with pytest.raises(flce.FlceError) as ei:
+        if V == 1 << 20:
+            eng().forward_backward(X[:4].to(dev), torch.zeros(V + 1, H, dtype=torch.bfloat16, device=dev),
+                                   y[:4].to(dev))
+        else:
+            eng().forward_backward(torch.zeros(4, H + 8, dtype=torch.bfloat16, device=dev),
+                                   torch.zeros(V, H + 8, dtype=torch.bfloat16, device=dev), y[:4].to(dev))
+    assert ei.value.code == -2
+
+
 def test_bt_zero():
     dev = device()
     announce("BT=0")
