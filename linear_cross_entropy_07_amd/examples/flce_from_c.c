@@ -5,11 +5,16 @@
  * usage: flce_from_c <inputs.bin> <outputs.bin>
  *
  * inputs.bin  (little endian): int64 BT, H, V; float softcap; int32 reduction (FLCE_MEAN or
- *             FLCE_SUM); then hidden [BT][H] and W [V][H] as bf16 bit patterns (uint16), labels [BT]
- *             int64.
- * outputs.bin: float loss; grad_hidden [BT][H] bf16 bit patterns; grad_W [V][H] float; then the
- *             forward-only call with FLCE_NONE: loss_rows [BT] float, lse_rows [BT] float; finally
- *             int32 status of each call (flce_status).
+ *             FLCE_SUM); int64 B (sequences for the sequence call, dividing BT); float grad_scale;
+ *             then hidden [BT][H] and W [V][H] as bf16 bit patterns (uint16), labels [BT] int64.
+ * outputs.bin: four calls on the same data, then int32 status of each call (flce_status):
+ *             1. flce_forward_backward: float loss; grad_hidden [BT][H] bf16 bit patterns; grad_W
+ *                [V][H] float;
+ *             2. flce_forward with FLCE_NONE: loss_rows [BT] float, lse_rows [BT] float;
+ *             3. flce_forward_backward_recompute with 256-wide vocabulary slices: as 1;
+ *             4. flce_forward_backward_rows over the rows as B sequences of T = BT / B positions,
+ *                each position scored against the next one's label (shift 1), gradients times
+ *                grad_scale: as 1 (the last position of each sequence gets a zero gradient row).
  * Exit code 0 on success; on any error a message names the failing call.
  */
 #include <stdint.h>
@@ -51,16 +56,17 @@ int main(int argc, char** argv) {
     fprintf(stderr, "cannot open %s\n", argv[1]);
     return 1;
   }
-  int64_t dims[3];
-  float softcap;
+  int64_t dims[3], nseq;
+  float softcap, grad_scale;
   int32_t reduction;
   if (!read_all(in, dims, sizeof dims) || !read_all(in, &softcap, sizeof softcap) ||
-      !read_all(in, &reduction, sizeof reduction)) {
+      !read_all(in, &reduction, sizeof reduction) || !read_all(in, &nseq, sizeof nseq) ||
+      !read_all(in, &grad_scale, sizeof grad_scale)) {
     fprintf(stderr, "short header\n");
     return 1;
   }
   const int64_t BT = dims[0], H = dims[1], V = dims[2];
-  if (BT <= 0 || H <= 0 || V <= 0) {
+  if (BT <= 0 || H <= 0 || V <= 0 || nseq <= 0 || BT % nseq != 0) {
     fprintf(stderr, "bad sizes\n");
     return 1;
   }
@@ -82,7 +88,7 @@ int main(int argc, char** argv) {
   }
   fclose(in);
 
-  void *d_x, *d_w, *d_y, *d_gh, *d_ws, *d_fws;
+  void *d_x, *d_w, *d_y, *d_gh, *d_ws, *d_fws, *d_rws, *d_sws;
   float *d_loss, *d_gw, *d_rows, *d_lse;
   HIP_OK(hipSetDevice(0));
   HIP_OK(hipMalloc(&d_x, nx * 2));
@@ -104,32 +110,62 @@ int main(int argc, char** argv) {
   FLCE_OK_(flce_forward_workspace_size(h, BT, H, V, FLCE_BF16, &fws_bytes));
   HIP_OK(hipMalloc(&d_ws, ws_bytes));
   HIP_OK(hipMalloc(&d_fws, fws_bytes));
+  const int64_t T = BT / nseq;
+  const flce_rows R = {nseq, T, 1, {T * H, H}, {T * H, H}, {T, 1}};
+  size_t rws_bytes = 0, sws_bytes = 0;
+  FLCE_OK_(flce_recompute_workspace_size(h, BT, H, V, FLCE_BF16, 256, &rws_bytes));
+  FLCE_OK_(flce_workspace_size_rows(h, &R, H, V, FLCE_BF16, &sws_bytes));
+  HIP_OK(hipMalloc(&d_rws, rws_bytes));
+  HIP_OK(hipMalloc(&d_sws, sws_bytes));
+  FILE* out = fopen(argv[2], "wb");
+  if (!out) {
+    fprintf(stderr, "cannot open %s\n", argv[2]);
+    return 1;
+  }
+#define COPY_OUT_(nbytes, host, dev)                                            \
+  do {                                                                          \
+    HIP_OK(hipMemcpy(host, dev, nbytes, hipMemcpyDeviceToHost));                \
+    if (!write_all(out, host, nbytes)) {                                        \
+      fprintf(stderr, "cannot write %s\n", argv[2]);                           \
+      return 1;                                                                 \
+    }                                                                           \
+  } while (0)
+  float loss = 0.0f;
+  int32_t st[4];
 
-  /* the fused forward + backward, then the forward alone with per-row terms, on the null stream */
+  /* 1. the fused forward + backward and 2. the forward alone with per-row terms, on the null stream */
   FLCE_OK_(flce_forward_backward(h, d_x, d_w, (const int64_t*)d_y, BT, H, V, FLCE_BF16, -100, softcap, reduction,
                                  d_loss, d_gh, d_gw, d_ws, ws_bytes, NULL));
-  const int32_t st1 = flce_status(h, NULL);
+  st[0] = flce_status(h, NULL);
+  COPY_OUT_(4, &loss, d_loss);
+  const float loss_fused = loss;
+  COPY_OUT_(nx * 2, gh, d_gh);
+  COPY_OUT_(nw * 4, gw, d_gw);
   FLCE_OK_(flce_forward(h, d_x, d_w, (const int64_t*)d_y, BT, H, V, FLCE_BF16, -100, softcap, FLCE_NONE, NULL,
                         d_rows, d_lse, d_fws, fws_bytes, NULL));
-  const int32_t st2 = flce_status(h, NULL);
-  HIP_OK(hipDeviceSynchronize());
-
-  float loss = 0.0f;
-  HIP_OK(hipMemcpy(&loss, d_loss, 4, hipMemcpyDeviceToHost));
-  HIP_OK(hipMemcpy(gh, d_gh, nx * 2, hipMemcpyDeviceToHost));
-  HIP_OK(hipMemcpy(gw, d_gw, nw * 4, hipMemcpyDeviceToHost));
-  HIP_OK(hipMemcpy(rows, d_rows, (size_t)BT * 4, hipMemcpyDeviceToHost));
-  HIP_OK(hipMemcpy(lse, d_lse, (size_t)BT * 4, hipMemcpyDeviceToHost));
-  FLCE_OK_(flce_destroy(h));
-
-  FILE* out = fopen(argv[2], "wb");
-  if (!out || !write_all(out, &loss, 4) || !write_all(out, gh, nx * 2) || !write_all(out, gw, nw * 4) ||
-      !write_all(out, rows, (size_t)BT * 4) || !write_all(out, lse, (size_t)BT * 4) ||
-      !write_all(out, &st1, 4) || !write_all(out, &st2, 4)) {
+  st[1] = flce_status(h, NULL);
+  COPY_OUT_((size_t)BT * 4, rows, d_rows);
+  COPY_OUT_((size_t)BT * 4, lse, d_lse);
+  /* 3. the same results with the logits formed twice and one 256-wide vocabulary slice kept */
+  FLCE_OK_(flce_forward_backward_recompute(h, d_x, d_w, (const int64_t*)d_y, BT, H, V, FLCE_BF16, -100, softcap,
+                                           reduction, 256, d_loss, d_gh, d_gw, d_rws, rws_bytes, NULL));
+  st[2] = flce_status(h, NULL);
+  COPY_OUT_(4, &loss, d_loss);
+  COPY_OUT_(nx * 2, gh, d_gh);
+  COPY_OUT_(nw * 4, gw, d_gw);
+  /* 4. the rows as sequences: next-token labels by addressing, scaled gradients */
+  FLCE_OK_(flce_forward_backward_rows(h, d_x, d_w, (const int64_t*)d_y, &R, H, V, FLCE_BF16, -100, softcap,
+                                      reduction, grad_scale, 0, d_loss, d_gh, d_gw, d_sws, sws_bytes, NULL));
+  st[3] = flce_status(h, NULL);
+  COPY_OUT_(4, &loss, d_loss);
+  COPY_OUT_(nx * 2, gh, d_gh);
+  COPY_OUT_(nw * 4, gw, d_gw);
+  if (!write_all(out, st, sizeof st)) {
     fprintf(stderr, "cannot write %s\n", argv[2]);
     return 1;
   }
   fclose(out);
+  FLCE_OK_(flce_destroy(h));
   hipFree(d_x);
   hipFree(d_w);
   hipFree(d_y);
@@ -140,6 +176,8 @@ int main(int argc, char** argv) {
   hipFree(d_lse);
   hipFree(d_ws);
   hipFree(d_fws);
+  hipFree(d_rws);
+  hipFree(d_sws);
   free(x);
   free(w);
   free(y);
@@ -147,7 +185,7 @@ int main(int argc, char** argv) {
   free(gw);
   free(rows);
   free(lse);
-  printf("flce_from_c: BT=%lld H=%lld V=%lld loss %.7f status %d %d\n", (long long)BT, (long long)H, (long long)V,
-         loss, st1, st2);
+  printf("flce_from_c: BT=%lld H=%lld V=%lld loss %.7f (sequences %.7f) status %d %d %d %d\n", (long long)BT,
+         (long long)H, (long long)V, loss_fused, loss, st[0], st[1], st[2], st[3]);
   return 0;
 }
