@@ -34,6 +34,9 @@
  *     outputs are then untouched. The compute entry points never allocate, never synchronise and
  *     enqueue all their work on `stream`.
  *   - A handle may be used by one stream at a time (it holds a small device status word).
+ *   - Since the compute entry points only launch kernels (no allocation, no memset, no copy, no
+ *     synchronisation), a caller may capture them into a HIP graph on `stream` and replay it; each
+ *     replay reads the buffers' current contents. flce_status and flce_profile_* are not capturable.
  */
 #ifndef FLCE_H
 #define FLCE_H
