@@ -789,13 +789,16 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
 }
 
 // ---- grad_hidden = dZ . W ---------------------------------------------------------------------
-// The fp32 tile goes through the (then idle) LDS ring in passes of kDxPassRows rows, one wave row-half
-// (WM rows) per pass, and leaves as 16-byte pieces of whole caller rows: each row is placed by the row
-// map (sequences with strides, shifted labels), and with `accumulate` added to what the row holds
-// (one rounding to the output type, after the add).
+// The fp32 tile goes through the (then idle) LDS ring in passes of kDxPassRows rows and leaves as
+// 16-byte pieces of whole caller rows: each row is placed by the row map (sequences with strides,
+// shifted labels), and with `accumulate` added to what the row holds (one rounding to the output
+// type, after the add). Pass p stages row blocks 2p and 2p+1 of every wave (tile rows
+// wm * WM + 64 p .. + 63), so the accumulators of a pass are dead before its read-out.
 constexpr int kDxRowBytes = TILE * 4;
 constexpr int kDxPassRows = WM;
 static_assert(kDxPassRows * kDxRowBytes <= kStages * kStageBytes, "a pass fits the LDS ring");
+static_assert(TBM % (TILE / kDxPassRows) == 0 && kDxPassRows == 2 * 32 * (TBM / (TILE / kDxPassRows)),
+              "a pass stages the same number of row blocks of each of the two wave-rows");
 template <typename T>
 __device__ __forceinline__ void dx_store_tile(const DxArgs& a, const f32x16 (&acc)[TBM][TBN], int c0, int h0,
                                               int vrows, char* smem) {
@@ -804,24 +807,26 @@ __device__ __forceinline__ void dx_store_tile(const DxArgs& a, const f32x16 (&ac
   constexpr int RPI = NTHR / TPR;          // rows per read-out iteration
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1, half = lane >> 5;
   const int ch = (int)threadIdx.x % TPR, h = h0 + ch * OV;
+  constexpr int kBlocksPerPass = TBM / (TILE / kDxPassRows);  // row blocks of a wave per pass (2)
+  constexpr int kWaveRows = 32 * kBlocksPerPass;              // rows of a wave-row per pass (64)
 #pragma unroll
   for (int pass = 0; pass < TILE / kDxPassRows; ++pass) {
-    if (wm == pass) {
 #pragma unroll
-      for (int i = 0; i < TBM; ++i)
+    for (int ib = 0; ib < kBlocksPerPass; ++ib) {
+      const int i = pass * kBlocksPerPass + ib;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * kWaveRows + 32 * ib + 8 * (r >> 2) + 4 * half + (r & 3);
 #pragma unroll
-          for (int j = 0; j < TBN; ++j) {
-            const int cl = wn * WN + 32 * j + (lane & 31);
-            *(float*)(smem + rl * kDxRowBytes + cl * 4) = acc[i][j][r];
-          }
+        for (int j = 0; j < TBN; ++j) {
+          const int cl = wn * WN + 32 * j + (lane & 31);
+          *(float*)(smem + rl * kDxRowBytes + cl * 4) = acc[i][j][r];
         }
+      }
     }
     __syncthreads();
     for (int rl = (int)threadIdx.x / TPR; rl < kDxPassRows; rl += RPI) {
-      const int c = pass * kDxPassRows + rl;
+      const int c = (rl / kWaveRows) * WM + pass * kWaveRows + rl % kWaveRows;
       if (c < vrows && h < a.H) {
         const float* src = (const float*)(smem + rl * kDxRowBytes) + ch * OV;
         float f[OV];
