@@ -852,7 +852,10 @@ __device__ __forceinline__ void dx_store_tile(const DxArgs& a, const f32x16 (&ac
   }
 }
 
-template <typename T>
+// PART: the tile leaves as fp32 partials (split-K, or the recompute mode's running sum) instead of
+// through the row-staged epilogue; one output path per instantiation keeps the register pressure of
+// the other out of each kernel.
+template <typename T, bool PART>
 __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes];
 
@@ -876,7 +879,7 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
 
   // output tile (c0, h0); rows past the chunk and columns past H are dropped
   const int vrows = min(TILE, a.rows - c0), ncols = (int)min<int64_t>(TILE, a.H - h0);
-  if (a.splits == 1 && !a.part_out) {
+  if constexpr (!PART) {
     dx_store_tile<T>(a, acc, c0, h0, vrows, smem);
   } else {
     const rsrc_t ro = make_rsrc(a.part + ((int64_t)split * a.rows + c0) * a.H + h0, ((int64_t)vrows * a.H - h0) * 4);
@@ -1291,10 +1294,18 @@ hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_
   a.part_out = part_mode != 0 ? 1 : 0;
   a.part_acc = part_mode == 2 ? 1 : 0;
   const unsigned tiles = (unsigned)(((rows + TILE - 1) / TILE) * ((p.H + TILE - 1) / TILE));
-  if (p.dtype == 0)
-    k_dx<__bf16><<<tiles * splits, NTHR, 0, stream>>>(a);
-  else
-    k_dx<float><<<tiles * splits, NTHR, 0, stream>>>(a);
+  const bool part = a.splits != 1 || a.part_out;
+  if (p.dtype == 0) {
+    if (part)
+      k_dx<__bf16, true><<<tiles * splits, NTHR, 0, stream>>>(a);
+    else
+      k_dx<__bf16, false><<<tiles * splits, NTHR, 0, stream>>>(a);
+  } else {
+    if (part)
+      k_dx<float, true><<<tiles * splits, NTHR, 0, stream>>>(a);
+    else
+      k_dx<float, false><<<tiles * splits, NTHR, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
