@@ -262,7 +262,8 @@ def main():
     # launch stream (events created here, before the timed region)
     vs_eff = min(-(-(args.vslice or 8192) // 256) * 256, -(-V // 256) * 256)
     launches_per_step = 8 + n_chunks * (8 + (4 * -(-V // vs_eff) if recompute else 8))
-    eng.profile_begin(max_launches=launches_per_step * args.steps)
+    capacity = launches_per_step * args.steps
+    eng.profile_begin(max_launches=capacity)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -272,7 +273,9 @@ def main():
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     kt = eng.profile_end(stream)
-    if kt["finalize"][1] != args.steps:  # the last launch of every step was recorded
+    # every launch was recorded: the events did not run out, and the last launch of every step (the
+    # loss; sequence calls also count their last-position zeroing under the same kind) is there
+    if sum(c for _, c in kt.values()) >= capacity or kt["finalize"][1] < args.steps:
         raise SystemExit("kernel profile incomplete: more launches per step than events")
     per = sorted(a.elapsed_time(b) for a, b in ev)
     ms_med = statistics.median(per)
