@@ -37,7 +37,9 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_head")
     ap.add_argument("--chunk", type=int, default=0, help="chunk_rows_max (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4608, help="rows of the oracle's bounded sample")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the oracle's bounded sample (0 = about 15 TFLOP of float64 work, at most the "
+                         "whole call)")
     ap.add_argument("--profile-only", action="store_true", help="warmup + steps, no extras (for rocprofv3)")
     ap.add_argument("--mode", choices=("fwd_bwd", "forward", "recompute"), default="fwd_bwd",
                     help="fwd_bwd: the fused forward + backward (default); forward: flce_forward only; "
@@ -70,22 +72,36 @@ def traffic_from_profiles(kernel: str, workload: str, launches_bytes_key: str = 
     return d.get(launches_bytes_key)
 
 
-def cpu_baseline(w, X, W, y, rows: int, forward_only: bool = False):
-    """The oracle as it stands, on the first `rows` rows of the same workload (bounded sample)."""
-    import numpy as np
+def cpu_rows_for(BT: int, H: int, V: int, forward_only: bool, rows: int = 0) -> int:
+    """Rows of the oracle's bounded sample: about 15 TFLOP of float64 work (10-20 s on the host's
+    cores), a multiple of 256, at most the whole call."""
+    if rows > 0:
+        return min(rows, BT)
+    per_row = (2.0 if forward_only else 6.0) * H * V
+    return max(1, min(BT, int(15e12 / per_row) // 256 * 256))
 
+
+def cpu_baseline(w, X, W, y, rows: int, forward_only: bool = False, BT: int | None = None):
+    """The oracle as it stands, timed on the first `rows` rows of the same workload (a bounded sample).
+    Its BLAS runs on as many threads as the process may use: the cores it is pinned to, capped by
+    OMP_NUM_THREADS when that is set (the host's share of cores); `cores` is that thread count."""
     import oracle
 
+    affinity = len(os.sched_getaffinity(0))
+    threads = affinity
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = max(1, min(threads, int(os.environ["OMP_NUM_THREADS"])))
     blas = "unknown"
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
 
-        info = threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] or [1])
-        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
                                  if i.get("user_api") == "blas"})) or blas
+        limiter = threadpool_limits(limits=threads, user_api="blas")
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+                           or [threads])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        limiter, blas_threads = None, threads
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -97,12 +113,16 @@ def cpu_baseline(w, X, W, y, rows: int, forward_only: bool = False):
     if forward_only:
         oracle.flce_forward(Xs, W, ys, -100, w.softcap, w.reduction)
     else:
-        oracle.flce_forward_backward(Xs, W, ys, -100, w.softcap, w.reduction)
+        oracle.flce_blocked(Xs, W, ys, -100, w.softcap, w.reduction, block_rows=1024)
     dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu": cpu, "blas": blas,
-            "sample": f"first {rows} of {w.BT} rows of {w.name} (full H={w.H}, V={w.V}), fp64 numpy/OpenBLAS "
-                      f"{'forward' if forward_only else 'forward+backward'} incl. widening inputs to fp64; "
-                      f"{dt:.2f} s"}
+    if limiter is not None:
+        limiter.unregister()
+    BT = w.BT if BT is None else BT
+    return {"value": rows / dt, "unit": "tokens/s", "cores": blas_threads, "affinity_cores": affinity,
+            "kind": "oracle", "cpu": cpu, "blas": blas,
+            "sample": f"first {rows} of {BT} rows of {w.name} (full H={w.H}, V={w.V}), fp64 numpy/OpenBLAS "
+                      f"{'forward' if forward_only else 'forward+backward (flce_blocked, 1024-row blocks)'} "
+                      f"incl. widening inputs to fp64; {dt:.2f} s on {blas_threads} BLAS threads"}
 
 
 def ragged_sweep(args, dev):
@@ -164,6 +184,10 @@ def ragged_sweep(args, dev):
                      "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
                      "traffic": None},
     }
+    if not args.no_cpu_baseline:
+        rows = cpu_rows_for(max(bts), H, V, False, args.cpu_rows)
+        print(f"# timing the oracle on {rows} rows", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, X, W, y, rows, BT=max(bts))
     print(json.dumps(out), flush=True)
 
 
@@ -257,28 +281,34 @@ def main():
         return
 
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    # per-kernel durations: the library brackets each of its launches with a HIP event pair on the
-    # launch stream (events created here, before the timed region)
+
+    def timed_pass():
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize(dev)
+        return sorted(a.elapsed_time(b) for a, b in ev), time.perf_counter() - t0
+
+    # the headline: K steps with nothing but one event pair per step around them
+    per, wall = timed_pass()
+    ms_med = statistics.median(per)
+    # the per-kernel breakdown: K more steps, each launch bracketed by a HIP event pair that the
+    # library records on the launch stream (events created before the timed region)
     vs_eff = min(-(-(args.vslice or 8192) // 256) * 256, -(-V // 256) * 256)
     launches_per_step = 8 + n_chunks * (8 + (4 * -(-V // vs_eff) if recompute else 8))
     capacity = launches_per_step * args.steps
     eng.profile_begin(max_launches=capacity)
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
+    per_prof, _ = timed_pass()
     kt = eng.profile_end(stream)
     # every launch was recorded: the events did not run out, and the last launch of every step (the
-    # loss; sequence calls also count their last-position zeroing under the same kind) is there
+    # loss) is there
     if sum(c for _, c in kt.values()) >= capacity or kt["finalize"][1] < args.steps:
         raise SystemExit("kernel profile incomplete: more launches per step than events")
-    per = sorted(a.elapsed_time(b) for a, b in ev)
-    ms_med = statistics.median(per)
     peak_extra = torch.cuda.max_memory_allocated(dev) - io_alloc
     print(f"# kernel ms/launch: " + ", ".join(f"{k} {v[0] / max(v[1], 1):.3f}x{v[1] // args.steps}"
                                             for k, v in kt.items() if v[1]), file=sys.stderr, flush=True)
@@ -316,6 +346,7 @@ def main():
         "mfma_frac_step": round(step_flops / (ms_med * 1e-3) / PEAK_BF16, 4),
         "ms_p10_p90": [round(per[len(per) // 10], 4), round(per[(9 * len(per)) // 10], 4)],
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "ms_per_step_with_kernel_events": round(statistics.median(per_prof), 4),
         "peak_bytes": {"workspace": ws_bytes, "handle_device_bytes": 256, "max_allocated_beyond_io": int(peak_extra),
                        "inputs_outputs": int(io_alloc - base_alloc),
                        "full_bf16_logits_not_allocated": BT * V * 2},
@@ -328,8 +359,13 @@ def main():
                      "flops_per_launch": flops_per_launch},
     }
     if not args.no_cpu_baseline:
-        print(f"# timing the oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, X, W, y, args.cpu_rows, fwd_only)
+        rows = cpu_rows_for(BT, H, V, fwd_only, args.cpu_rows)
+        Xc, yc = X, y
+        if nseq:  # the call's rows: every position but the last of each sequence, scored against the next label
+            Xc = X.reshape(nseq, BT // nseq + 1, H)[:, :-1].reshape(BT, H)
+            yc = y.reshape(nseq, BT // nseq + 1)[:, 1:].reshape(BT)
+        print(f"# timing the oracle on {rows} rows", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, Xc, W, yc, rows, fwd_only)
     print(json.dumps(out), flush=True)
 
 

@@ -189,8 +189,12 @@ typedef struct {
   int64_t label_stride[2];       /* elements from (b, t) to (b+1, t) and to (b, t+1) of labels */
 } flce_rows;
 
-/* Flags of flce_forward_backward_rows. */
-enum { FLCE_ACCUMULATE_GRAD_HIDDEN = 1, FLCE_ACCUMULATE_GRAD_W = 2 };
+/* Flags of flce_forward_backward_rows. FLCE_NO_GRAD_HIDDEN / FLCE_NO_GRAD_W leave one gradient out
+ * (a frozen input or a frozen LM-head weight, e.g. the frozen base weights of the QLoRA recipe in the
+ * torchtune issue #1228 discussion): its GEMM is not run and its pointer may be NULL. Setting both
+ * is FLCE_ERR_INVALID_ARG (use flce_forward_rows), and so is accumulating into a gradient that is
+ * left out. */
+enum { FLCE_ACCUMULATE_GRAD_HIDDEN = 1, FLCE_ACCUMULATE_GRAD_W = 2, FLCE_NO_GRAD_HIDDEN = 4, FLCE_NO_GRAD_W = 8 };
 
 /* Bytes of device workspace flce_forward_backward_rows needs (host-only arithmetic; h may be NULL).
  * Equal to flce_workspace_size for BT = B * (T - shift) when the hidden rows lie in the plain
@@ -204,7 +208,9 @@ int flce_workspace_size_rows(flce_handle h, const flce_rows* rows, int64_t H, in
  *                loss, e.g. 1 / gradient-accumulation steps as in the training loop of the
  *                torchtune issue #1228 discussion; finite, else FLCE_ERR_INVALID_ARG
  *   flags        FLCE_ACCUMULATE_GRAD_HIDDEN: grad_hidden rows get += instead of =
- *                FLCE_ACCUMULATE_GRAD_W: grad_W gets += instead of =; other bits FLCE_ERR_INVALID_ARG
+ *                FLCE_ACCUMULATE_GRAD_W: grad_W gets += instead of =
+ *                FLCE_NO_GRAD_HIDDEN / FLCE_NO_GRAD_W: that gradient is not computed (NULL allowed)
+ *                other bits FLCE_ERR_INVALID_ARG
  *   grad_hidden  device, B x T rows at grad_hidden_stride (written): the rows of the call get their
  *                gradient; with shift = 1 the last position of each sequence gets 0 (or is left as it
  *                is with FLCE_ACCUMULATE_GRAD_HIDDEN)
@@ -240,7 +246,8 @@ int flce_status(flce_handle h, void* stream);
  * flce_profile_begin, never inside flce_forward_backward. Returns FLCE_OK, FLCE_ERR_INVALID_ARG or
  * FLCE_ERR_HIP. */
 enum { FLCE_K_PREPASS = 0, FLCE_K_FWD = 1, FLCE_K_MERGE = 2, FLCE_K_DX = 3, FLCE_K_DX_REDUCE = 4,
-       FLCE_K_DW = 5, FLCE_K_FINALIZE = 6, FLCE_K_TRANSPOSE = 7, FLCE_K_ROWS = 8, FLCE_K_COUNT = 9 };
+       FLCE_K_DW = 5, FLCE_K_FINALIZE = 6, FLCE_K_TRANSPOSE = 7, FLCE_K_ROWS = 8, FLCE_K_ZERO = 9,
+       FLCE_K_COUNT = 10 };
 int flce_profile_begin(flce_handle h, int max_launches);
 int flce_profile_end(flce_handle h, void* stream, double* ms_out, int64_t* count_out);
 

@@ -330,23 +330,30 @@ Call make_call(flce_ctx* h, const Layout& L, const Rows& R, int64_t H, int64_t V
   } while (0)
 
 // The fused forward + backward over the rows R (sizes already checked).
-int run_fused(flce_ctx* h, const void* hidden, const void* W, const int64_t* labels, const Rows& R, int64_t H,
-              int64_t V, int dtype, int64_t ignore_index, float softcap, int reduction, float grad_scale,
+// cmax: the chunk cap (0 = the handle's).
+int run_fused(flce_ctx* h, int64_t cmax, const void* hidden, const void* W, const int64_t* labels, const Rows& R,
+              int64_t H, int64_t V, int dtype, int64_t ignore_index, float softcap, int reduction, float grad_scale,
               int flags, float* loss, void* grad_hidden, float* grad_W, void* workspace, size_t workspace_bytes,
               void* stream_ptr) {
   const int64_t BT = R.BT;
   if (reduction == FLCE_NONE) return FLCE_ERR_UNSUPPORTED;
   if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARG;
   if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_INVALID_ARG;
-  if (!W || !loss || !grad_W || !workspace) return FLCE_ERR_INVALID_ARG;
+  // one of the two gradients may be left out (a frozen weight or a frozen input); not both
+  const bool need_gh = (flags & FLCE_NO_GRAD_HIDDEN) == 0, need_gw = (flags & FLCE_NO_GRAD_W) == 0;
+  if (!need_gh && !need_gw) return FLCE_ERR_INVALID_ARG;
+  if ((!need_gh && (flags & FLCE_ACCUMULATE_GRAD_HIDDEN)) || (!need_gw && (flags & FLCE_ACCUMULATE_GRAD_W)))
+    return FLCE_ERR_INVALID_ARG;
+  if (!W || !loss || (need_gw && !grad_W) || !workspace) return FLCE_ERR_INVALID_ARG;
   // grad_hidden is written on every row of the call and on the skipped last positions
-  const bool gh_rows = BT > 0 || (R.shift == 1 && R.B > 0 && R.T > 0);
+  const bool gh_rows = need_gh && (BT > 0 || (R.shift == 1 && R.B > 0 && R.T > 0));
   if ((BT > 0 && (!hidden || !labels)) || (gh_rows && !grad_hidden)) return FLCE_ERR_INVALID_ARG;
-  if (!aligned(W, 16) || !aligned(loss, 4) || !aligned(grad_W, 16) || !aligned(workspace, 256))
+  if (!aligned(W, 16) || !aligned(loss, 4) || (need_gw && !aligned(grad_W, 16)) || !aligned(workspace, 256))
     return FLCE_ERR_INVALID_ARG;
   if (BT > 0 && (!aligned(hidden, 16) || !aligned(labels, 8))) return FLCE_ERR_INVALID_ARG;
   if (gh_rows && !aligned(grad_hidden, 16)) return FLCE_ERR_INVALID_ARG;
-  const Layout L = layout(BT, H, V, dtype, h->chunk_rows_max, h->ncu, true, !R.dense);
+  if (cmax <= 0) cmax = h->chunk_rows_max;  // 0: the handle's chunk cap
+  const Layout L = layout(BT, H, V, dtype, cmax, h->ncu, true, !R.dense);
   if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
 
   DeviceGuard g(h->device);
@@ -359,27 +366,30 @@ int run_fused(flce_ctx* h, const void* hidden, const void* W, const int64_t* lab
 
   FLCE_LAUNCH(FLCE_K_PREPASS, flce::launch_prepass(p, labels, w, h->d_status, stream));
   // the last position of each sequence is no row when labels are shifted: its gradient is zero
-  if (R.shift == 1 && R.T > 0 && !p.acc_gh)
-    FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_zero_rows(p, grad_hidden, R.B, (R.T - 1) * R.gmap.st, stream));
+  if (need_gh && R.shift == 1 && R.T > 0 && !p.acc_gh)
+    FLCE_LAUNCH(FLCE_K_ZERO, flce::launch_zero_rows(p, grad_hidden, R.B, (R.T - 1) * R.gmap.st, stream));
   if (BT == 0) {
-    if (!p.acc_gw) FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_zero_f32(grad_W, V * H, stream));
+    if (need_gw && !p.acc_gw) FLCE_LAUNCH(FLCE_K_ZERO, flce::launch_zero_f32(grad_W, V * H, stream));
     FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
     return FLCE_OK;
   }
   int64_t n_chunks, crows;
-  plan(BT, h->chunk_rows_max, &n_chunks, &crows);
+  plan(BT, cmax, &n_chunks, &crows);
   for (int64_t ci = 0; ci < n_chunks; ++ci) {
     const int64_t row0 = ci * crows;
     const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
     FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
     FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, true, stream));
     FLCE_LAUNCH(FLCE_K_MERGE, flce::launch_merge(p, w, row0, rows, stream));
-    int splits = L.splits > 1 ? dx_splits(rows, H, p.V_pad, dtype, h->ncu) : 1;
-    if (splits > L.splits) splits = L.splits;
-    FLCE_LAUNCH(FLCE_K_DX, flce::launch_dx(p, W, w, grad_hidden, row0, rows, splits, stream));
-    if (splits > 1)
-      FLCE_LAUNCH(FLCE_K_DX_REDUCE, flce::launch_dx_reduce(p, w, grad_hidden, row0, rows, splits, stream));
-    FLCE_LAUNCH(FLCE_K_DW, flce::launch_dw(p, hidden, w, grad_W, row0, rows, ci > 0 || p.acc_gw, stream));
+    if (need_gh) {
+      int splits = L.splits > 1 ? dx_splits(rows, H, p.V_pad, dtype, h->ncu) : 1;
+      if (splits > L.splits) splits = L.splits;
+      FLCE_LAUNCH(FLCE_K_DX, flce::launch_dx(p, W, w, grad_hidden, row0, rows, splits, stream));
+      if (splits > 1)
+        FLCE_LAUNCH(FLCE_K_DX_REDUCE, flce::launch_dx_reduce(p, w, grad_hidden, row0, rows, splits, stream));
+    }
+    if (need_gw)
+      FLCE_LAUNCH(FLCE_K_DW, flce::launch_dw(p, hidden, w, grad_W, row0, rows, ci > 0 || p.acc_gw, stream));
   }
   FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
   return FLCE_OK;
@@ -420,7 +430,7 @@ int run_recompute(flce_ctx* h, const void* hidden, const void* W, const int64_t*
 
   FLCE_LAUNCH(FLCE_K_PREPASS, flce::launch_prepass(p, labels, w, h->d_status, stream));
   if (BT == 0) {
-    FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_zero_f32(grad_W, V * H, stream));
+    FLCE_LAUNCH(FLCE_K_ZERO, flce::launch_zero_f32(grad_W, V * H, stream));
     FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
     return FLCE_OK;
   }
@@ -558,7 +568,7 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
   if (!h) return FLCE_ERR_INVALID_ARG;
   const int rc = check_sizes(BT, H, V, dtype);
   if (rc != FLCE_OK) return rc;
-  return run_fused(h, hidden, W, labels, plain_rows(BT, H), H, V, dtype, ignore_index, softcap, reduction, 1.0f,
+  return run_fused(h, 0, hidden, W, labels, plain_rows(BT, H), H, V, dtype, ignore_index, softcap, reduction, 1.0f,
                    0, loss, grad_hidden, grad_W, workspace, workspace_bytes, stream_ptr);
 }
 
@@ -584,9 +594,10 @@ int flce_forward_backward_rows(flce_handle h, const void* hidden, const void* W,
   if (rc == FLCE_OK) rc = check_sizes(R.BT, H, V, dtype);
   if (rc != FLCE_OK) return rc;
   if (!std::isfinite(grad_scale)) return FLCE_ERR_INVALID_ARG;
-  if (flags & ~(FLCE_ACCUMULATE_GRAD_HIDDEN | FLCE_ACCUMULATE_GRAD_W)) return FLCE_ERR_INVALID_ARG;
-  return run_fused(h, hidden, W, labels, R, H, V, dtype, ignore_index, softcap, reduction, grad_scale, flags, loss,
-                   grad_hidden, grad_W, workspace, workspace_bytes, stream_ptr);
+  if (flags & ~(FLCE_ACCUMULATE_GRAD_HIDDEN | FLCE_ACCUMULATE_GRAD_W | FLCE_NO_GRAD_HIDDEN | FLCE_NO_GRAD_W))
+    return FLCE_ERR_INVALID_ARG;
+  return run_fused(h, 0, hidden, W, labels, R, H, V, dtype, ignore_index, softcap, reduction, grad_scale, flags,
+                   loss, grad_hidden, grad_W, workspace, workspace_bytes, stream_ptr);
 }
 
 int flce_recompute_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, int64_t v_slice,

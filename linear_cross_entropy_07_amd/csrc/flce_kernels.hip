@@ -11,7 +11,8 @@
 //             q = exp(s - segment max) * (softcap derivative). No [BT, V] tensor exists.
 //   k_merge_dlogits  per row: lse from the segment statistics and the loss term; then one sweep
 //             over the row rebuilds the softmax from q and turns it into dZ in place, in the operand
-//             type of the backward GEMMs. No separate softmax or dlogits tensor exists.
+//             type of the backward GEMMs: the chunk's dZ exists in HBM (in the q buffer) until the
+//             backward GEMMs have read it.
 //   k_dx      grad_hidden chunk = dZ . W on MFMA (W read MN-contiguous, transposed by the LDS
 //             transpose reads on its way to the matrix cores).
 //   k_dw      grad_W (+)= dZ^T . X on MFMA; both operands read MN-contiguous and transposed the same
@@ -149,7 +150,7 @@ __device__ __forceinline__ u32 lds_addr(const void* p) {
 __device__ __forceinline__ void dma16(i32x4 desc, u32 voff, u32 lds) {
   // M0 must be written one instruction before an LDS-DMA load reads it.
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(voff), "s"(desc), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+               :: "v"(voff), "s"(desc), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 
 // Range-checked buffer accesses for epilogues: loads outside the range return 0, stores outside it

@@ -47,7 +47,7 @@ class Rows(ctypes.Structure):
                 ("label_stride", ctypes.c_int64 * 2)]
 
 
-FLCE_ACCUMULATE_GRAD_HIDDEN, FLCE_ACCUMULATE_GRAD_W = 1, 2
+FLCE_ACCUMULATE_GRAD_HIDDEN, FLCE_ACCUMULATE_GRAD_W, FLCE_NO_GRAD_HIDDEN, FLCE_NO_GRAD_W = 1, 2, 4, 8
 
 
 _LIB = None
@@ -178,6 +178,20 @@ class FLCE:
     def chunk_plan(self, BT):
         return chunk_plan(BT, self._h)
 
+    def _stream(self, stream, tensors):
+        """The stream a call enqueues on. Another stream than the current one first waits for the
+        current stream (which produced the inputs and the tensors allocated for the call), and every
+        tensor of the call, the cached workspace included, is marked as used on it, so that torch's
+        caching allocator does not hand that memory out again while the stream may still use it."""
+        cur = torch.cuda.current_stream(self.device)
+        if stream is None or stream == cur:
+            return cur
+        stream.wait_stream(cur)
+        for t in tensors:
+            if t is not None:
+                t.record_stream(stream)
+        return stream
+
     def workspace(self, nbytes: int) -> torch.Tensor:
         """A cached uint8 device buffer of at least nbytes (grown when too small)."""
         if self._ws is None or self._ws.numel() < nbytes:
@@ -206,29 +220,46 @@ class FLCE:
 
     def forward_backward(self, hidden: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
                          ignore_index: int = -100, softcap: float = 0.0, reduction: str = "mean",
-                         out=None, workspace: torch.Tensor | None = None, stream=None):
-        """Run the fused forward + backward; returns (loss [0-dim fp32], grad_hidden, grad_W fp32)."""
+                         out=None, workspace: torch.Tensor | None = None, stream=None,
+                         grad_hidden: bool = True, grad_W: bool = True):
+        """Run the fused forward + backward; returns (loss [0-dim fp32], grad_hidden, grad_W fp32).
+        With grad_hidden=False or grad_W=False that gradient is not computed (its GEMM does not run)
+        and None is returned in its place."""
         BT, H, V = self._check_inputs(hidden, W, labels)
         if reduction not in _REDUCTIONS:
             raise ValueError("reduction must be 'mean' or 'sum'")
+        if not (grad_hidden or grad_W):
+            raise ValueError("no gradient asked for: use forward()")
         dt = _DTYPES[hidden.dtype]
         need = self.workspace_size(BT, H, V, hidden.dtype)
         if workspace is None:
             workspace = self.workspace(need)
         if out is None:
             loss = torch.empty((), dtype=torch.float32, device=self.device)
-            gh = torch.empty_like(hidden)
-            gw = torch.empty((V, H), dtype=torch.float32, device=self.device)
+            gh = torch.empty_like(hidden) if grad_hidden else None
+            gw = torch.empty((V, H), dtype=torch.float32, device=self.device) if grad_W else None
         else:
             loss, gh, gw = out
-        if stream is None:
-            stream = torch.cuda.current_stream(self.device)
-        rc = lib().flce_forward_backward(
-            self._h, hidden.data_ptr(), W.data_ptr(), labels.data_ptr(), BT, H, V, dt,
-            int(ignore_index), float(softcap), _REDUCTIONS[reduction], loss.data_ptr(),
-            gh.data_ptr(), gw.data_ptr(), workspace.data_ptr(), workspace.numel(),
-            ctypes.c_void_p(stream.cuda_stream))
-        _check(rc, "flce_forward_backward")
+            gh, gw = (gh if grad_hidden else None), (gw if grad_W else None)
+        stream = self._stream(stream, (hidden, W, labels, loss, gh, gw, workspace))
+        ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        if grad_hidden and grad_W:
+            rc = lib().flce_forward_backward(
+                self._h, hidden.data_ptr(), W.data_ptr(), labels.data_ptr(), BT, H, V, dt,
+                int(ignore_index), float(softcap), _REDUCTIONS[reduction], loss.data_ptr(),
+                gh.data_ptr(), gw.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                ctypes.c_void_p(stream.cuda_stream))
+            _check(rc, "flce_forward_backward")
+        else:
+            # the plain [BT, H] layout as one sequence of BT positions, with one gradient left out
+            rows = Rows(1, BT, 0, (ctypes.c_int64 * 2)(0, H), (ctypes.c_int64 * 2)(0, H),
+                        (ctypes.c_int64 * 2)(0, 1))
+            flags = (0 if grad_hidden else FLCE_NO_GRAD_HIDDEN) | (0 if grad_W else FLCE_NO_GRAD_W)
+            rc = lib().flce_forward_backward_rows(
+                self._h, hidden.data_ptr(), W.data_ptr(), labels.data_ptr(), ctypes.byref(rows), H, V, dt,
+                int(ignore_index), float(softcap), _REDUCTIONS[reduction], 1.0, flags, loss.data_ptr(),
+                ptr(gh), ptr(gw), workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+            _check(rc, "flce_forward_backward_rows")
         return loss, gh, gw
 
     def forward_backward_recompute(self, hidden: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
@@ -248,8 +279,7 @@ class FLCE:
             gw = torch.empty((V, H), dtype=torch.float32, device=self.device)
         else:
             loss, gh, gw = out
-        if stream is None:
-            stream = torch.cuda.current_stream(self.device)
+        stream = self._stream(stream, (hidden, W, labels, loss, gh, gw, workspace))
         rc = lib().flce_forward_backward_recompute(
             self._h, hidden.data_ptr(), W.data_ptr(), labels.data_ptr(), BT, H, V, _DTYPES[hidden.dtype],
             int(ignore_index), float(softcap), _REDUCTIONS[reduction], int(v_slice), loss.data_ptr(),
@@ -272,8 +302,7 @@ class FLCE:
         loss = torch.empty((), dtype=torch.float32, device=self.device) if reduction != "none" else None
         rows = torch.empty(BT, dtype=torch.float32, device=self.device) if reduction == "none" else None
         lse = torch.empty(BT, dtype=torch.float32, device=self.device) if return_lse else None
-        if stream is None:
-            stream = torch.cuda.current_stream(self.device)
+        stream = self._stream(stream, (hidden, W, labels, loss, rows, lse, workspace))
         ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
         rc = lib().flce_forward(
             self._h, hidden.data_ptr(), W.data_ptr(), labels.data_ptr(), BT, H, V, dt, int(ignore_index),
@@ -316,37 +345,49 @@ class FLCE:
                              grad_scale: float = 1.0, grad_hidden: torch.Tensor | None = None,
                              grad_W: torch.Tensor | None = None, accumulate_grad_hidden: bool = False,
                              accumulate_grad_W: bool = False, loss: torch.Tensor | None = None,
-                             workspace: torch.Tensor | None = None, stream=None):
+                             workspace: torch.Tensor | None = None, stream=None, need_grad_hidden: bool = True,
+                             need_grad_W: bool = True):
         """Fused forward + backward over a batch of sequences hidden [B,T,H] (any strides with H
         contiguous) and labels [B,T]; with shift, position t is scored against label t+1 and the
         last position gets no gradient of its own. Gradients are multiplied by grad_scale and
         written into (or, with the accumulate flags, added to) grad_hidden [B,T,H] and grad_W
-        [V,H] fp32, allocated when not given. Returns (loss, grad_hidden, grad_W)."""
+        [V,H] fp32, allocated when not given. need_grad_hidden=False / need_grad_W=False leave that
+        gradient out (its GEMM does not run; None is returned for it). Returns (loss, grad_hidden,
+        grad_W)."""
         if reduction not in _REDUCTIONS:
             raise ValueError("reduction must be 'mean' or 'sum'")
+        if not (need_grad_hidden or need_grad_W):
+            raise ValueError("no gradient asked for: use forward_seq()")
         if accumulate_grad_hidden and grad_hidden is None or accumulate_grad_W and grad_W is None:
             raise ValueError("accumulating needs the gradient tensor to add to")
-        if grad_hidden is None:
+        if (accumulate_grad_hidden and not need_grad_hidden) or (accumulate_grad_W and not need_grad_W):
+            raise ValueError("cannot accumulate into a gradient that is left out")
+        if not need_grad_hidden:
+            grad_hidden = None
+        elif grad_hidden is None:
             grad_hidden = torch.empty(hidden.shape, dtype=hidden.dtype, device=self.device)
         rows, B, T, H, V = self._seq_rows(hidden, W, labels, shift, grad_hidden)
-        if grad_W is None:
+        if not need_grad_W:
+            grad_W = None
+        elif grad_W is None:
             grad_W = torch.empty((V, H), dtype=torch.float32, device=self.device)
-        if tuple(grad_W.shape) != (V, H) or grad_W.dtype != torch.float32 or not grad_W.is_contiguous() \
-                or grad_W.device != self.device:
+        if grad_W is not None and (tuple(grad_W.shape) != (V, H) or grad_W.dtype != torch.float32
+                                   or not grad_W.is_contiguous() or grad_W.device != self.device):
             raise ValueError("grad_W must be a contiguous [V,H] float32 tensor on the handle's device")
         if loss is None:
             loss = torch.empty((), dtype=torch.float32, device=self.device)
         flags = (FLCE_ACCUMULATE_GRAD_HIDDEN if accumulate_grad_hidden else 0) | \
-                (FLCE_ACCUMULATE_GRAD_W if accumulate_grad_W else 0)
+                (FLCE_ACCUMULATE_GRAD_W if accumulate_grad_W else 0) | \
+                (0 if need_grad_hidden else FLCE_NO_GRAD_HIDDEN) | (0 if need_grad_W else FLCE_NO_GRAD_W)
         need = workspace_size_rows(rows, H, V, hidden.dtype, self._h)
         if workspace is None:
             workspace = self.workspace(need)
-        if stream is None:
-            stream = torch.cuda.current_stream(self.device)
+        stream = self._stream(stream, (hidden, W, labels, loss, grad_hidden, grad_W, workspace))
+        ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
         rc = lib().flce_forward_backward_rows(
             self._h, hidden.data_ptr(), W.data_ptr(), labels.data_ptr(), ctypes.byref(rows), H, V,
             _DTYPES[hidden.dtype], int(ignore_index), float(softcap), _REDUCTIONS[reduction], float(grad_scale),
-            flags, loss.data_ptr(), grad_hidden.data_ptr(), grad_W.data_ptr(), workspace.data_ptr(),
+            flags, loss.data_ptr(), ptr(grad_hidden), ptr(grad_W), workspace.data_ptr(),
             workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
         _check(rc, "flce_forward_backward_rows")
         return loss, grad_hidden, grad_W
@@ -366,8 +407,7 @@ class FLCE:
         loss = torch.empty((), dtype=torch.float32, device=self.device) if reduction != "none" else None
         per = torch.empty((B, P), dtype=torch.float32, device=self.device) if reduction == "none" else None
         lse = torch.empty((B, P), dtype=torch.float32, device=self.device) if return_lse else None
-        if stream is None:
-            stream = torch.cuda.current_stream(self.device)
+        stream = self._stream(stream, (hidden, W, labels, loss, per, lse, workspace))
         ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
         rc = lib().flce_forward_rows(
             self._h, hidden.data_ptr(), W.data_ptr(), labels.data_ptr(), ctypes.byref(rows), H, V,
@@ -377,7 +417,7 @@ class FLCE:
         out = loss if reduction != "none" else per
         return (out, lse) if return_lse else out
 
-    KERNELS = ("prepass", "fwd", "merge", "dx", "dx_reduce", "dw", "finalize", "transpose", "rows")
+    KERNELS = ("prepass", "fwd", "merge", "dx", "dx_reduce", "dw", "finalize", "transpose", "rows", "zero")
 
     def profile_begin(self, max_launches: int = 4096):
         """Bracket every following kernel launch with HIP events on its stream (diagnostics)."""
@@ -414,13 +454,19 @@ def engine(device=None) -> FLCE:
 
 
 class _FLCEFunction(torch.autograd.Function):
+    """The loss with its gradients computed in the same fused call: only the gradients autograd will
+    ask for are computed and kept (hidden's, W's or both)."""
+
     @staticmethod
     def forward(ctx, hidden, W, labels, ignore_index, softcap, reduction, shift):
         e = engine(hidden.device)
+        need_gh, need_gw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         if hidden.dim() == 3:
-            loss, gh, gw = e.forward_backward_seq(hidden, W, labels, shift, ignore_index, softcap, reduction)
+            loss, gh, gw = e.forward_backward_seq(hidden, W, labels, shift, ignore_index, softcap, reduction,
+                                                  need_grad_hidden=need_gh, need_grad_W=need_gw)
         else:
-            loss, gh, gw = e.forward_backward(hidden, W, labels, ignore_index, softcap, reduction)
+            loss, gh, gw = e.forward_backward(hidden, W, labels, ignore_index, softcap, reduction,
+                                              grad_hidden=need_gh, grad_W=need_gw)
         ctx.save_for_backward(gh, gw)
         ctx.w_dtype = W.dtype
         return loss
@@ -428,7 +474,9 @@ class _FLCEFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_out):
         gh, gw = ctx.saved_tensors
-        return gh * grad_out.to(gh.dtype), (gw * grad_out).to(ctx.w_dtype), None, None, None, None, None
+        dh = gh * grad_out.to(gh.dtype) if gh is not None else None
+        dw = (gw * grad_out).to(ctx.w_dtype) if gw is not None else None
+        return dh, dw, None, None, None, None, None
 
 
 def flce_loss(hidden, W, labels, ignore_index: int = -100, softcap: float = 0.0, reduction: str = "mean",
@@ -441,4 +489,10 @@ def flce_loss(hidden, W, labels, ignore_index: int = -100, softcap: float = 0.0,
     by the upstream gradient in backward (e.g. a gradient-accumulation divisor)."""
     if shift and hidden.dim() != 3:
         raise ValueError("shift needs hidden [B, T, H] and labels [B, T]")
+    if not (torch.is_grad_enabled() and (hidden.requires_grad or W.requires_grad)):
+        # no gradient will be asked for (evaluation, torch.no_grad): the forward alone, one GEMM
+        e = engine(hidden.device)
+        if hidden.dim() == 3:
+            return e.forward_seq(hidden, W, labels, shift, ignore_index, softcap, reduction)
+        return e.forward(hidden, W, labels, ignore_index, softcap, reduction)
     return _FLCEFunction.apply(hidden, W, labels, ignore_index, softcap, reduction, bool(shift))

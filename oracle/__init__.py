@@ -14,5 +14,6 @@ from .flce_oracle import (  # noqa: F401
     flce_forward,
     flce_rows,
     flce_vocab_rows,
+    flce_blocked,
     flce_sequences,
 )

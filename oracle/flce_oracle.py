@@ -39,9 +39,9 @@ Readings taken where the pages are silent (the same list is kept with the design
     float64 and every step stays in float64.
 
 There is no online softmax, chunking or fusion here: rows are independent, and
-each row's whole logits vector is built. All functions but flce_vocab_rows build
-the [BT, V] logits matrix of the rows asked for at once; flce_vocab_rows, which
-must cover every row of a full-size call, builds it in blocks of rows.
+each row's whole logits vector is built. Most functions build the [BT, V] logits
+matrix of the rows asked for at once; flce_vocab_rows and flce_blocked, which
+must cover every row of a full-size call, build it in blocks of rows.
 """
 from __future__ import annotations
 
@@ -55,6 +55,7 @@ __all__ = [
     "flce_forward_backward",
     "flce_rows",
     "flce_vocab_rows",
+    "flce_blocked",
     "flce_sequences",
 ]
 
@@ -264,6 +265,50 @@ def flce_vocab_rows(X, W, y, vrows, ignore_index: int = -100, softcap: float = 0
         dW += d
     lse = np.concatenate([l for l, _ in parts]) if parts else np.zeros(0)
     return dict(dW=dW, lse=lse, N=N)
+
+
+def _row_blocks(n: int, block_rows: int):
+    """Consecutive row ranges [b0, b1) that cover rows 0 .. n-1 once, block_rows rows each (the last
+    one shorter when block_rows does not divide n)."""
+    return [(b0, min(b0 + block_rows, n)) for b0 in range(0, n, block_rows)]
+
+
+def flce_blocked(X, W, y, ignore_index: int = -100, softcap: float = 0.0, reduction: str = "mean",
+                 block_rows: int = 1024):
+    """flce_forward_backward for a call of any size, with host memory bounded by a block of rows.
+
+    Rows of the method are independent except for the mean's divisor N, so N is counted over the
+    whole call first; then each block of block_rows rows goes through exactly the per-row steps of
+    flce_forward_backward (its whole float64 logits rows built, the two-pass max and sum, the loss
+    terms, dZ) and contributes dX_b = dZ_b W and dZ_b^T X_b, the latter summed into dW in block
+    order. The loss is the sum of all rows' terms (in row order) over N, or that sum.
+    Returns (loss, dX [BT, H] f64, dW [V, H] f64, dict(lse [BT], loss_rows [BT], N)).
+    """
+    Xf = _f64(X)
+    Wf = _f64(W)
+    yl = _labels(y)
+    _check(Xf, Wf, yl, softcap, reduction)
+    if block_rows <= 0:
+        raise ValueError("block_rows must be positive")
+    BT, H = Xf.shape
+    V = Wf.shape[0]
+    N = int(valid_mask(yl, V, ignore_index).sum())
+    dX = np.zeros((BT, H))
+    dW = np.zeros((V, H))
+    lse = np.zeros(BT)
+    loss_rows = np.zeros(BT)
+    for b0, b1 in _row_blocks(BT, block_rows):
+        t = _row_terms(Xf[b0:b1], Wf, yl[b0:b1], ignore_index, softcap, reduction, N)
+        dX[b0:b1] = t["dZ"] @ Wf
+        dW += t["dZ"].T @ Xf[b0:b1]
+        lse[b0:b1] = t["lse"]
+        loss_rows[b0:b1] = t["loss_rows"]
+    total = float(loss_rows.sum())
+    if reduction == "mean":
+        loss = total / N if N > 0 else 0.0
+    else:
+        loss = total
+    return loss, dX, dW, dict(lse=lse, loss_rows=loss_rows, N=N)
 
 
 def flce_sequences(X3, W, Y2, shift: int = 1, ignore_index: int = -100, softcap: float = 0.0,

@@ -11,3 +11,5 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long CPU test")
+    config.addinivalue_line("markers", "fullsize: GPU test at a workload's full size with the CPU oracle on the "
+                                       "whole call (minutes of host time)")

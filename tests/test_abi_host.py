@@ -182,7 +182,7 @@ def test_rows_entry_points_reject_before_any_device_call():
     assert _fbr(fake, _rows(shift=3)) == -1
     assert _fbr(fake, _rows(), scale=float("nan")) == -1
     assert _fbr(fake, _rows(), scale=float("inf")) == -1
-    assert _fbr(fake, _rows(), flags=4) == -1
+    assert _fbr(fake, _rows(), flags=16) == -1       # an unknown flag bit
     assert _fbr(fake, _rows(), red=0) == -2
     assert _fbr(fake, _rows(), ptr=264) == -1
     p = ctypes.c_void_p(256)
@@ -266,3 +266,27 @@ def test_recompute_rejects_before_any_device_call():
     assert call(fake, vs=-5) == -1
     assert call(fake, softcap=float("nan")) == -1
     assert call(fake, ptr=ctypes.c_void_p(264)) == -1
+
+
+def _rows_call(h, flags, gh=256, gw=256):
+    r = flce.Rows(1, 4, 0, (ctypes.c_int64 * 2)(0, 64), (ctypes.c_int64 * 2)(0, 64), (ctypes.c_int64 * 2)(0, 1))
+    p = ctypes.c_void_p(256)
+    v = lambda a: ctypes.c_void_p(a) if a else NULL  # noqa: E731
+    return L.flce_forward_backward_rows(h, p, p, p, ctypes.byref(r), 64, 10, 0, -100, 0.0, 1, 1.0, flags, p,
+                                        v(gh), v(gw), p, 1 << 30, NULL)
+
+
+def test_gradient_flags_are_validated_before_any_device_call():
+    fake = ctypes.c_void_p(1)  # never dereferenced: argument checks come first
+    assert _rows_call(fake, flce.FLCE_NO_GRAD_HIDDEN | flce.FLCE_NO_GRAD_W) == -1   # use flce_forward_rows
+    assert _rows_call(fake, flce.FLCE_NO_GRAD_W | flce.FLCE_ACCUMULATE_GRAD_W) == -1
+    assert _rows_call(fake, flce.FLCE_NO_GRAD_HIDDEN | flce.FLCE_ACCUMULATE_GRAD_HIDDEN) == -1
+    assert _rows_call(fake, 16) == -1                                                # unknown bit
+    assert _rows_call(fake, 0, gw=0) == -1                                           # grad_W needed
+    assert _rows_call(fake, 0, gh=0) == -1                                           # grad_hidden needed
+
+
+def test_profile_kinds_match_the_header():
+    text = open(build_lib.INCLUDE + "/flce.h").read()
+    assert "FLCE_K_ZERO = 9" in text and "FLCE_K_COUNT = 10" in text
+    assert len(flce.FLCE.KERNELS) == 10 and flce.FLCE.KERNELS[9] == "zero"

@@ -492,3 +492,58 @@ def test_sequence_pin_catches_planted_mistakes(monkeypatch, mutation):
     tl, tdX, tdW = _torch_sequences(X3, W, Y2, 1, 0.0, "mean", scale, dX0, dW0)
     ok = abs(got[0] - tl) <= 1e-12 * abs(tl) and _rel(got[1], tdX) < 1e-12 and _rel(got[2], tdW) < 1e-12
     assert not ok
+
+
+# ---------------------------------------------------------------- the blocked full-size oracle
+@pytest.mark.parametrize("softcap", [0.0, 4.0])
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+@pytest.mark.parametrize("block_rows", [1, 5, 16, 37, 64])
+def test_blocked_matches_torch(softcap, reduction, block_rows):
+    """flce_blocked (row blocks, N over the whole call, dW summed over blocks) against the independent
+    PyTorch float64 implementation, with block sizes that leave a ragged last block (37 rows)."""
+    rng = np.random.default_rng(70 + block_rows)
+    X, W, y = _rand_case(rng, 37, 12, 23, ignore=5, w_scale=3.0)
+    tl, tdx, tdw = _torch_reference(X, W, y, softcap, reduction)
+    loss, dX, dW, d = oracle.flce_blocked(X, W, y, IGN, softcap, reduction, block_rows=block_rows)
+    assert abs(loss - tl) <= 1e-12 * abs(tl)
+    assert np.allclose(dX, tdx, rtol=0, atol=1e-13)
+    assert np.allclose(dW, tdw, rtol=0, atol=1e-13)
+    assert d["N"] == 32 and np.all(d["loss_rows"][y == IGN] == 0.0)
+    # per-row lse against torch's logsumexp of the (softcapped) logits
+    z = torch.tensor(X) @ torch.tensor(W).T
+    if softcap > 0:
+        z = softcap * torch.tanh(z / softcap)
+    assert np.allclose(d["lse"], torch.logsumexp(z, 1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_blocked_no_valid_rows_and_block_larger_than_call():
+    rng = np.random.default_rng(5)
+    X, W, y = _rand_case(rng, 9, 8, 7)
+    y[:] = IGN
+    loss, dX, dW, d = oracle.flce_blocked(X, W, y, IGN, block_rows=4)
+    assert loss == 0.0 and not dX.any() and not dW.any() and d["N"] == 0
+    X, W, y = _rand_case(rng, 9, 8, 7, ignore=2)
+    tl, tdx, tdw = _torch_reference(X, W, y, 0.0, "mean")
+    loss, dX, dW, _ = oracle.flce_blocked(X, W, y, IGN, block_rows=1000)
+    assert abs(loss - tl) <= 1e-12 * tl and np.allclose(dX, tdx, atol=1e-13) and np.allclose(dW, tdw, atol=1e-13)
+
+
+@pytest.mark.parametrize("mutation", ["drop_tail", "overlap", "per_block_N", "skip_first"])
+def test_blocked_pin_catches_planted_mistakes(monkeypatch, mutation):
+    """Mistakes at the block boundaries or in the cross-block divisor, planted in the oracle, must make
+    the pin against torch fail."""
+    if mutation == "drop_tail":      # the last, shorter block is never visited
+        monkeypatch.setattr(O, "_row_blocks", lambda n, b: [(i, i + b) for i in range(0, n - n % b, b)])
+    elif mutation == "overlap":      # blocks share a row: its dW contribution counts twice
+        monkeypatch.setattr(O, "_row_blocks", lambda n, b: [(i, min(i + b + 1, n)) for i in range(0, n, b)])
+    elif mutation == "skip_first":   # off by one at the start of every block
+        monkeypatch.setattr(O, "_row_blocks", lambda n, b: [(i + 1, min(i + b, n)) for i in range(0, n, b)])
+    else:                            # the mean's divisor counted per block instead of per call
+        orig = O._row_terms
+        monkeypatch.setattr(O, "_row_terms", lambda X, W, y, ig, c, r, n: orig(X, W, y, ig, c, r, None))
+    rng = np.random.default_rng(71)
+    X, W, y = _rand_case(rng, 37, 12, 23, ignore=5, w_scale=3.0)
+    tl, tdx, tdw = _torch_reference(X, W, y, 0.0, "mean")
+    loss, dX, dW, _ = oracle.flce_blocked(X, W, y, IGN, 0.0, "mean", block_rows=8)
+    ok = abs(loss - tl) <= 1e-12 * abs(tl) and np.allclose(dX, tdx, atol=1e-13) and np.allclose(dW, tdw, atol=1e-13)
+    assert not ok
