@@ -251,6 +251,29 @@ enum { FLCE_K_PREPASS = 0, FLCE_K_FWD = 1, FLCE_K_MERGE = 2, FLCE_K_DX = 3, FLCE
 int flce_profile_begin(flce_handle h, int max_launches);
 int flce_profile_end(flce_handle h, void* stream, double* ms_out, int64_t* count_out);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): flce_forward_backward with no workspace argument. The work runs
+ * in a static device array of FLCE_STATIC_SCRATCH_BYTES bytes that the library's code object carries:
+ * every device the library is loaded on holds one copy until the process ends; flce_create looks up
+ * its address on the handle's device. The call allocates nothing (no hipMalloc, no allocating
+ * library routine) and, like flce_forward_backward, never synchronises.
+ *   Arguments as for flce_forward_backward, without workspace and workspace_bytes.
+ *   Chunk plan: the largest chunk_rows_max' <= the handle's chunk_rows_max, a multiple of 256, for
+ *   which flce_workspace_size (with chunk_rows_max') fits FLCE_STATIC_SCRATCH_BYTES; the result is
+ *   bitwise that of flce_forward_backward on a handle configured with chunk_rows_max'.
+ *   Sizes whose workspace exceeds the scratch even with 256-row chunks (e.g. V above ~2^19, or a very
+ *   large BT) return FLCE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.
+ * Every call on a device shares that device's one array, and nothing in it needs to start at zero
+ * (each call writes every byte it reads): calls on one device that overlap in time (on different
+ * streams, or from different handles or threads without ordering between them) race and give wrong
+ * results. Order them, e.g. by issuing them on one stream. */
+#define FLCE_STATIC_SCRATCH_BYTES ((size_t)256 << 20)
+int flce_forward_backward_static(flce_handle h,
+                                 const void* hidden, const void* W, const int64_t* labels,
+                                 int64_t BT, int64_t H, int64_t V, int dtype,
+                                 int64_t ignore_index, float softcap, int reduction,
+                                 float* loss, void* grad_hidden, float* grad_W, void* stream);
+
 /* Static description of a return code. */
 const char* flce_error_string(int code);
 

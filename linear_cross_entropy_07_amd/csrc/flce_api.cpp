@@ -24,6 +24,7 @@ struct flce_ctx {
   int ncu;        // compute units of the device
   int64_t chunk_rows_max;
   int* d_status;  // device status word written by the label pre-pass
+  void* scratch;  // this device's copy of the library's static scratch (flce_forward_backward_static)
   // kernel timing (flce_profile_begin/end): event pairs recorded around each launch
   bool prof_on = false;
   std::vector<hipEvent_t> prof_events;
@@ -520,6 +521,9 @@ int flce_create(flce_handle* out, int device, const flce_config* cfg) {
   int ncu = 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || ncu <= 0)
     return FLCE_ERR_HIP;
+  // this device's copy of the static scratch, looked up once per device with the device current
+  void* scratch = nullptr;
+  if (flce::scratch_for_device(device, &scratch) != hipSuccess) return FLCE_ERR_HIP;
   int* st = nullptr;
   if (hipMalloc(&st, 256) != hipSuccess) return FLCE_ERR_HIP;
   if (hipMemset(st, 0, 256) != hipSuccess) {
@@ -531,6 +535,7 @@ int flce_create(flce_handle* out, int device, const flce_config* cfg) {
   h->ncu = ncu;
   h->chunk_rows_max = cmax;
   h->d_status = st;
+  h->scratch = scratch;
   *out = h;
   return FLCE_OK;
 }
@@ -570,6 +575,23 @@ int flce_forward_backward(flce_handle h, const void* hidden, const void* W, cons
   if (rc != FLCE_OK) return rc;
   return run_fused(h, 0, hidden, W, labels, plain_rows(BT, H), H, V, dtype, ignore_index, softcap, reduction, 1.0f,
                    0, loss, grad_hidden, grad_W, workspace, workspace_bytes, stream_ptr);
+}
+
+int flce_forward_backward_static(flce_handle h, const void* hidden, const void* W, const int64_t* labels,
+                                 int64_t BT, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                                 float softcap, int reduction, float* loss, void* grad_hidden, float* grad_W,
+                                 void* stream) {
+  if (!h) return FLCE_ERR_INVALID_ARG;
+  const int rc = check_sizes(BT, H, V, dtype);
+  if (rc != FLCE_OK) return rc;
+  if (!h->scratch) return FLCE_ERR_HIP;
+  // the largest chunk (a multiple of 256 rows, at most the handle's) whose workspace fits the scratch
+  int64_t cmax = h->chunk_rows_max;
+  while (cmax >= flce::kRowAlign && layout(BT, H, V, dtype, cmax, h->ncu).total > flce::kScratchBytes)
+    cmax -= flce::kRowAlign;
+  if (cmax < flce::kRowAlign) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  return run_fused(h, cmax, hidden, W, labels, plain_rows(BT, H), H, V, dtype, ignore_index, softcap, reduction,
+                   1.0f, 0, loss, grad_hidden, grad_W, h->scratch, flce::kScratchBytes, stream);
 }
 
 int flce_workspace_size_rows(flce_handle h, const flce_rows* rows, int64_t H, int64_t V, int dtype,
@@ -709,7 +731,9 @@ const char* flce_error_string(int code) {
     case FLCE_OK: return "ok";
     case FLCE_ERR_INVALID_ARG: return "invalid argument";
     case FLCE_ERR_UNSUPPORTED: return "unsupported problem (H must be a multiple of 8; size limits)";
-    case FLCE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than flce_workspace_size";
+    case FLCE_ERR_WORKSPACE_TOO_SMALL:
+      return "workspace smaller than flce_workspace_size (flce_forward_backward_static: the problem needs more "
+             "than the library's static scratch even in 256-row chunks)";
     case FLCE_ERR_HIP: return "HIP runtime error";
     case FLCE_ERR_LABEL_RANGE: return "a label is outside [0, V) and is not ignore_index";
     default: return "unknown error code";

@@ -103,4 +103,11 @@ hipError_t launch_dw(const Problem& p, const void* hidden, const Work& w, float*
 hipError_t launch_finalize(const Problem& p, const Work& w, float* loss, hipStream_t stream);
 hipError_t launch_zero_f32(float* ptr, int64_t n, hipStream_t stream);
 
+// Library-owned static device scratch (the allocation-free entry point's workspace): kScratchBytes
+// per device, held by the loaded code object until the process ends. scratch_for_device() must be
+// called with `device` current; it looks the array's address up once per device and returns it.
+constexpr size_t kScratchBytes = size_t(256) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t scratch_for_device(int device, void** out);
+
 }  // namespace flce

@@ -22,6 +22,8 @@
 // each wave a 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (or 32x32x2f32 for
 // fp32 inputs). Operands reach LDS by DMA (buffer loads that write LDS directly) into a ring of
 // kStages stages of kStepBytes of K per row, XOR-swizzled against bank conflicts.
+#include <mutex>
+
 #include "flce_internal.h"
 
 namespace flce {
@@ -1186,6 +1188,28 @@ __global__ __launch_bounds__(256) void k_zero_rows(T* p, int64_t B, int64_t sb, 
 }
 
 }  // namespace
+
+// ---- static scratch of the allocation-free entry point ---------------------------------------
+// A file-scope device array: every device the code object is loaded on holds its own copy at its
+// own address. Host code never passes the array's name to a kernel or a runtime call (in host code
+// it names a host-side stand-in); it uses the address the runtime reports for the current device.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+hipError_t scratch_for_device(int device, void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (!out || device < 0 || device >= kMaxDevices) return hipErrorInvalidValue;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *out = addr[device];
+  return hipSuccess;
+}
 
 // ---- launchers ------------------------------------------------------------------------------
 hipError_t launch_prepass(const Problem& p, const int64_t* labels, const Work& w, int* status_out,

@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
             L.flce_recompute_workspace_size.argtypes = [vp, i64, i64, i64, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
             L.flce_forward_backward_recompute.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, ctypes.c_float,
                                                           i32, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            L.flce_forward_backward_static.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, ctypes.c_float,
+                                                       i32, vp, vp, vp, vp]
             L.flce_status.argtypes = [vp, vp]
             L.flce_profile_begin.argtypes = [vp, i32]
             L.flce_profile_end.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
@@ -96,7 +98,7 @@ def lib() -> ctypes.CDLL:
                       "flce_forward_backward", "flce_forward_workspace_size", "flce_forward", "flce_status",
                       "flce_workspace_size_rows", "flce_forward_backward_rows", "flce_forward_rows",
                       "flce_recompute_workspace_size", "flce_forward_backward_recompute",
-                      "flce_profile_begin", "flce_profile_end"):
+                      "flce_profile_begin", "flce_profile_end", "flce_forward_backward_static"):
                 getattr(L, f).restype = i32
             _LIB = L
     return _LIB

@@ -286,6 +286,15 @@ def test_gradient_flags_are_validated_before_any_device_call():
     assert _rows_call(fake, 0, gh=0) == -1                                           # grad_hidden needed
 
 
+def test_static_entry_checks_before_touching_the_handle():
+    p = ctypes.c_void_p(256)
+    assert L.flce_forward_backward_static(NULL, p, p, p, 4, 64, 10, 0, -100, 0.0, 1, p, p, p, NULL) == -1
+    fake = ctypes.c_void_p(1)  # size checks come before the handle is read
+    assert L.flce_forward_backward_static(fake, p, p, p, 4, 60, 10, 0, -100, 0.0, 1, p, p, p, NULL) == -2
+    assert L.flce_forward_backward_static(fake, p, p, p, -1, 64, 10, 0, -100, 0.0, 1, p, p, p, NULL) == -1
+    assert L.flce_forward_backward_static(fake, p, p, p, 4, 64, 10, 7, -100, 0.0, 1, p, p, p, NULL) == -1
+
+
 def test_profile_kinds_match_the_header():
     text = open(build_lib.INCLUDE + "/flce.h").read()
     assert "FLCE_K_ZERO = 9" in text and "FLCE_K_COUNT = 10" in text
