@@ -1,7 +1,8 @@
 """Benchmark: fused linear + cross-entropy forward+backward on one MI355X.
 
 One step = one flce_forward_backward call over the whole batch (label pre-pass, label logits, and per
-BT chunk: logits GEMM + epilogue, row merge, grad_hidden GEMM, grad_W GEMM; then the loss), with
+BT chunk: row references, logits GEMM + epilogue, row statistics, per-row factors, grad_hidden GEMM,
+grad_W GEMM; then the loss), with
 inputs and outputs resident in HBM. Prints one JSON line.
 
 Workload (default): the Llama-3-8B LM head, BT=8192, H=4096, V=128256, bf16, RMS-normalised hidden,

@@ -18,8 +18,10 @@
  *   g = 1/N (mean) or 1 (sum) on valid rows, 0 on rows whose label is ignore_index.
  *
  * The softmax is never stored: as the PR #126348 description proposes, the backward rebuilds it from
- * the logits and the small per-row max/sum statistics. Logits exist only as a bounded 16-bit
- * [chunk_rows, V] workspace; no [BT, V] buffer is allocated by the library or required of the caller.
+ * the logits and the small per-row max/sum statistics. Per chunk of rows the workspace holds one
+ * 16-bit [chunk_rows, V] buffer of softmax numerators exp(s - c) (c a per-row reference); the backward
+ * GEMMs read it as it is and apply the per-row normalisation by linearity, so dlogits are never
+ * written. No [BT, V] buffer is allocated by the library or required of the caller.
  * B*T may be any value (ragged batches, as in the benchmark comment of Liger-Kernel issue #227): the
  * library splits the rows into balanced chunks of at most chunk_rows_max rows with one code object.
  *
@@ -84,10 +86,11 @@ int flce_create(flce_handle* out, int device, const flce_config* cfg);
 int flce_destroy(flce_handle h);
 
 /* Bytes of device workspace flce_forward_backward needs for this problem (host-only arithmetic, no
- * device call). h may be NULL (default configuration). The workspace holds one chunk of 16-bit
- * logits-derived values ([chunk_rows][V rounded up to 256], fp16 for FLCE_BF16, fp32 for
- * FLCE_FP32), per-(row, 128-wide V segment) statistics, per-row label data, split-K partials
- * of grad_hidden and one chunk of hidden transposed. It never grows with BT beyond O(BT) bytes of per-row data.
+ * device call). h may be NULL (default configuration). The workspace holds one chunk of
+ * logits-derived values ([chunk_rows][V rounded up to 256], bf16 for FLCE_BF16, fp32 for
+ * FLCE_FP32), per-(row, 128-wide V segment) statistics, per-row data, split-K partials of
+ * grad_hidden, and two [chunk_rows][H] copies of the chunk's hidden rows (transposed; scaled by the
+ * per-row factor of the backward). It never grows with BT beyond O(BT) bytes of per-row data.
  * Returns FLCE_OK and writes *bytes, or FLCE_ERR_INVALID_ARG. */
 int flce_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, size_t* bytes);
 
@@ -196,9 +199,8 @@ typedef struct {
  * left out. */
 enum { FLCE_ACCUMULATE_GRAD_HIDDEN = 1, FLCE_ACCUMULATE_GRAD_W = 2, FLCE_NO_GRAD_HIDDEN = 4, FLCE_NO_GRAD_W = 8 };
 
-/* Bytes of device workspace flce_forward_backward_rows needs (host-only arithmetic; h may be NULL).
- * Equal to flce_workspace_size for BT = B * (T - shift) when the hidden rows lie in the plain
- * [BT][H] layout; otherwise one chunk of gathered hidden rows ([chunk_rows][H] of dtype) more.
+/* Bytes of device workspace flce_forward_backward_rows needs (host-only arithmetic; h may be NULL):
+ * flce_workspace_size for BT = B * (T - shift), whatever the strides.
  * Returns FLCE_OK, FLCE_ERR_INVALID_ARG or FLCE_ERR_UNSUPPORTED. */
 int flce_workspace_size_rows(flce_handle h, const flce_rows* rows, int64_t H, int64_t V, int dtype,
                              size_t* bytes);
@@ -245,9 +247,9 @@ int flce_status(flce_handle h, void* stream);
  * (arrays of FLCE_K_COUNT entries, host memory), and releases the events. Events are created in
  * flce_profile_begin, never inside flce_forward_backward. Returns FLCE_OK, FLCE_ERR_INVALID_ARG or
  * FLCE_ERR_HIP. */
-enum { FLCE_K_PREPASS = 0, FLCE_K_FWD = 1, FLCE_K_MERGE = 2, FLCE_K_DX = 3, FLCE_K_DX_REDUCE = 4,
+enum { FLCE_K_PREPASS = 0, FLCE_K_FWD = 1, FLCE_K_LSE = 2, FLCE_K_DX = 3, FLCE_K_DX_REDUCE = 4,
        FLCE_K_DW = 5, FLCE_K_FINALIZE = 6, FLCE_K_TRANSPOSE = 7, FLCE_K_ROWS = 8, FLCE_K_ZERO = 9,
-       FLCE_K_COUNT = 10 };
+       FLCE_K_ROWREF = 10, FLCE_K_ROWFIX = 11, FLCE_K_COUNT = 12 };
 int flce_profile_begin(flce_handle h, int max_launches);
 int flce_profile_end(flce_handle h, void* stream, double* ms_out, int64_t* count_out);
 

@@ -81,17 +81,15 @@ int dx_splits(int64_t rows, int64_t H, int64_t V_pad, int dtype, int ncu) {
 }
 
 struct Layout {
-  size_t off_e, off_m, off_s, off_y, off_sl, off_og, off_loss, off_part, off_xt, off_xs, off_lse, off_params, total;
-  bool has_xs;  // the gathered-rows copy of hidden exists
+  size_t off_e, off_m, off_s, off_y, off_sl, off_loss, off_cref, off_lse, off_fs, off_part, off_xt, off_xf, off_params,
+      total;
   int splits;
   int64_t chunk_rows;
 };
 
-// Workspace carving. The forward-only path (backward = false) needs no q/dZ chunk and no split-K
-// partials; a gathered copy of the chunk's hidden rows (xstage) is needed only by the backward of
-// rows that are not in the plain [BT][H] layout.
-Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu, bool backward = true,
-              bool xstage = false) {
+// Workspace carving. The forward-only path (backward = false) needs no q chunk, no per-row references
+// or factors, no split-K partials and no scaled copy of the chunk's hidden rows.
+Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu, bool backward = true) {
   Layout L{};
   int64_t n, rows;
   plan(BT, cmax, &n, &rows);
@@ -112,13 +110,13 @@ Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu
   L.off_s = take((size_t)rows * nseg * 4);
   L.off_y = take((size_t)BT * 4);
   L.off_sl = take((size_t)BT * 4);
-  L.off_og = take((size_t)BT * 4);
   L.off_loss = take((size_t)BT * 4);
+  L.off_cref = take(backward ? (size_t)BT * 4 : 0);
+  L.off_lse = take(backward ? (size_t)BT * 4 : 0);
+  L.off_fs = take(backward ? (size_t)BT * 4 : 0);
   L.off_part = take(L.splits > 1 ? (size_t)L.splits * rows * H * 4 : 0);
   L.off_xt = take((size_t)rows * H * esz);
-  L.has_xs = backward && xstage;
-  L.off_xs = take(L.has_xs ? (size_t)rows * H * esz : 0);
-  L.off_lse = take(0);
+  L.off_xf = take(backward ? (size_t)rows * H * esz : 0);
   L.total = off;
   return L;
 }
@@ -134,10 +132,11 @@ int64_t vslice_of(int64_t vs, int64_t V) {
   return vs < vmax ? vs : vmax;
 }
 
-// Workspace of the recompute mode. Per chunk of C rows: q/dZ of one vocabulary slice
-// [C][slice], the statistics of the whole vocabulary [C][V_pad/128] (pass 1), the fp32 grad_hidden
-// accumulator [C][H] and hidden^T [H][C]; per row: labels, label logit, one-hot coefficient, loss
-// term and lse. No buffer spans the whole vocabulary for more than its 128-wide segment statistics.
+// Workspace of the recompute mode. Per chunk of C rows: q of one vocabulary slice [C][slice], the
+// statistics of the whole vocabulary [C][V_pad/128] (pass 1), the fp32 grad_hidden accumulator
+// [C][H], hidden^T [H][C] and f times the chunk's hidden rows [C][H]; per row: label, label logit,
+// loss term, reference, lse and f. No buffer spans the whole vocabulary for more than its 128-wide
+// segment statistics.
 Layout layout_recompute(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int64_t vs) {
   Layout L{};
   int64_t n, rows;
@@ -159,12 +158,13 @@ Layout layout_recompute(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cma
   L.off_s = take((size_t)rows * nseg * 4);
   L.off_y = take((size_t)BT * 4);
   L.off_sl = take((size_t)BT * 4);
-  L.off_og = take((size_t)BT * 4);
   L.off_loss = take((size_t)BT * 4);
+  L.off_cref = take((size_t)BT * 4);
   L.off_lse = take((size_t)BT * 4);
+  L.off_fs = take((size_t)BT * 4);
   L.off_part = take((size_t)rows * H * 4);
   L.off_xt = take((size_t)rows * H * esz);
-  L.off_xs = take(0);
+  L.off_xf = take((size_t)rows * H * esz);
   L.total = off;
   return L;
 }
@@ -182,7 +182,6 @@ int check_sizes(int64_t BT, int64_t H, int64_t V, int dtype) {
 struct Rows {
   int64_t B = 0, T = 0, shift = 0, BT = 0;
   flce::RowMap hmap{}, gmap{}, lmap{};
-  bool dense = true;  // hidden rows in the plain [BT][H] layout
 };
 
 // The plain layout: hidden and grad_hidden [BT][H], labels [BT].
@@ -241,8 +240,6 @@ int check_rows(const flce_rows* d, int64_t H, int dtype, bool grads, Rows* out) 
   r.hmap = flce::RowMap{d->hidden_stride[0], d->hidden_stride[1], 0, up};
   r.gmap = flce::RowMap{d->grad_hidden_stride[0], d->grad_hidden_stride[1], 0, up};
   r.lmap = flce::RowMap{d->label_stride[0], d->label_stride[1], d->shift * d->label_stride[1], up};
-  // plain [BT][H] rows: consecutive positions H apart, consecutive sequences per * H apart
-  r.dense = (per <= 1 || d->hidden_stride[1] == H) && (d->batch <= 1 || d->hidden_stride[0] == per * H);
   *out = r;
   return FLCE_OK;
 }
@@ -295,7 +292,6 @@ Call make_call(flce_ctx* h, const Layout& L, const Rows& R, int64_t H, int64_t V
   p.hmap = R.hmap;
   p.gmap = R.gmap;
   p.lmap = R.lmap;
-  p.hidden_dense = R.dense;
   p.grad_scale = grad_scale;
   p.acc_gh = (flags & FLCE_ACCUMULATE_GRAD_HIDDEN) != 0;
   p.acc_gw = (flags & FLCE_ACCUMULATE_GRAD_W) != 0;
@@ -315,12 +311,14 @@ Call make_call(flce_ctx* h, const Layout& L, const Rows& R, int64_t H, int64_t V
   w.seg_s = (float*)(base + L.off_s);
   w.y32 = (int*)(base + L.off_y);
   w.s_label = (float*)(base + L.off_sl);
-  w.og = (float*)(base + L.off_og);
   w.loss_row = (float*)(base + L.off_loss);
+  w.cref = (float*)(base + L.off_cref);
+  w.lse = (float*)(base + L.off_lse);
+  w.fscale = (float*)(base + L.off_fs);
   w.dx_part = L.splits > 1 ? (float*)(base + L.off_part) : nullptr;
   w.params = (flce::DevParams*)(base + L.off_params);
   w.xt = base + L.off_xt;
-  w.xs = L.has_xs ? base + L.off_xs : nullptr;
+  w.xf = base + L.off_xf;
   w.chunk_cap = L.chunk_rows;
   return c;
 }
@@ -354,7 +352,7 @@ int run_fused(flce_ctx* h, int64_t cmax, const void* hidden, const void* W, cons
   if (BT > 0 && (!aligned(hidden, 16) || !aligned(labels, 8))) return FLCE_ERR_INVALID_ARG;
   if (gh_rows && !aligned(grad_hidden, 16)) return FLCE_ERR_INVALID_ARG;
   if (cmax <= 0) cmax = h->chunk_rows_max;  // 0: the handle's chunk cap
-  const Layout L = layout(BT, H, V, dtype, cmax, h->ncu, true, !R.dense);
+  const Layout L = layout(BT, H, V, dtype, cmax, h->ncu, true);
   if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
 
   DeviceGuard g(h->device);
@@ -380,8 +378,10 @@ int run_fused(flce_ctx* h, int64_t cmax, const void* hidden, const void* W, cons
     const int64_t row0 = ci * crows;
     const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
     FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
+    FLCE_LAUNCH(FLCE_K_ROWREF, flce::launch_rowref(p, hidden, W, w, row0, rows, stream));
     FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, true, stream));
-    FLCE_LAUNCH(FLCE_K_MERGE, flce::launch_merge(p, w, row0, rows, stream));
+    FLCE_LAUNCH(FLCE_K_LSE, flce::launch_lse(p, w, row0, rows, true, stream));
+    FLCE_LAUNCH(FLCE_K_ROWFIX, flce::launch_rowfix(p, hidden, w, row0, rows, stream, flce::VSlice{}, 3));
     if (need_gh) {
       int splits = L.splits > 1 ? dx_splits(rows, H, p.V_pad, dtype, h->ncu) : 1;
       if (splits > L.splits) splits = L.splits;
@@ -389,17 +389,17 @@ int run_fused(flce_ctx* h, int64_t cmax, const void* hidden, const void* W, cons
       if (splits > 1)
         FLCE_LAUNCH(FLCE_K_DX_REDUCE, flce::launch_dx_reduce(p, w, grad_hidden, row0, rows, splits, stream));
     }
-    if (need_gw)
-      FLCE_LAUNCH(FLCE_K_DW, flce::launch_dw(p, hidden, w, grad_W, row0, rows, ci > 0 || p.acc_gw, stream));
+    if (need_gw) FLCE_LAUNCH(FLCE_K_DW, flce::launch_dw(p, w, grad_W, rows, ci > 0 || p.acc_gw, stream));
   }
   FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
   return FLCE_OK;
 }
 
 // The recompute mode over the rows R (plain layout; sizes already checked). Per chunk: the forward
-// pass over the whole vocabulary gives each row's lse; then per vocabulary slice the logits are
-// formed again, turned into dZ against that lse, and used at once for the slice's grad_W rows and
-// the chunk's fp32 grad_hidden sum.
+// pass over the whole vocabulary gives each row's lse and maximum, hence its final reference and its
+// factor f; then per vocabulary slice the logits are formed again into q against that reference
+// (the label entry folded in when the label lies in the slice), and used at once for the slice's
+// grad_W rows and the chunk's fp32 grad_hidden sum, which is multiplied by f at the end.
 int run_recompute(flce_ctx* h, const void* hidden, const void* W, const int64_t* labels, const Rows& R, int64_t H,
                   int64_t V, int dtype, int64_t ignore_index, float softcap, int reduction, int64_t v_slice,
                   float* loss, void* grad_hidden, float* grad_W, void* workspace, size_t workspace_bytes,
@@ -425,9 +425,7 @@ int run_recompute(flce_ctx* h, const void* hidden, const void* W, const int64_t*
   const hipStream_t stream = call.stream;
   const flce::Problem& p = call.p;
   flce::Work& w = call.w;
-  char* base = (char*)workspace;
-  w.dx_part = (float*)(base + L.off_part);
-  float* lse = (float*)(base + L.off_lse);
+  w.dx_part = (float*)((char*)workspace + L.off_part);
 
   FLCE_LAUNCH(FLCE_K_PREPASS, flce::launch_prepass(p, labels, w, h->d_status, stream));
   if (BT == 0) {
@@ -441,16 +439,18 @@ int run_recompute(flce_ctx* h, const void* hidden, const void* W, const int64_t*
     const int64_t row0 = ci * crows;
     const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
     FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
-    // pass 1: row statistics over the whole vocabulary -> lse and the loss terms
+    FLCE_LAUNCH(FLCE_K_ROWREF, flce::launch_rowref(p, hidden, W, w, row0, rows, stream));
+    // pass 1: row statistics over the whole vocabulary -> lse, the loss terms, the final references
     FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, false, stream));
-    FLCE_LAUNCH(FLCE_K_ROWS, flce::launch_rows(p, w, row0, rows, nullptr, lse, stream));
+    FLCE_LAUNCH(FLCE_K_LSE, flce::launch_lse(p, w, row0, rows, false, stream));
+    FLCE_LAUNCH(FLCE_K_ROWFIX, flce::launch_rowfix(p, hidden, w, row0, rows, stream, flce::VSlice{}, 1));
     // pass 2: per vocabulary slice
     for (int64_t v0 = 0, si = 0; v0 < V; v0 += vs, ++si) {
       const flce::VSlice sl{v0, (V - v0) < vs ? (V - v0) : vs};
-      FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, true, stream, sl));
-      FLCE_LAUNCH(FLCE_K_MERGE, flce::launch_merge(p, w, row0, rows, stream, sl, lse));
+      FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, true, stream, sl, true));
+      FLCE_LAUNCH(FLCE_K_ROWFIX, flce::launch_rowfix(p, hidden, w, row0, rows, stream, sl, 2));
       FLCE_LAUNCH(FLCE_K_DX, flce::launch_dx(p, W, w, grad_hidden, row0, rows, 1, stream, sl, si == 0 ? 1 : 2));
-      FLCE_LAUNCH(FLCE_K_DW, flce::launch_dw(p, hidden, w, grad_W, row0, rows, ci > 0, stream, sl));
+      FLCE_LAUNCH(FLCE_K_DW, flce::launch_dw(p, w, grad_W, rows, ci > 0, stream, sl));
     }
     FLCE_LAUNCH(FLCE_K_DX_REDUCE, flce::launch_dx_reduce(p, w, grad_hidden, row0, rows, 1, stream));
   }
@@ -481,8 +481,7 @@ int run_forward(flce_ctx* h, const void* hidden, const void* W, const int64_t* l
   const int red = reduction == FLCE_NONE ? FLCE_SUM : reduction;
   Call call = make_call(h, L, R, H, V, dtype, ignore_index, softcap, red, 1.0f, 0, workspace, stream_ptr);
   const hipStream_t stream = call.stream;
-  flce::Problem& p = call.p;
-  p.hidden_dense = true;  // no grad_W product: the transpose alone reads the mapped rows
+  const flce::Problem& p = call.p;
   const flce::Work& w = call.w;
 
   FLCE_LAUNCH(FLCE_K_PREPASS, flce::launch_prepass(p, labels, w, h->d_status, stream));
@@ -601,7 +600,7 @@ int flce_workspace_size_rows(flce_handle h, const flce_rows* rows, int64_t H, in
   int rc = check_rows(rows, H, dtype, true, &R);
   if (rc == FLCE_OK) rc = check_sizes(R.BT, H, V, dtype);
   if (rc != FLCE_OK) return rc;
-  *bytes = layout(R.BT, H, V, dtype, chunk_max_of(h), ncu_of(h), true, !R.dense).total;
+  *bytes = layout(R.BT, H, V, dtype, chunk_max_of(h), ncu_of(h), true).total;
   return FLCE_OK;
 }
 

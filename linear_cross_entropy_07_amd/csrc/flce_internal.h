@@ -42,16 +42,18 @@ struct DevParams {
 
 // Views of the workspace for one call (carved by the host).
 struct Work {
-  void* ws_e;          // [chunk_rows][V_pad] fp16 (bf16 path) or fp32 (fp32 path)
-  float* seg_m;        // [chunk_rows][nseg]: segment max, then (after merge) per-segment scale
+  void* ws_e;          // [chunk_rows][V_pad] q = exp(s - c) (softcap derivative), bf16 or fp32
+  float* seg_m;        // [chunk_rows][nseg]: segment max
   float* seg_s;        // [chunk_rows][nseg]: segment sum of exp(s - segment max)
   int* y32;            // [BT] label or -1 for rows that do not count
   float* s_label;      // [BT] softcapped label logit (written by the logits epilogue)
-  float* og;           // [BT] g * d s_label / d z_label (one-hot coefficient of dZ)
   float* loss_row;     // [BT]
+  float* cref;         // [BT] reference c of each row (label logit, or the row maximum)
+  float* lse;          // [BT] log-sum-exp of each row
+  float* fscale;       // [BT] f = g exp(c - lse): dZ = f q away from the label
   float* dx_part;      // [splits][chunk_rows][H] fp32 split-K partials of grad_hidden (may be null)
   void* xt;            // [H][chunk_cap] the current chunk of hidden, transposed
-  void* xs;            // [chunk_cap][H] the current chunk of hidden, gathered (only for mapped rows)
+  void* xf;            // [chunk_cap][H] f times the current chunk's rows of hidden (grad_W operand)
   int64_t chunk_cap;   // row capacity of one chunk (a multiple of 256)
   DevParams* params;   // in the workspace
 };
@@ -66,7 +68,6 @@ struct Problem {
   RowMap hmap;         // rows of hidden (elements)
   RowMap gmap;         // rows of grad_hidden (elements)
   RowMap lmap;         // labels (elements)
-  bool hidden_dense;   // hmap is the plain [BT][H] layout: the grad_W product reads hidden directly
   float grad_scale;    // multiplies both gradients
   bool acc_gh, acc_gw; // add into grad_hidden / grad_W instead of overwriting
 };
@@ -83,13 +84,21 @@ hipError_t launch_prepass(const Problem& p, const int64_t* labels, const Work& w
                           hipStream_t stream);
 hipError_t launch_transpose(const Problem& p, const void* hidden, const Work& w, int64_t row0, int64_t rows,
                             hipStream_t stream);
+// store_q: write q (else the forward-only path); qonly: write q but no statistics or label logits.
 hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t row0, int64_t rows,
-                      bool store_q, hipStream_t stream, VSlice vs = VSlice{});
+                      bool store_q, hipStream_t stream, VSlice vs = VSlice{}, bool qonly = false);
 hipError_t launch_rows(const Problem& p, const Work& w, int64_t row0, int64_t rows, float* loss_rows,
                        float* lse_rows, hipStream_t stream);
-// lse_in: per-row lse of the whole vocabulary (the recompute mode); null: from the chunk's statistics.
-hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream,
-                        VSlice vs = VSlice{}, const float* lse_in = nullptr);
+// per-row reference (label logit) of a chunk
+hipError_t launch_rowref(const Problem& p, const void* hidden, const void* W, const Work& w, int64_t row0,
+                         int64_t rows, hipStream_t stream);
+// per-row lse and loss term; references moved to the row maximum where needed, with rescale_q the
+// stored q of those rows rescaled to match
+hipError_t launch_lse(const Problem& p, const Work& w, int64_t row0, int64_t rows, bool rescale_q,
+                      hipStream_t stream);
+// mode bit 1: f and hidden_f; bit 2: the label entry of q (labels within the slice vs)
+hipError_t launch_rowfix(const Problem& p, const void* hidden, const Work& w, int64_t row0, int64_t rows,
+                         hipStream_t stream, VSlice vs, int mode);
 // part_mode: 0 the normal output, 1 write the fp32 [rows][H] partials (one split), 2 add to them.
 hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_hidden, int64_t row0,
                      int64_t rows, int splits, hipStream_t stream, VSlice vs = VSlice{}, int part_mode = 0);
@@ -98,8 +107,8 @@ hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_
 hipError_t launch_zero_rows(const Problem& p, void* grad_hidden, int64_t B, int64_t off, hipStream_t stream);
 hipError_t launch_dx_reduce(const Problem& p, const Work& w, void* grad_hidden, int64_t row0, int64_t rows,
                             int splits, hipStream_t stream);
-hipError_t launch_dw(const Problem& p, const void* hidden, const Work& w, float* grad_W, int64_t row0,
-                     int64_t rows, bool accumulate, hipStream_t stream, VSlice vs = VSlice{});
+hipError_t launch_dw(const Problem& p, const Work& w, float* grad_W, int64_t rows, bool accumulate,
+                     hipStream_t stream, VSlice vs = VSlice{});
 hipError_t launch_finalize(const Problem& p, const Work& w, float* loss, hipStream_t stream);
 hipError_t launch_zero_f32(float* ptr, int64_t n, hipStream_t stream);
 

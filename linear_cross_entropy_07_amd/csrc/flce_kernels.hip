@@ -6,17 +6,25 @@
 // the backward pass rebuilds the softmax from the softmax input and the small max/sum tensors
 // instead of reading a saved softmax output. Here that happens per BT chunk:
 //
+//   k_rowref  per row: a reference c = the (softcapped) label logit, one dot product of hidden and
+//             the label's row of W, known before the logits exist.
 //   k_fwd     Z^T tile = W_tile . X_tile^T on MFMA (bf16 -> fp32), epilogue: optional softcap,
 //             per-(row, 128-wide V segment) max and sum of exp, and one 16-bit store per logit of
-//             q = exp(s - segment max) * (softcap derivative). No [BT, V] tensor exists.
-//   k_merge_dlogits  per row: lse from the segment statistics and the loss term; then one sweep
-//             over the row rebuilds the softmax from q and turns it into dZ in place, in the operand
-//             type of the backward GEMMs: the chunk's dZ exists in HBM (in the q buffer) until the
-//             backward GEMMs have read it.
-//   k_dx      grad_hidden chunk = dZ . W on MFMA (W read MN-contiguous, transposed by the LDS
-//             transpose reads on its way to the matrix cores).
-//   k_dw      grad_W (+)= dZ^T . X on MFMA; both operands read MN-contiguous and transposed the same
-//             way; fp32 accumulation in place across chunks.
+//             q = exp(s - c) * (softcap derivative): the softmax numerator against the row's
+//             reference. No [BT, V] tensor exists.
+//   k_lse     per row: lse from the segment statistics and the loss term; a row whose maximum lies
+//             more than kRefSpan above its reference gets the maximum as reference, its stored q
+//             rescaled segment by segment to match (the usual rows do nothing more).
+//   k_rowfix  per row: f = g exp(c - lse), so that dZ_v = f q_v for v != label; the label entry of
+//             q becomes (p_y - 1) / f, computed from the exact label logit; and hidden_f = f hidden.
+//   k_dx      grad_hidden chunk = f . (q . W) on MFMA (W read MN-contiguous, transposed by the LDS
+//             transpose reads on its way to the matrix cores; f applied to each output row).
+//   k_dw      grad_W (+)= q^T . hidden_f on MFMA; both operands read MN-contiguous and transposed the
+//             same way; fp32 accumulation in place across chunks.
+// So the softmax is rebuilt from the stored softmax input and the small per-row max/sum statistics,
+// and dlogits are never written: the backward GEMMs take q as it was stored and the per-row factor
+// f enters by linearity (an output-row scale for grad_hidden, a scaled copy of the chunk's hidden
+// rows for grad_W).
 //
 // One GEMM core serves the three products: 256 threads (4 waves of 64) compute a 256 x 256 tile,
 // each wave a 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (or 32x32x2f32 for
@@ -36,8 +44,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // GEMM block: a 256 x 256 output tile split over NW waves as 2 (M) x NW/2 (N). With 8 waves each
 // wave owns 128 x 64 (128 accumulator registers) and two waves share each SIMD, which doubles the
@@ -55,10 +62,16 @@ constexpr int TBN = WN / 32;     // ... along N (2 or 4)
 static_assert(NW == 4 || NW == 8, "4 or 8 waves per GEMM block");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// q = exp(s - c) is stored against a per-row reference c, the exponent of its segment factor clamped
+// at kRefSpan; a row whose maximum lies more than kRefSpan above c (only possible where the label
+// logit lies that far below the row's maximum) is rescaled to its maximum afterwards.
+// exp(kRefSpan) = 7e20 keeps q, and the fp32 sums of q times W over up to 2^20 vocabulary rows, far
+// from overflow.
+constexpr float kRefSpan = 48.0f;
 
 template <typename T> struct Traits;
 template <> struct Traits<__bf16> {
-  using S = _Float16;                 // workspace element type
+  using S = __bf16;                   // workspace element type (q is an operand of the bf16 GEMMs)
   static constexpr int KV = 8;        // elements per 16-byte chunk
 };
 template <> struct Traits<float> {
@@ -88,11 +101,6 @@ __device__ __forceinline__ void mma(f32x16& acc, u32x4 a, u32x4 b, float*) {
 }
 
 // ---- 16-byte chunk conversions -------------------------------------------------------------
-__device__ __forceinline__ void unpack(u32x4 v, float (&f)[8], _Float16*) {
-  const f16x8 h = __builtin_bit_cast(f16x8, v);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
-}
 __device__ __forceinline__ void unpack(u32x4 v, float (&f)[8], __bf16*) {
   const f32x8 h = __builtin_convertvector(__builtin_bit_cast(bf16x8, v), f32x8);
 #pragma unroll
@@ -114,6 +122,9 @@ __device__ __forceinline__ u32x4 pack(const float (&f)[4], float*) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = f[i];
   return __builtin_bit_cast(u32x4, v);
+}
+__device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
+  return __builtin_bit_cast(u32x2, __builtin_convertvector((f32x4{a, b, c, d}), bf16x4));  // nearest even
 }
 
 // ---- block -> tile mapping -------------------------------------------------------------------
@@ -150,9 +161,11 @@ __device__ __forceinline__ u32 lds_addr(const void* p) {
   return (u32)(size_t)(__attribute__((address_space(3))) const void*)p;
 }
 __device__ __forceinline__ void dma16(i32x4 desc, u32 voff, u32 lds) {
-  // M0 must be written one instruction before an LDS-DMA load reads it.
+  // M0 must be written one instruction before an LDS-DMA load reads it. M0 is a reserved register for
+  // the compiler (never allocated; its own users write it right before they read it), so it cannot
+  // appear in a clobber list and nothing the compiler emits relies on M0 across this statement.
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(voff), "s"(desc), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+               :: "v"(voff), "s"(desc), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
 // Range-checked buffer accesses for epilogues: loads outside the range return 0, stores outside it
@@ -506,8 +519,7 @@ struct FwdArgs {
   float* seg_s;
   const int* y;       // chunk row 0: label or -1
   float* s_label;     // chunk row 0
-  float* og;          // chunk row 0
-  const DevParams* prm;
+  const float* cref;  // chunk row 0: the reference c of each row (q = exp(s - c) ...)
   int64_t H, V, V_pad;  // V columns of W starting at W's row 0 (a slice of the vocabulary: V = slice width)
   int nseg, rows;
   int yoff;           // vocabulary index of W's row 0: labels are taken relative to it
@@ -516,7 +528,8 @@ struct FwdArgs {
 
 struct DxArgs {
   const void* W;
-  const void* ws;     // dZ of the chunk, [rows][V_pad]
+  const void* ws;     // q of the chunk, [rows][V_pad]
+  const float* fscale;  // chunk row 0: the per-row factor f of dZ = f q (applied to the output rows)
   void* out;          // grad_hidden (splits == 1): row r of the call starts at element gmap(r)
   RowMap gmap;
   int64_t row0;       // call row of chunk row 0
@@ -528,8 +541,8 @@ struct DxArgs {
 };
 
 struct DwArgs {
-  const void* X;      // hidden, chunk row 0
-  const void* ws;     // dZ of the chunk, [rows][V_pad]
+  const void* X;      // hidden_f = f hidden of the chunk, [rows][H]
+  const void* ws;     // q of the chunk, [rows][V_pad]
   float* dW;
   int64_t H, V, V_pad;
   int rows, accumulate;
@@ -573,7 +586,7 @@ constexpr int kGroupDw = FLCE_GROUP_DW;
 // whether the quarter crosses V (EDGE): the common case has no per-element masking at all. For each
 // 32-row block j, each lane holds column c (a chunk row) and 64 v values; the two lanes c and c+32
 // hold the two halves of the wave's 128-wide segment of row c.
-// Labels of this lane's 4 chunk rows (range-checked loads; -1 past the chunk).
+// Labels of this lane's chunk rows (range-checked loads; -1 past the chunk).
 __device__ __forceinline__ void fwd_labels(const FwdArgs& a, int c0, int (&ylab)[TBN]) {
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) >> 1;
   const rsrc_t ry = make_rsrc(a.y, (int64_t)a.rows * 4);
@@ -593,13 +606,21 @@ __device__ __forceinline__ u32 qlds(int cl, int vl) {  // byte address of q(cl, 
   return (u32)(cl * (TILE * 2) + (((vl >> 3) ^ (cl & 31)) << 4) + ((vl & 7) << 1));
 }
 
-template <typename T, bool CAP, bool EDGE, bool STORE_Q, int J0, int JG>
+// QONLY: store q only (slices of the recompute mode), no statistics or label logits.
+template <typename T, bool CAP, bool EDGE, bool STORE_Q, bool QONLY, int J0, int JG>
 __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc)[TBM][TBN], int v0, int c0,
                                                   const int (&ylab)[TBN], char* smem) {
   using S = typename Traits<T>::S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int vw = v0 + wm * WM, seg = vw / kSeg, half = lane >> 5;
   const float cap = a.softcap, icap = CAP ? 1.0f / cap : 0.0f;
+  // references of the lane's rows (0 past the chunk), consumed in phase 3
+  float cr[TBN];
+  if constexpr (STORE_Q) {
+    const rsrc_t rc = make_rsrc(a.cref, (int64_t)a.rows * 4);
+#pragma unroll
+    for (int j = J0; j < J0 + JG; ++j) cr[j] = bload_f32(rc, (u32)(c0 + wn * WN + 32 * j + (lane & 31)) * 4, 0);
+  }
   // Row blocks J0 .. J0+JG-1. They are independent; each phase runs over all of them so that the
   // single wave per SIMD has independent work (and the cross-half exchanges are in flight together).
   // Phase 1: softcap in place and the maxima (4 chains per j).
@@ -634,7 +655,9 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
 #pragma unroll
     for (int j = J0; j < J0 + JG; ++j) mx[j] = fmaxf(mx[j], o[j]);
   }
-  // Phase 3: q = exp(s - segment max) (times the softcap derivative) to the workspace, and the sums.
+  // Phase 3: the sums of e = exp(s - segment max), and q = e exp(segment max - c) (times the softcap
+  // derivative) = exp(s - c) to the workspace, the exponent of the second factor clamped at kRefSpan
+  // (k_lse rescales rows beyond it). Rows that do not count have c = +inf, hence q = 0.
   // q tile: rows c0.. of the chunk (rows past the chunk are dropped), columns v0 .. v0+255 < V_pad
   const rsrc_t rq = make_rsrc((S*)a.ws + (int64_t)c0 * a.V_pad + v0,
                               (int64_t)min(TILE, a.rows - c0) * a.V_pad * (int64_t)sizeof(S));
@@ -644,6 +667,7 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
     const int c = c0 + wn * WN + 32 * j + (lane & 31);
     const float ms = mx[j] == kNegInf ? 0.0f : mx[j];
     const float msl = -ms * kLog2e;
+    const float kq = STORE_Q ? ex2(fminf(ms - cr[j], kRefSpan) * kLog2e) : 1.0f;
     const u32 qrow = (u32)(((int64_t)(c - c0) * a.V_pad + wm * WM + 4 * half) * (int64_t)sizeof(S));
     float sum4[TBM];
 #pragma unroll
@@ -663,20 +687,18 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
           sum4[i] += e;
           if constexpr (CAP) {
             const float t = s * icap;
-            q[rr] = e * (1.0f - t * t);
+            q[rr] = (e * kq) * (1.0f - t * t);
           } else {
-            q[rr] = e;
+            q[rr] = e * kq;
           }
         }
         const u32 qoff = qrow + (u32)((32 * i + 8 * g) * sizeof(S));
         if constexpr (!STORE_Q) {
           (void)qoff;
         } else if constexpr (kStageQ<T>) {
-          f16x4 h{(S)q[0], (S)q[1], (S)q[2], (S)q[3]};
-          *(u32x2*)(smem + qlds(c - c0, wm * WM + 32 * i + 8 * g + 4 * half)) = __builtin_bit_cast(u32x2, h);
+          *(u32x2*)(smem + qlds(c - c0, wm * WM + 32 * i + 8 * g + 4 * half)) = pack4_bf16(q[0], q[1], q[2], q[3]);
         } else if constexpr (sizeof(S) == 2) {
-          f16x4 h{(S)q[0], (S)q[1], (S)q[2], (S)q[3]};
-          bstore_b64(rq, qoff, __builtin_bit_cast(u32x2, h));
+          bstore_b64(rq, qoff, pack4_bf16(q[0], q[1], q[2], q[3]));
         } else {
           bstore_b128(rq, qoff, __builtin_bit_cast(u32x4, f32x4{q[0], q[1], q[2], q[3]}));
         }
@@ -684,6 +706,8 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
     }
     sum[j] = (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
   }
+  // Phases 4 and 5 (not for vocabulary slices, whose statistics exist already).
+  if constexpr (QONLY) return;
   // Phase 4: segment statistics of the tile's rows.
   {
     float o[TBN];
@@ -717,20 +741,18 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
       }
       if (mine) {
         const int c = c0 + wn * WN + 32 * j + (lane & 31);
-        const float g = a.prm->ginv, t = sy * icap;
         a.s_label[c] = sy;
-        a.og[c] = CAP ? g * (1.0f - t * t) : g;
       }
     }
   }
 }
 
-template <typename T, bool CAP, bool EDGE, bool STORE_Q>
+template <typename T, bool CAP, bool EDGE, bool STORE_Q, bool QONLY>
 __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16 (&acc)[TBM][TBN], int v0, int c0,
                                              const int (&ylab)[TBN], char* smem) {
   // two row blocks at a time: enough independent work, few enough live values to stay in registers
-  fwd_epilogue_part<T, CAP, EDGE, STORE_Q, 0, 2>(a, acc, v0, c0, ylab, smem);
-  if constexpr (TBN > 2) fwd_epilogue_part<T, CAP, EDGE, STORE_Q, 2, 2>(a, acc, v0, c0, ylab, smem);
+  fwd_epilogue_part<T, CAP, EDGE, STORE_Q, QONLY, 0, 2>(a, acc, v0, c0, ylab, smem);
+  if constexpr (TBN > 2) fwd_epilogue_part<T, CAP, EDGE, STORE_Q, QONLY, 2, 2>(a, acc, v0, c0, ylab, smem);
 }
 
 // Staged q tile -> workspace: 32 threads per 512-byte row, each one 16-byte chunk; rows past the
@@ -749,17 +771,10 @@ __device__ __forceinline__ void fwd_store_staged(const FwdArgs& a, int v0, int c
   }
 }
 
-// STORE_Q = false is the forward-only path: the row statistics and label logits are produced, the
-// q tile is not stored.
-template <typename T, bool STORE_Q>
-__global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes];
-
-  const int mt = (int)(a.V_pad / TILE), nt = (a.rows + TILE - 1) / TILE;
-  int tm, tn;
-  grouped(xcd_remap(blockIdx.x, gridDim.x), mt, nt, kGroupFwd, tm, tn);
-  const int v0 = tm * TILE, c0 = tn * TILE;
-
+// One 256 x 256 tile of the logits product and its epilogue. STORE_Q = false is the forward-only
+// path: the row statistics and label logits are produced, the q tile is not stored. QONLY: q only.
+template <typename T, bool STORE_Q, bool QONLY>
+__device__ __forceinline__ void fwd_tile(const FwdArgs& a, int v0, int c0, char* smem) {
   OpK<T> la;   // W rows v0.., K = h contiguous
   la.init((const T*)a.W + (int64_t)v0 * a.H, a.H, (int)min<int64_t>(TILE, a.V - v0), (int)a.H);
   OpMN<T> lb;  // hidden^T: source rows are h (K), columns the chunk rows c0..
@@ -776,14 +791,14 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
   const bool edge = v0 + (((int)threadIdx.x >> 6) & 1) * WM + WM > a.V;
   if (a.softcap > 0.0f) {
     if (edge)
-      fwd_epilogue<T, true, true, STORE_Q>(a, acc, v0, c0, ylab, smem);
+      fwd_epilogue<T, true, true, STORE_Q, QONLY>(a, acc, v0, c0, ylab, smem);
     else
-      fwd_epilogue<T, true, false, STORE_Q>(a, acc, v0, c0, ylab, smem);
+      fwd_epilogue<T, true, false, STORE_Q, QONLY>(a, acc, v0, c0, ylab, smem);
   } else {
     if (edge)
-      fwd_epilogue<T, false, true, STORE_Q>(a, acc, v0, c0, ylab, smem);
+      fwd_epilogue<T, false, true, STORE_Q, QONLY>(a, acc, v0, c0, ylab, smem);
     else
-      fwd_epilogue<T, false, false, STORE_Q>(a, acc, v0, c0, ylab, smem);
+      fwd_epilogue<T, false, false, STORE_Q, QONLY>(a, acc, v0, c0, ylab, smem);
   }
   if constexpr (STORE_Q && kStageQ<T>) {
     __syncthreads();
@@ -791,11 +806,20 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
   }
 }
 
-// ---- grad_hidden = dZ . W ---------------------------------------------------------------------
+template <typename T, bool STORE_Q, bool QONLY>
+__global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes];
+  const int mt = (int)(a.V_pad / TILE), nt = (a.rows + TILE - 1) / TILE;
+  int tm, tn;
+  grouped(xcd_remap(blockIdx.x, gridDim.x), mt, nt, kGroupFwd, tm, tn);
+  fwd_tile<T, STORE_Q, QONLY>(a, tm * TILE, tn * TILE, smem);
+}
+
+// ---- grad_hidden = f . (q . W) -------------------------------------------------------------------
 // The fp32 tile goes through the (then idle) LDS ring in passes of kDxPassRows rows and leaves as
-// 16-byte pieces of whole caller rows: each row is placed by the row map (sequences with strides,
-// shifted labels), and with `accumulate` added to what the row holds (one rounding to the output
-// type, after the add). Pass p stages row blocks 2p and 2p+1 of every wave (tile rows
+// 16-byte pieces of whole caller rows: each row is multiplied by its factor f, placed by the row map
+// (sequences with strides, shifted labels), and with `accumulate` added to what the row holds (one
+// rounding to the output type, after the add). Pass p stages row blocks 2p and 2p+1 of every wave (tile rows
 // wm * WM + 64 p .. + 63), so the accumulators of a pass are dead before its read-out.
 constexpr int kDxRowBytes = TILE * 4;
 constexpr int kDxPassRows = WM;
@@ -832,14 +856,15 @@ __device__ __forceinline__ void dx_store_tile(const DxArgs& a, const f32x16 (&ac
       const int c = (rl / kWaveRows) * WM + pass * kWaveRows + rl % kWaveRows;
       if (c < vrows && h < a.H) {
         const float* src = (const float*)(smem + rl * kDxRowBytes) + ch * OV;
+        const float fs = a.fscale[c0 + c];
         float f[OV];
 #pragma unroll
         for (int e = 0; e < OV; e += 4) {
           const f32x4 v = *(const f32x4*)(src + e);
-          f[e] = v[0];
-          f[e + 1] = v[1];
-          f[e + 2] = v[2];
-          f[e + 3] = v[3];
+          f[e] = v[0] * fs;
+          f[e + 1] = v[1] * fs;
+          f[e + 2] = v[2] * fs;
+          f[e + 3] = v[3] * fs;
         }
         T* dst = (T*)a.out + a.gmap(a.row0 + c0 + c) + h;
         if (a.accumulate) {
@@ -873,7 +898,7 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
   const int nk = (int)(a.V_pad / BK);
   const int kb = split * a.ksteps_per_split;
   const int ke = min(nk, kb + a.ksteps_per_split);
-  OpK<T> la;  // dZ rows of the chunk, K = v (only this split's K range is loaded)
+  OpK<T> la;  // q rows of the chunk, K = v (only this split's K range is loaded)
   la.init((const T*)a.ws + (int64_t)c0 * a.V_pad, a.V_pad, min(TILE, a.rows - c0), ke * BK);
   OpMN<T> lb;  // W: source rows are v (K), columns h
   lb.init((const T*)a.W + h0, a.H, (int)min<int64_t>(a.V, (int64_t)ke * BK), (int)min<int64_t>(TILE, a.H - h0));
@@ -915,11 +940,12 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
   }
 }
 
-// Fixed-order sum of the split-K partials of grad_hidden, placed by the row map (and added to what the
-// row holds with `accumulate`). Blocks: x over H, y over chunk rows (grid-stride).
+// Fixed-order sum of the split-K partials of grad_hidden times the row's factor f, placed by the row
+// map (and added to what the row holds with `accumulate`). Blocks: x over H, y over chunk rows
+// (grid-stride).
 template <typename T>
 __global__ __launch_bounds__(256) void k_dx_reduce(const float* part, int splits, int rows, int64_t H, T* out,
-                                                   RowMap gmap, int64_t row0, int accumulate) {
+                                                   RowMap gmap, int64_t row0, int accumulate, const float* fscale) {
   const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (h >= H) return;
   const int64_t n = (int64_t)rows * H;
@@ -927,13 +953,14 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const float* part, int splits
     const int64_t i = (int64_t)c * H + h;
     float s = 0.0f;
     for (int k = 0; k < splits; ++k) s += part[(int64_t)k * n + i];
+    s *= fscale[c];
     T* dst = out + gmap(row0 + c) + h;
     if (accumulate) s += (float)*dst;
     *dst = (T)s;
   }
 }
 
-// ---- grad_W (+)= dZ^T . X -----------------------------------------------------------------------
+// ---- grad_W (+)= q^T . hidden_f ---------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes];
@@ -943,9 +970,9 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
   grouped(xcd_remap(blockIdx.x, gridDim.x), mt, nt, kGroupDw, tm, tn);
   const int v0 = tm * TILE, h0 = tn * TILE;
 
-  OpMN<T> la;  // dZ^T: source rows are chunk rows (K), columns are v (M); v0 + 256 <= V_pad
+  OpMN<T> la;  // q^T: source rows are chunk rows (K), columns are v (M); v0 + 256 <= V_pad
   la.init((const T*)a.ws + v0, a.V_pad, a.rows, TILE);
-  OpMN<T> lb;  // X: source rows are chunk rows (K), columns h
+  OpMN<T> lb;  // hidden_f: source rows are chunk rows (K), columns h
   lb.init((const T*)a.X + h0, a.H, a.rows, (int)min<int64_t>(TILE, a.H - h0));
 
   const int nk = (a.rows + OpMN<T>::BK - 1) / OpMN<T>::BK;
@@ -992,11 +1019,10 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
 }
 
 // ---- hidden chunk transpose: [rows][H] -> [H][ldt] through a 64 x 64 LDS tile ------------------
-// Row r of the chunk is call row row0 + r, found in hidden by the row map; with Xs the chunk is also
-// gathered into a plain [rows][H] copy (for the grad_W product when the rows are mapped).
+// Row r of the chunk is call row row0 + r, found in hidden by the row map.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* X, RowMap hmap, int64_t row0, int rows, int H, T* XT,
-                                                   int64_t ldt, T* Xs) {
+                                                   int64_t ldt) {
   __shared__ T tile[64][65];
   __shared__ int64_t roff[64];
   const int r0 = blockIdx.y * 64, h0 = blockIdx.x * 64;
@@ -1007,9 +1033,7 @@ __global__ __launch_bounds__(256) void k_transpose(const T* X, RowMap hmap, int6
   for (int k = 0; k < 16; ++k) {
     const int r = r0 + ty + 4 * k, h = h0 + tx;
     const bool in = r < rows && h < H;
-    const T v = in ? X[roff[ty + 4 * k] + h] : (T)0.0f;
-    tile[ty + 4 * k][tx] = v;
-    if (Xs && in) Xs[(int64_t)r * H + h] = v;
+    tile[ty + 4 * k][tx] = in ? X[roff[ty + 4 * k] + h] : (T)0.0f;
   }
   __syncthreads();
 #pragma unroll
@@ -1066,17 +1090,14 @@ __global__ __launch_bounds__(1024) void k_prepass(const int64_t* labels, RowMap 
   }
 }
 
-// Row merge + dlogits (one block per chunk row): lse from the segment statistics, the loss term,
-// then one sweep over the row turning q into dZ = q * g * exp(m_seg - lse) - [v == y] * og, written
-// in place in the operand type of the backward GEMMs. This is where the softmax is rebuilt from the
-// logits-derived q and the small per-row max/sum statistics.
 // Per-row log-sum-exp from the per-(row, 128-wide segment) statistics of the logits epilogue, in a
 // fixed order (max over the segments, then the rescaled sum), and the row's loss term (0 on rows that
 // do not count). One 256-thread block per row; every thread returns the row's lse.
 __device__ __forceinline__ float row_lse(const float* m, const float* sp, int nseg, int c, const int* y32,
-                                         const float* s_label, float* loss_row, float* lse_out) {
+                                         const float* s_label, float* loss_row, float* lse_out,
+                                         float* max_out = nullptr) {
   __shared__ float red[4];
-  __shared__ float s_lse;
+  __shared__ float s_lse, s_max;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float M = kNegInf;
   for (int j = threadIdx.x; j < nseg; j += 256) M = fmaxf(M, m[j]);
@@ -1084,6 +1105,7 @@ __device__ __forceinline__ float row_lse(const float* m, const float* sp, int ns
   if (lane == 0) red[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (threadIdx.x == 0) s_max = M;
   __syncthreads();
   float Ssum = 0.0f;
   for (int j = threadIdx.x; j < nseg; j += 256) Ssum += sp[j] * ex2((m[j] - M) * kLog2e);
@@ -1097,50 +1119,110 @@ __device__ __forceinline__ float row_lse(const float* m, const float* sp, int ns
     if (lse_out) lse_out[c] = lse;
   }
   __syncthreads();
+  if (max_out) *max_out = s_max;
   return s_lse;
 }
 
-// With lse_in (the recompute mode) the row's lse comes from the forward pass over the whole
-// vocabulary, the statistics and q cover one vocabulary slice starting at index yoff, and no loss term
-// is written.
+// Reference of each row of a chunk (one wave per row): c = the softcapped label logit, the dot product
+// of the row of hidden with the label's row of W in fp32; +inf for rows that do not count (their q is
+// then 0).
 template <typename T>
-__global__ __launch_bounds__(256) void k_merge_dlogits(void* ws, const float* seg_m, const float* seg_s,
-                                                       int nseg, int64_t V_pad, const int* y32,
-                                                       const float* s_label, const float* og,
-                                                       const DevParams* prm, float* loss_row,
-                                                       const float* lse_in, int yoff) {
+__global__ __launch_bounds__(256) void k_rowref(const T* X, RowMap hmap, int64_t row0, int rows, int H, const T* W,
+                                                const int* y32, float softcap, float* cref) {
+  constexpr int KV = Traits<T>::KV;
+  const int lane = threadIdx.x & 63, r = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int y = y32[r];
+  if (y < 0) {
+    if (lane == 0) cref[r] = __builtin_huge_valf();
+    return;
+  }
+  const T* x = X + hmap(row0 + r);
+  const T* w = W + (int64_t)y * H;
+  float acc = 0.0f;
+  for (int h = lane * KV; h < H; h += 64 * KV) {
+    float a[KV], b[KV];
+    unpack(*(const u32x4*)(x + h), a, (T*)nullptr);
+    unpack(*(const u32x4*)(w + h), b, (T*)nullptr);
+#pragma unroll
+    for (int e = 0; e < KV; ++e) acc = fmaf(a[e], b[e], acc);
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) cref[r] = softcap > 0.0f ? softcap * tanh_via_exp(acc / softcap) : acc;
+}
+
+// Per row of a chunk (one block per row): lse from the segment statistics and the loss term. A row
+// whose maximum M lies more than kRefSpan above its reference c gets M as its reference; with `q`
+// (the fused call, where q exists already) its stored q is rescaled to match: segment j was stored as
+// exp(s - m_j) exp(min(m_j - c, kRefSpan)) (m_j the segment maximum), so it is multiplied by
+// exp(m_j - M - min(m_j - c, kRefSpan)), a factor at most exp(-kRefSpan). Other rows stop after the
+// statistics.
+template <typename T>
+__global__ __launch_bounds__(256) void k_lse(const float* seg_m, const float* seg_s, int nseg, const int* y32,
+                                             const float* s_label, float* loss_row, float* lse, float* cref,
+                                             void* q, int64_t ldq) {
   using S = typename Traits<T>::S;
   constexpr int KV = Traits<T>::KV;
-  extern __shared__ float sc_seg[];  // [nseg]: g * exp(m_seg - lse)
   const int c = blockIdx.x;
   const float* m = seg_m + (int64_t)c * nseg;
-  const float lse = lse_in ? lse_in[c] : row_lse(m, seg_s + (int64_t)c * nseg, nseg, c, y32, s_label, loss_row, nullptr);
-  const int y0 = y32[c];
-  const float g = y0 >= 0 ? prm->ginv : 0.0f;
-  const int y = y0 >= 0 ? y0 - yoff : -1;  // the label's column in this slice (outside it: no match)
-  for (int j = threadIdx.x; j < nseg; j += 256) sc_seg[j] = g * ex2((m[j] - lse) * kLog2e);
-  __syncthreads();
-  const float oc = og[c];
-  // one sweep over the row, four 16-byte chunks per thread in flight; range-checked accesses make
-  // the tail branch-free (loads past the row read zeros, stores past it are dropped)
-  const int nch = (int)(V_pad / KV);
-  const rsrc_t rr = make_rsrc((S*)ws + (int64_t)c * V_pad, V_pad * (int64_t)sizeof(S));
-  for (int base = threadIdx.x; base < nch; base += 4 * 256) {
-    u32x4 v[4];
+  float M;
+  row_lse(m, seg_s + (int64_t)c * nseg, nseg, c, y32, s_label, loss_row, lse, &M);
+  const float c_old = cref[c];
+  if (!(M - c_old > kRefSpan)) return;  // the same decision in every thread of the block
+  __syncthreads();                      // every thread has read the old reference
+  if (threadIdx.x == 0) cref[c] = M;
+  if (!q) return;
+  S* row = (S*)q + (int64_t)c * ldq;
+  for (int k = (int)threadIdx.x; k < (int)(ldq / KV); k += 256) {
+    const float mj = m[k * KV / kSeg];
+    if (mj == kNegInf) continue;  // a segment wholly past V: its q is 0
+    const float f = ex2((mj - M - fminf(mj - c_old, kRefSpan)) * kLog2e);
+    float v[KV];
+    unpack(*(const u32x4*)(row + k * KV), v, (S*)nullptr);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (base + 256 * u) * 16, 0, 0));
+    for (int e = 0; e < KV; ++e) v[e] *= f;
+    *(u32x4*)(row + k * KV) = pack(v, (S*)nullptr);
+  }
+}
+
+// Per row of a chunk (one block per row), after the last q of the row is formed.
+//   SCALE: f = g exp(c - lse) (0 for rows that do not count), so that dZ_v = f q_v away from the
+//          label; fscale gets f and hidden_f (plain [rows][H]) gets f times the row of hidden.
+//   FOLD:  the label's entry of q (when the label lies in the vocabulary columns [v0, v0 + vn) that q
+//          holds) becomes dZ_y / f = (softcap derivative) exp(lse - c) expm1(s_y - lse), computed
+//          in fp32 from the exact label logit s_y, so that dZ_y = g (p_y - 1) (softcap derivative)
+//          keeps its relative precision when p_y is close to 1. Both factors are finite: lse - c is at
+//          most ln V + kRefSpan once the reference is within kRefSpan of the row maximum, and
+//          expm1(s_y - lse) lies in (-1, 0].
+template <typename T>
+__global__ __launch_bounds__(256) void k_rowfix(const T* X, RowMap hmap, int64_t row0, int H, T* Xf,
+                                                const int* y32, const float* s_label, const float* lse,
+                                                const float* cref, const DevParams* prm, float softcap,
+                                                float* fscale, void* q, int64_t ldq, int v0, int vn, int mode) {
+  using S = typename Traits<T>::S;
+  constexpr int KV = Traits<T>::KV;
+  const int c = blockIdx.x;
+  const int y = y32[c];
+  const float l = lse[c], cr = cref[c];
+  if (mode & 1) {
+    const float g = y >= 0 ? prm->ginv : 0.0f;
+    const float f = g == 0.0f ? 0.0f : g * ex2((cr - l) * kLog2e);
+    if (threadIdx.x == 0) fscale[c] = f;
+    const T* x = X + hmap(row0 + c);
+    T* xf = Xf + (int64_t)c * H;
+    for (int h = (int)threadIdx.x * KV; h < H; h += 256 * KV) {
+      float v[KV];
+      unpack(*(const u32x4*)(x + h), v, (T*)nullptr);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = base + 256 * u, v0 = q * KV;
-      const float sc = sc_seg[min(v0 / kSeg, nseg - 1)];
-      float f[KV];
-      unpack(v[u], f, (S*)nullptr);
-      const unsigned rel = (unsigned)(y - v0);
-#pragma unroll
-      for (int e = 0; e < KV; ++e) f[e] = f[e] * sc - (rel == (unsigned)e ? oc : 0.0f);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pack(f, (T*)nullptr)), rr, q * 16, 0, 0);
+      for (int e = 0; e < KV; ++e) v[e] *= f;
+      *(u32x4*)(xf + h) = pack(v, (T*)nullptr);
     }
+  }
+  if ((mode & 2) && threadIdx.x == 0 && y >= v0 && y < v0 + vn) {
+    const float sy = s_label[c];
+    const float t = softcap > 0.0f ? sy / softcap : 0.0f;
+    const float val = (1.0f - t * t) * ex2((l - cr) * kLog2e) * expm1f(sy - l);
+    ((S*)q)[(int64_t)c * ldq + (y - v0)] = (S)val;
   }
 }
 
@@ -1222,19 +1304,17 @@ hipError_t launch_prepass(const Problem& p, const int64_t* labels, const Work& w
 hipError_t launch_transpose(const Problem& p, const void* hidden, const Work& w, int64_t row0, int64_t rows,
                             hipStream_t stream) {
   const dim3 grid((unsigned)((p.H + 63) / 64), (unsigned)((rows + 63) / 64));
-  if (!p.hidden_dense && !w.xs) return hipErrorInvalidValue;
-  void* xs = p.hidden_dense ? nullptr : w.xs;
   if (p.dtype == 0)
     k_transpose<__bf16><<<grid, 256, 0, stream>>>((const __bf16*)hidden, p.hmap, row0, (int)rows, (int)p.H,
-                                                  (__bf16*)w.xt, w.chunk_cap, (__bf16*)xs);
+                                                  (__bf16*)w.xt, w.chunk_cap);
   else
     k_transpose<float><<<grid, 256, 0, stream>>>((const float*)hidden, p.hmap, row0, (int)rows, (int)p.H,
-                                                 (float*)w.xt, w.chunk_cap, (float*)xs);
+                                                 (float*)w.xt, w.chunk_cap);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t row0, int64_t rows,
-                      bool store_q, hipStream_t stream, VSlice vs) {
+namespace {
+FwdArgs fwd_args(const Problem& p, const void* W, const Work& w, int64_t row0, int64_t rows, VSlice vs) {
   if (vs.vn < 0) vs = VSlice{0, p.V};
   const int64_t V_pad = (vs.vn + TILE - 1) / TILE * TILE;
   const size_t esz = p.dtype == 0 ? 2 : 4;
@@ -1247,8 +1327,7 @@ hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t ro
   a.seg_s = w.seg_s;
   a.y = w.y32 + row0;
   a.s_label = w.s_label + row0;
-  a.og = w.og + row0;
-  a.prm = w.params;
+  a.cref = w.cref + row0;
   a.H = p.H;
   a.V = vs.vn;
   a.V_pad = V_pad;
@@ -1256,34 +1335,69 @@ hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t ro
   a.rows = (int)rows;
   a.yoff = (int)vs.v0;
   a.softcap = p.softcap;
-  const unsigned grid = (unsigned)((V_pad / TILE) * ((rows + TILE - 1) / TILE));
+  return a;
+}
+}  // namespace
+
+hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t row0, int64_t rows,
+                      bool store_q, hipStream_t stream, VSlice vs, bool qonly) {
+  const FwdArgs a = fwd_args(p, W, w, row0, rows, vs);
+  const unsigned grid = (unsigned)((a.V_pad / TILE) * ((rows + TILE - 1) / TILE));
+  if (!store_q && qonly) return hipErrorInvalidValue;
   if (p.dtype == 0) {
-    if (store_q)
-      k_fwd<__bf16, true><<<grid, NTHR, 0, stream>>>(a);
+    if (!store_q)
+      k_fwd<__bf16, false, false><<<grid, NTHR, 0, stream>>>(a);
+    else if (qonly)
+      k_fwd<__bf16, true, true><<<grid, NTHR, 0, stream>>>(a);
     else
-      k_fwd<__bf16, false><<<grid, NTHR, 0, stream>>>(a);
+      k_fwd<__bf16, true, false><<<grid, NTHR, 0, stream>>>(a);
   } else {
-    if (store_q)
-      k_fwd<float, true><<<grid, NTHR, 0, stream>>>(a);
+    if (!store_q)
+      k_fwd<float, false, false><<<grid, NTHR, 0, stream>>>(a);
+    else if (qonly)
+      k_fwd<float, true, true><<<grid, NTHR, 0, stream>>>(a);
     else
-      k_fwd<float, false><<<grid, NTHR, 0, stream>>>(a);
+      k_fwd<float, true, false><<<grid, NTHR, 0, stream>>>(a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const Problem& p, const Work& w, int64_t row0, int64_t rows, hipStream_t stream,
-                        VSlice vs, const float* lse_in) {
-  if (vs.vn < 0) vs = VSlice{0, p.V};
-  const int64_t V_pad = (vs.vn + TILE - 1) / TILE * TILE, nseg = V_pad / kSeg;
-  const float* lse = lse_in ? lse_in + row0 : nullptr;
+hipError_t launch_rowref(const Problem& p, const void* hidden, const void* W, const Work& w, int64_t row0,
+                         int64_t rows, hipStream_t stream) {
+  const unsigned grid = (unsigned)((rows + 3) / 4);
   if (p.dtype == 0)
-    k_merge_dlogits<__bf16><<<(unsigned)rows, 256, (size_t)nseg * 4, stream>>>(
-        w.ws_e, w.seg_m, w.seg_s, (int)nseg, V_pad, w.y32 + row0, w.s_label + row0, w.og + row0, w.params,
-        w.loss_row + row0, lse, (int)vs.v0);
+    k_rowref<__bf16><<<grid, 256, 0, stream>>>((const __bf16*)hidden, p.hmap, row0, (int)rows, (int)p.H,
+                                               (const __bf16*)W, w.y32 + row0, p.softcap, w.cref + row0);
   else
-    k_merge_dlogits<float><<<(unsigned)rows, 256, (size_t)nseg * 4, stream>>>(
-        w.ws_e, w.seg_m, w.seg_s, (int)nseg, V_pad, w.y32 + row0, w.s_label + row0, w.og + row0, w.params,
-        w.loss_row + row0, lse, (int)vs.v0);
+    k_rowref<float><<<grid, 256, 0, stream>>>((const float*)hidden, p.hmap, row0, (int)rows, (int)p.H,
+                                              (const float*)W, w.y32 + row0, p.softcap, w.cref + row0);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse(const Problem& p, const Work& w, int64_t row0, int64_t rows, bool rescale_q,
+                      hipStream_t stream) {
+  void* q = rescale_q ? w.ws_e : nullptr;
+  if (p.dtype == 0)
+    k_lse<__bf16><<<(unsigned)rows, 256, 0, stream>>>(w.seg_m, w.seg_s, (int)p.nseg, w.y32 + row0, w.s_label + row0,
+                                                      w.loss_row + row0, w.lse + row0, w.cref + row0, q, p.V_pad);
+  else
+    k_lse<float><<<(unsigned)rows, 256, 0, stream>>>(w.seg_m, w.seg_s, (int)p.nseg, w.y32 + row0, w.s_label + row0,
+                                                     w.loss_row + row0, w.lse + row0, w.cref + row0, q, p.V_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowfix(const Problem& p, const void* hidden, const Work& w, int64_t row0, int64_t rows,
+                         hipStream_t stream, VSlice vs, int mode) {
+  if (vs.vn < 0) vs = VSlice{0, p.V};
+  const int64_t ldq = (vs.vn + TILE - 1) / TILE * TILE;
+  if (p.dtype == 0)
+    k_rowfix<__bf16><<<(unsigned)rows, 256, 0, stream>>>(
+        (const __bf16*)hidden, p.hmap, row0, (int)p.H, (__bf16*)w.xf, w.y32 + row0, w.s_label + row0, w.lse + row0,
+        w.cref + row0, w.params, p.softcap, w.fscale + row0, w.ws_e, ldq, (int)vs.v0, (int)vs.vn, mode);
+  else
+    k_rowfix<float><<<(unsigned)rows, 256, 0, stream>>>(
+        (const float*)hidden, p.hmap, row0, (int)p.H, (float*)w.xf, w.y32 + row0, w.s_label + row0, w.lse + row0,
+        w.cref + row0, w.params, p.softcap, w.fscale + row0, w.ws_e, ldq, (int)vs.v0, (int)vs.vn, mode);
   return hipGetLastError();
 }
 
@@ -1305,6 +1419,7 @@ hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_
   DxArgs a;
   a.W = (const char*)W + vs.v0 * p.H * (int64_t)esz;
   a.ws = w.ws_e;
+  a.fscale = w.fscale + row0;
   a.out = grad_hidden;
   a.gmap = p.gmap;
   a.row0 = row0;
@@ -1340,10 +1455,10 @@ hipError_t launch_dx_reduce(const Problem& p, const Work& w, void* grad_hidden, 
   const int acc = p.acc_gh ? 1 : 0;
   if (p.dtype == 0)
     k_dx_reduce<__bf16><<<grid, 256, 0, stream>>>(w.dx_part, splits, (int)rows, p.H, (__bf16*)grad_hidden, p.gmap,
-                                                  row0, acc);
+                                                  row0, acc, w.fscale + row0);
   else
     k_dx_reduce<float><<<grid, 256, 0, stream>>>(w.dx_part, splits, (int)rows, p.H, (float*)grad_hidden, p.gmap,
-                                                 row0, acc);
+                                                 row0, acc, w.fscale + row0);
   return hipGetLastError();
 }
 
@@ -1357,15 +1472,12 @@ hipError_t launch_zero_rows(const Problem& p, void* grad_hidden, int64_t B, int6
   return hipGetLastError();
 }
 
-hipError_t launch_dw(const Problem& p, const void* hidden, const Work& w, float* grad_W, int64_t row0,
-                     int64_t rows, bool accumulate, hipStream_t stream, VSlice vs) {
+hipError_t launch_dw(const Problem& p, const Work& w, float* grad_W, int64_t rows, bool accumulate,
+                     hipStream_t stream, VSlice vs) {
   if (vs.vn < 0) vs = VSlice{0, p.V};
   const int64_t V_pad = (vs.vn + TILE - 1) / TILE * TILE;
-  const size_t esz = p.dtype == 0 ? 2 : 4;
-  if (!p.hidden_dense && !w.xs) return hipErrorInvalidValue;
   DwArgs a;
-  // rows in the plain layout are read where they are; mapped rows from the chunk's gathered copy
-  a.X = p.hidden_dense ? (const void*)((const char*)hidden + row0 * p.H * esz) : (const void*)w.xs;
+  a.X = w.xf;  // f times the chunk's rows of hidden, [rows][H]
   a.ws = w.ws_e;
   a.dW = grad_W + vs.v0 * p.H;
   a.H = p.H;

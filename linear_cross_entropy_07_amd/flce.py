@@ -419,7 +419,8 @@ class FLCE:
         out = loss if reduction != "none" else per
         return (out, lse) if return_lse else out
 
-    KERNELS = ("prepass", "fwd", "merge", "dx", "dx_reduce", "dw", "finalize", "transpose", "rows", "zero")
+    KERNELS = ("prepass", "fwd", "lse", "dx", "dx_reduce", "dw", "finalize", "transpose", "rows", "zero",
+               "rowref", "rowfix")
 
     def profile_begin(self, max_launches: int = 4096):
         """Bracket every following kernel launch with HIP events on its stream (diagnostics)."""

@@ -131,3 +131,35 @@ def make_ragged_call(BT: int, seed: int, W_seed: int = 0):
 
 def with_bt(w: Workload, BT: int) -> Workload:
     return replace(w, BT=BT)
+
+
+def far_label_case(BT: int, H: int, V: int, dtype: str = "bf16", far: float = 60.0, near: float = 40.0,
+                   every: int = 5, ignore_frac: float = 0.05, seed: int = 0):
+    """Inputs where some rows' label logit lies far below the row's largest logit.
+
+    Two vocabulary rows a = 7 and b = V - 3 hold +alpha u and -alpha u for a random unit vector u. Hidden
+    rows 0, every, 2 every, ... are beta u plus small noise, with label b: their logit at a exceeds
+    their label logit by 2 alpha beta, which is `far` for every other planted row and `near` for the
+    rest. Other rows and weights are the usual Gaussian draws (W ~ N(0, 0.05^2)); round(ignore_frac *
+    BT) rows that are not planted are set to ignore_index."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((BT, H), dtype=np.float32)
+    W = (rng.standard_normal((V, H), dtype=np.float32) * np.float32(0.05)).astype(np.float32)
+    y = rng.integers(0, V, size=BT, dtype=np.int64)
+    u = rng.standard_normal(H).astype(np.float64)
+    u /= np.linalg.norm(u)
+    a, b, alpha = 7, V - 3, 4.0
+    W[a] = (alpha * u).astype(np.float32)
+    W[b] = (-alpha * u).astype(np.float32)
+    planted = np.arange(0, BT, every)
+    for k, r in enumerate(planted):
+        beta = (far if k % 2 == 0 else near) / (2.0 * alpha)
+        x[r] = (beta * u + 0.01 * rng.standard_normal(H)).astype(np.float32)
+        y[r] = b
+    others = np.setdiff1d(np.arange(BT), planted)
+    n_ign = min(int(round(ignore_frac * BT)), others.size)
+    if n_ign:
+        y[rng.permutation(others)[:n_ign]] = IGNORE_INDEX
+    return _to_dtype(x, dtype), _to_dtype(W, dtype), torch.from_numpy(y)

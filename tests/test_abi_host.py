@@ -146,10 +146,13 @@ def test_rows_workspace_size():
     # hidden rows already in the plain [BT][H] layout (B = 1, shift = 1): same as the plain call
     dense = _rows(B=1, T=8193, hs=(8193 * H, H), gs=(8193 * H, H), ls=(8193, 1))
     assert flce.workspace_size_rows(dense, H, V) == flce.workspace_size(8192, H, V)
-    # [8, 1025, H] with the shift: rows are not in the plain layout, one gathered chunk more
+    # [8, 1025, H] with the shift: rows are not in the plain layout; the grad_W operand is a scaled
+    # copy of the chunk's rows in every case, so the workspace is the same
     shifted = _rows(B=8, T=1025, hs=(1025 * H, H), gs=(1025 * H, H), ls=(1025, 1))
+    assert flce.workspace_size_rows(shifted, H, V) == flce.workspace_size(8192, H, V)
+    # the scaled copy of one chunk of hidden rows is part of every fused workspace
     n, c = flce.chunk_plan(8192)
-    assert flce.workspace_size_rows(shifted, H, V) == flce.workspace_size(8192, H, V) + c * H * 2
+    assert flce.workspace_size(8192, H, V) >= c * V * 2 + 2 * c * H * 2
     # no shift, contiguous [B, T, H]: plain again
     plain = _rows(B=8, T=1024, shift=0, hs=(1024 * H, H), gs=(1024 * H, H), ls=(1024, 1))
     assert flce.workspace_size_rows(plain, H, V) == flce.workspace_size(8192, H, V)
@@ -297,5 +300,9 @@ def test_static_entry_checks_before_touching_the_handle():
 
 def test_profile_kinds_match_the_header():
     text = open(build_lib.INCLUDE + "/flce.h").read()
-    assert "FLCE_K_ZERO = 9" in text and "FLCE_K_COUNT = 10" in text
-    assert len(flce.FLCE.KERNELS) == 10 and flce.FLCE.KERNELS[9] == "zero"
+    import re
+
+    kinds = {m.group(1).lower(): int(m.group(2)) for m in re.finditer(r"FLCE_K_(\w+) = (\d+)", text)}
+    count = kinds.pop("count")
+    assert count == len(flce.FLCE.KERNELS) == len(kinds)
+    assert all(flce.FLCE.KERNELS[v] == k for k, v in kinds.items())

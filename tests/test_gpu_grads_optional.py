@@ -37,7 +37,7 @@ def test_no_grad_loss_runs_the_forward_only(softcap):
         loss, cnt = _counts(e, lambda: flce.flce_loss(Xd, Wd, yd, softcap=softcap))
     torch.cuda.synchronize()
     print(f"   launches {cnt}", flush=True)
-    assert cnt["dx"] == 0 and cnt["dw"] == 0 and cnt["merge"] == 0 and cnt["fwd"] >= 1
+    assert cnt["dx"] == 0 and cnt["dw"] == 0 and cnt["rowfix"] == 0 and cnt["fwd"] >= 1
     assert not loss.requires_grad
     ol = oracle.flce_forward(X, W, y, -100, softcap, "mean")[0]
     assert abs(float(loss) - ol) <= TOL["bf16"]["loss"] * ol

@@ -243,3 +243,17 @@ def test_workspace_too_small_is_rejected():
     with pytest.raises(flce.FlceError) as ei:
         e.forward_backward(X, W, y, workspace=ws)
     assert ei.value.code == -3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("softcap,far,near,every", [(0.0, 60.0, 40.0, 5), (30.0, 120.0, 40.0, 5),
+                                                    (0.0, 70.0, 70.0, 1)])
+def test_label_far_below_the_row_maximum(dtype, softcap, far, near, every):
+    """Rows whose label logit lies more than the library's reference span (48) below their largest logit
+    (their stored softmax numerators are re-referenced to the row maximum after the statistics are
+    known), next to rows 40 below it (large numerators, no re-reference), in several chunks; with
+    every=1 all rows are of the first kind."""
+    X, W, y = inputs.far_label_case(700, 128, 3000, dtype, far=far, near=near, every=every, seed=11)
+    announce("label far below the row maximum", dtype, f"softcap={softcap} far={far} near={near} every={every}",
+             "chunk 256")
+    check_against_oracle(run_gpu(eng(256), X, W, y, softcap=softcap), X, W, y, dtype, softcap=softcap)

@@ -88,3 +88,18 @@ def test_llama_head_equals_fused_call():
     _, gh, _, d = _run_device(e, X, W, y, 0.0, "mean", 8192)
     assert torch.isfinite(gh.float()).all().item()
     assert d <= 5e-3
+
+
+@pytest.mark.parametrize("softcap,far", [(0.0, 60.0), (30.0, 120.0)])
+def test_label_far_below_the_row_maximum(softcap, far):
+    """Rows whose label logit lies more than the reference span below their maximum: the recompute mode
+    forms their numerators against the row maximum directly (the fused call rescales stored ones, so
+    the two agree to rounding here, not bitwise); against the oracle."""
+    e = eng(256)
+    dev = e.device
+    X, W, y = inputs.far_label_case(700, 128, 3000, "bf16", far=far, near=40.0, every=5, seed=12)
+    announce("recompute: label far below the row maximum", f"softcap={softcap}", "v_slice 1024, chunk 256")
+    rl, rgh, rgw = e.forward_backward_recompute(X.to(dev), W.to(dev), y.to(dev), -100, softcap, "mean", 1024)
+    torch.cuda.synchronize(dev)
+    got = (float(rl.cpu()), rgh.double().cpu().numpy(), rgw.double().cpu().numpy())
+    check_against_oracle(got, X, W, y, "bf16", softcap=softcap, reduction="mean")
