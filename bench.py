@@ -42,10 +42,11 @@ def parse():
                     help="rows of the oracle's bounded sample (0 = about 15 TFLOP of float64 work, at most the "
                          "whole call)")
     ap.add_argument("--profile-only", action="store_true", help="warmup + steps, no extras (for rocprofv3)")
-    ap.add_argument("--mode", choices=("fwd_bwd", "forward", "recompute"), default="fwd_bwd",
+    ap.add_argument("--mode", choices=("fwd_bwd", "forward", "recompute", "hipblaslt"), default="fwd_bwd",
                     help="fwd_bwd: the fused forward + backward (default); forward: flce_forward only; "
                          "recompute: flce_forward_backward_recompute (logits formed twice, one vocabulary "
-                         "slice kept)")
+                         "slice kept); hipblaslt: torch.matmul (hipBLASLt) alone at the three GEMM shapes of "
+                         "one chunk, for comparison (never part of the library)")
     ap.add_argument("--vslice", type=int, default=0, help="vocabulary slice of the recompute mode (0 = 8192)")
     ap.add_argument("--sequences", type=int, default=0,
                     help="B > 0: lay the BT rows out as B sequences of BT/B + 1 positions, hidden [B, T+1, H], "
@@ -124,6 +125,61 @@ def cpu_baseline(w, X, W, y, rows: int, forward_only: bool = False, BT: int | No
             "sample": f"first {rows} of {BT} rows of {w.name} (full H={w.H}, V={w.V}), fp64 numpy/OpenBLAS "
                       f"{'forward' if forward_only else 'forward+backward (flce_blocked, 1024-row blocks)'} "
                       f"incl. widening inputs to fp64; {dt:.2f} s on {blas_threads} BLAS threads"}
+
+
+def library_gemms(args, dev, w):
+    """torch.matmul (hipBLASLt, bf16 in and out, fp32 accumulation) at the three GEMM shapes of one
+    chunk of the workload, for comparison with the library's kernels under the same counters. The
+    logits product is W [V,H] . X^T [H,C] (the library's orientation, M = V); grad_hidden dZ [C,V] .
+    W [V,H]; grad_W dZ^T [V,C] . X [C,H]. Operands are random and contiguous (transposes made once,
+    outside the timed region)."""
+    import torch
+
+    from linear_cross_entropy_07_amd import flce
+
+    eng = flce.FLCE(dev, chunk_rows_max=args.chunk)
+    n, C = eng.chunk_plan(w.BT)
+    H, V = w.H, w.V
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    Wm = (torch.randn(V, H, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    X = torch.randn(C, H, device=dev, generator=g).to(torch.bfloat16)
+    dZ = (torch.randn(C, V, device=dev, generator=g) * 1e-4).to(torch.bfloat16)
+    Xt, dZt = X.t().contiguous(), dZ.t().contiguous()
+    prods = {"fwd": lambda: torch.matmul(Wm, Xt), "dx": lambda: torch.matmul(dZ, Wm),
+             "dw": lambda: torch.matmul(dZt, X)}
+    flops = 2.0 * C * H * V
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)  # the reference dispatch: reads and writes exactly 1 GiB
+        torch.cuda.synchronize(dev)
+        del src, dst
+    out = {}
+    for name, f in prods.items():
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize(dev)
+        if args.profile_only:
+            for _ in range(args.steps):
+                f()
+            torch.cuda.synchronize(dev)
+            continue
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            f()
+            b.record()
+        torch.cuda.synchronize(dev)
+        ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+        out[name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1), "frac": round(flops / ms * 1e3 / PEAK_BF16, 4)}
+    if args.profile_only:
+        print(f"# profiled {args.steps} calls of each product", file=sys.stderr, flush=True)
+        return
+    print(json.dumps({"metric": "torch.matmul (hipBLASLt) at the FLCE GEMM shapes of one chunk (comparison only)",
+                      "config": {"workload": w.name, "chunk_rows": C, "H": H, "V": V}, "steps": args.steps,
+                      "products": out}), flush=True)
 
 
 def ragged_sweep(args, dev):
@@ -212,6 +268,8 @@ def main():
     w = inputs.WORKLOADS[args.workload]
     if w.name == "ragged":
         return ragged_sweep(args, dev)
+    if args.mode == "hipblaslt":
+        return library_gemms(args, dev, w)
     print(f"# generating {w.name}: BT={w.BT} H={w.H} V={w.V} {w.dtype}", file=sys.stderr, flush=True)
     BT, H, V = w.BT, w.H, w.V
     nseq = args.sequences
