@@ -281,6 +281,8 @@ def main():
         X, W, y = inputs.make_inputs(w, seed=0)
     eng = flce.FLCE(dev, chunk_rows_max=args.chunk)
     n_chunks, chunk_rows = eng.chunk_plan(BT)
+    if args.mode == "recompute":  # one pass over all rows, vocabulary slices outermost
+        n_chunks, chunk_rows = 1, -(-BT // 256) * 256
 
     base_alloc = torch.cuda.memory_allocated(dev)
     Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)

@@ -123,19 +123,26 @@ int flce_forward_backward(flce_handle h,
                           float* loss, void* grad_hidden, float* grad_W,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* The recompute mode: the result of flce_forward_backward with less workspace and more work. The
- * PR #126348 description rebuilds the softmax in the backward pass from the softmax input and the
- * per-row max/sum; here the softmax input itself is rebuilt too. Per chunk of rows, a forward pass
- * over the whole vocabulary gives each row's log-sum-exp. Then, per vocabulary slice of v_slice
- * columns, the logits are computed again and turned into dZ against that lse. That dZ is used at
- * once for the slice's rows of grad_W and for an fp32 running sum of grad_hidden. The logits GEMM runs
- * twice: 8 * BT * H * V flop instead of 6. The workspace holds one [chunk_rows][v_slice] 16-bit slice
- * instead of a [chunk_rows][V] one.
+/* The recompute mode: the result of flce_forward_backward with no [rows][V] buffer and more work.
+ * The PR #126348 description rebuilds the softmax in the backward pass from the softmax input and
+ * the per-row max/sum; here the softmax input itself is rebuilt too. One pass covers all BT rows
+ * (the handle's chunk_rows_max does not apply): a forward pass over the whole vocabulary gives each
+ * row's log-sum-exp; then, per vocabulary slice of v_slice columns, outermost, the logits of all
+ * rows are computed again and turned into dZ against that lse. That dZ is used at once for the
+ * slice's rows of grad_W, written once, and for an fp32 [BT][H] running sum of grad_hidden. The
+ * logits GEMM runs twice: 8 * BT * H * V flop instead of 6. The workspace holds one [BT][v_slice]
+ * slice of dZ numerators (16-bit for bf16, fp32 for fp32), per-row statistics of 128-wide vocabulary
+ * segments ([BT][V/128], twice, fp32), the fp32 [BT][H] accumulator and two [BT][H] copies of hidden
+ * (transposed, and scaled per row) in the input dtype: linear in BT, independent of V but for the
+ * segment statistics.
  *   v_slice      vocabulary columns per slice: 0 = 8192; rounded up to a multiple of 256; at most V
  *                rounded up; negative is FLCE_ERR_INVALID_ARG
- * Everything else as for flce_forward_backward. The loss and grad_W are bitwise those of
- * flce_forward_backward on the same inputs and handle; grad_hidden differs only by the order of its
- * fp32 sums (one per slice, added in slice order). */
+ * Everything else as for flce_forward_backward. The loss is bitwise that of flce_forward_backward on
+ * the same inputs. grad_W is bitwise that of flce_forward_backward on a handle whose chunk plan puts
+ * all BT rows in one chunk, as long as no counted row's largest logit exceeds its label logit by more
+ * than 48 (such rows have their stored numerators rescaled by the fused call and formed against the
+ * final maximum here: the two agree to rounding). grad_hidden differs from the fused call's only by
+ * the order of its fp32 sums (one per slice, added in slice order). */
 int flce_recompute_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype,
                                   int64_t v_slice, size_t* bytes);
 int flce_forward_backward_recompute(flce_handle h,

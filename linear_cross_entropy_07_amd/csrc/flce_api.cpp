@@ -132,15 +132,17 @@ int64_t vslice_of(int64_t vs, int64_t V) {
   return vs < vmax ? vs : vmax;
 }
 
-// Workspace of the recompute mode. Per chunk of C rows: q of one vocabulary slice [C][slice], the
-// statistics of the whole vocabulary [C][V_pad/128] (pass 1), the fp32 grad_hidden accumulator
-// [C][H], hidden^T [H][C] and f times the chunk's hidden rows [C][H]; per row: label, label logit,
-// loss term, reference, lse and f. No buffer spans the whole vocabulary for more than its 128-wide
-// segment statistics.
-Layout layout_recompute(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int64_t vs) {
+// Rows of the recompute mode's single pass: all BT rows, rounded up to the row alignment.
+int64_t recompute_rows(int64_t BT) { return round_up(BT, flce::kRowAlign); }
+
+// Workspace of the recompute mode, whose one pass covers all R = recompute_rows(BT) rows: q of one
+// vocabulary slice [R][slice], the statistics of the whole vocabulary [R][V_pad/128] (pass 1), the
+// fp32 grad_hidden accumulator [R][H], hidden^T [H][R] and f times the hidden rows [R][H]; per row:
+// label, label logit, loss term, reference, lse and f. No buffer spans the whole vocabulary for more
+// than its 128-wide segment statistics.
+Layout layout_recompute(int64_t BT, int64_t H, int64_t V, int dtype, int64_t vs) {
   Layout L{};
-  int64_t n, rows;
-  plan(BT, cmax, &n, &rows);
+  const int64_t rows = recompute_rows(BT);
   const int64_t V_pad = round_up(V, flce::kTile);
   const int64_t nseg = V_pad / flce::kSeg;
   const size_t esz = dtype == 0 ? 2 : 4;
@@ -395,11 +397,12 @@ int run_fused(flce_ctx* h, int64_t cmax, const void* hidden, const void* W, cons
   return FLCE_OK;
 }
 
-// The recompute mode over the rows R (plain layout; sizes already checked). Per chunk: the forward
-// pass over the whole vocabulary gives each row's lse and maximum, hence its final reference and its
-// factor f; then per vocabulary slice the logits are formed again into q against that reference
-// (the label entry folded in when the label lies in the slice), and used at once for the slice's
-// grad_W rows and the chunk's fp32 grad_hidden sum, which is multiplied by f at the end.
+// The recompute mode over the rows R (plain layout; sizes already checked), vocabulary slices
+// outermost over all rows at once: the forward pass over the whole vocabulary gives each row's lse
+// and maximum, hence its final reference and its factor f; then per vocabulary slice the logits are
+// formed again into q against that reference (the label entry folded in when the label lies in the
+// slice) and used at once for the slice's grad_W rows, written once, and for the fp32 grad_hidden
+// sum over slices, which is multiplied by f at the end.
 int run_recompute(flce_ctx* h, const void* hidden, const void* W, const int64_t* labels, const Rows& R, int64_t H,
                   int64_t V, int dtype, int64_t ignore_index, float softcap, int reduction, int64_t v_slice,
                   float* loss, void* grad_hidden, float* grad_W, void* workspace, size_t workspace_bytes,
@@ -416,7 +419,7 @@ int run_recompute(flce_ctx* h, const void* hidden, const void* W, const int64_t*
   if (BT > 0 && (!aligned(hidden, 16) || !aligned(labels, 8) || !aligned(grad_hidden, 16)))
     return FLCE_ERR_INVALID_ARG;
   const int64_t vs = vslice_of(v_slice, V);
-  const Layout L = layout_recompute(BT, H, V, dtype, h->chunk_rows_max, vs);
+  const Layout L = layout_recompute(BT, H, V, dtype, vs);
   if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
 
   DeviceGuard g(h->device);
@@ -433,27 +436,22 @@ int run_recompute(flce_ctx* h, const void* hidden, const void* W, const int64_t*
     FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
     return FLCE_OK;
   }
-  int64_t n_chunks, crows;
-  plan(BT, h->chunk_rows_max, &n_chunks, &crows);
-  for (int64_t ci = 0; ci < n_chunks; ++ci) {
-    const int64_t row0 = ci * crows;
-    const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
-    FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
-    FLCE_LAUNCH(FLCE_K_ROWREF, flce::launch_rowref(p, hidden, W, w, row0, rows, stream));
-    // pass 1: row statistics over the whole vocabulary -> lse, the loss terms, the final references
-    FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, false, stream));
-    FLCE_LAUNCH(FLCE_K_LSE, flce::launch_lse(p, w, row0, rows, false, stream));
-    FLCE_LAUNCH(FLCE_K_ROWFIX, flce::launch_rowfix(p, hidden, w, row0, rows, stream, flce::VSlice{}, 1));
-    // pass 2: per vocabulary slice
-    for (int64_t v0 = 0, si = 0; v0 < V; v0 += vs, ++si) {
-      const flce::VSlice sl{v0, (V - v0) < vs ? (V - v0) : vs};
-      FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, true, stream, sl, true));
-      FLCE_LAUNCH(FLCE_K_ROWFIX, flce::launch_rowfix(p, hidden, w, row0, rows, stream, sl, 2));
-      FLCE_LAUNCH(FLCE_K_DX, flce::launch_dx(p, W, w, grad_hidden, row0, rows, 1, stream, sl, si == 0 ? 1 : 2));
-      FLCE_LAUNCH(FLCE_K_DW, flce::launch_dw(p, w, grad_W, rows, ci > 0, stream, sl));
-    }
-    FLCE_LAUNCH(FLCE_K_DX_REDUCE, flce::launch_dx_reduce(p, w, grad_hidden, row0, rows, 1, stream));
+  const int64_t row0 = 0, rows = BT;
+  FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
+  FLCE_LAUNCH(FLCE_K_ROWREF, flce::launch_rowref(p, hidden, W, w, row0, rows, stream));
+  // pass 1: row statistics over the whole vocabulary -> lse, the loss terms, the final references
+  FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, false, stream));
+  FLCE_LAUNCH(FLCE_K_LSE, flce::launch_lse(p, w, row0, rows, false, stream));
+  FLCE_LAUNCH(FLCE_K_ROWFIX, flce::launch_rowfix(p, hidden, w, row0, rows, stream, flce::VSlice{}, 1));
+  // pass 2: per vocabulary slice over all rows
+  for (int64_t v0 = 0, si = 0; v0 < V; v0 += vs, ++si) {
+    const flce::VSlice sl{v0, (V - v0) < vs ? (V - v0) : vs};
+    FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, true, stream, sl, true));
+    FLCE_LAUNCH(FLCE_K_ROWFIX, flce::launch_rowfix(p, hidden, w, row0, rows, stream, sl, 2));
+    FLCE_LAUNCH(FLCE_K_DX, flce::launch_dx(p, W, w, grad_hidden, row0, rows, 1, stream, sl, si == 0 ? 1 : 2));
+    FLCE_LAUNCH(FLCE_K_DW, flce::launch_dw(p, w, grad_W, rows, false, stream, sl));
   }
+  FLCE_LAUNCH(FLCE_K_DX_REDUCE, flce::launch_dx_reduce(p, w, grad_hidden, row0, rows, 1, stream));
   FLCE_LAUNCH(FLCE_K_FINALIZE, flce::launch_finalize(p, w, loss, stream));
   return FLCE_OK;
 }
@@ -626,7 +624,7 @@ int flce_recompute_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t 
   if (!bytes || v_slice < 0) return FLCE_ERR_INVALID_ARG;
   const int rc = check_sizes(BT, H, V, dtype);
   if (rc != FLCE_OK) return rc;
-  *bytes = layout_recompute(BT, H, V, dtype, chunk_max_of(h), vslice_of(v_slice, V)).total;
+  *bytes = layout_recompute(BT, H, V, dtype, vslice_of(v_slice, V)).total;
   return FLCE_OK;
 }
 

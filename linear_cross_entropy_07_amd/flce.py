@@ -267,8 +267,9 @@ class FLCE:
     def forward_backward_recompute(self, hidden: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
                                    ignore_index: int = -100, softcap: float = 0.0, reduction: str = "mean",
                                    v_slice: int = 0, out=None, workspace: torch.Tensor | None = None, stream=None):
-        """The recompute mode (logits formed twice, one vocabulary slice of 16-bit values kept at a
-        time); returns (loss, grad_hidden, grad_W fp32) like forward_backward."""
+        """The recompute mode (logits formed twice; vocabulary slices outermost over all rows, one
+        slice of dZ numerators kept at a time); returns (loss, grad_hidden, grad_W fp32) like
+        forward_backward."""
         BT, H, V = self._check_inputs(hidden, W, labels)
         if reduction not in _REDUCTIONS:
             raise ValueError("reduction must be 'mean' or 'sum'")

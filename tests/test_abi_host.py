@@ -249,8 +249,8 @@ def test_recompute_workspace_size_keeps_a_vocabulary_slice():
     ws = {vs: flce.recompute_workspace_size(8192, H, V, v_slice=vs) for vs in (0, 1024, 4096, 8192, 16384)}
     assert ws[0] == ws[8192]                      # 0 selects 8192 columns
     assert ws[1024] < ws[4096] < ws[8192] < ws[16384] < full
-    # one 16-bit [4096][slice] buffer instead of [4096][V]: the slice difference is exactly that
-    assert ws[16384] - ws[8192] == 4096 * 8192 * 2
+    # one 16-bit [BT][slice] buffer over all rows: the slice difference is exactly that
+    assert ws[16384] - ws[8192] == 8192 * 8192 * 2
     # a slice wider than V is capped at V rounded up to the tile width
     assert flce.recompute_workspace_size(300, 128, 1000, v_slice=1 << 20) == \
         flce.recompute_workspace_size(300, 128, 1000, v_slice=1024)
