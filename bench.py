@@ -138,8 +138,8 @@ def library_gemms(args, dev, w):
     from linear_cross_entropy_07_amd import flce
 
     eng = flce.FLCE(dev, chunk_rows_max=args.chunk)
-    n, C = eng.chunk_plan(w.BT)
     H, V = w.H, w.V
+    n, C = eng.chunk_plan(w.BT, H, V)
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     Wm = (torch.randn(V, H, device=dev, generator=g) * 0.02).to(torch.bfloat16)
@@ -280,7 +280,7 @@ def main():
     else:
         X, W, y = inputs.make_inputs(w, seed=0)
     eng = flce.FLCE(dev, chunk_rows_max=args.chunk)
-    n_chunks, chunk_rows = eng.chunk_plan(BT)
+    n_chunks, chunk_rows = eng.chunk_plan(BT, H, V, X.dtype)
     if args.mode == "recompute":  # one pass over all rows, vocabulary slices outermost
         n_chunks, chunk_rows = 1, -(-BT // 256) * 256
 

@@ -23,7 +23,7 @@
  * GEMMs read it as it is and apply the per-row normalisation by linearity, so dlogits are never
  * written. No [BT, V] buffer is allocated by the library or required of the caller.
  * B*T may be any value (ragged batches, as in the benchmark comment of Liger-Kernel issue #227): the
- * library splits the rows into balanced chunks of at most chunk_rows_max rows with one code object.
+ * library splits the rows into balanced chunks (flce_chunk_plan) with one code object.
  *
  * Conventions for every entry point:
  *   - Pointers named "device" are HIP device pointers on the handle's device; "host" pointers are
@@ -71,7 +71,8 @@ enum {
 
 /* Configuration passed to flce_create; a NULL pointer or zero fields select the defaults. */
 typedef struct {
-  int64_t chunk_rows_max; /* rows per chunk (0 = 4096); rounded up to a multiple of 256 */
+  int64_t chunk_rows_max; /* row cap of a chunk (0 = automatic, see flce_chunk_plan); rounded up to a
+                           * multiple of 256 */
   int64_t reserved[3];    /* must be zero */
 } flce_config;
 
@@ -94,10 +95,17 @@ int flce_destroy(flce_handle h);
  * Returns FLCE_OK and writes *bytes, or FLCE_ERR_INVALID_ARG. */
 int flce_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, size_t* bytes);
 
-/* Chunk plan for BT rows (host-only): n = ceil(BT / chunk_rows_max) chunks of chunk_rows rows
- * (a multiple of 256, at most chunk_rows_max), the last one holding BT - (n-1)*chunk_rows rows.
- * h may be NULL. Returns FLCE_OK or FLCE_ERR_INVALID_ARG. */
-int flce_chunk_plan(flce_handle h, int64_t BT, int64_t* n_chunks, int64_t* chunk_rows);
+/* Chunk plan for BT rows of a problem with hidden size H, vocabulary V and dtype (host-only):
+ * n = ceil(BT / cap) chunks of chunk_rows rows (a multiple of 256, at most cap), the last one holding
+ * BT - (n-1)*chunk_rows rows. cap is the handle's chunk_rows_max if configured; otherwise (also for
+ * h == NULL) it is automatic: max(4096, min(2^24 / H rounded up to 256, the largest multiple of 256
+ * whose [rows][V rounded up to 256] buffer of the dtype fits 2 GiB)). The 2^24 / H term gives one
+ * chunk's grad_hidden product (rows x H) at least 256 output tiles of 256 x 256, one per compute unit,
+ * for narrow hidden sizes (H = 768: 16384-row chunks at BT = 32768). Every entry point that chunks
+ * rows follows this plan. Returns FLCE_OK, FLCE_ERR_INVALID_ARG (NULL outputs, BT < 0, H or V <= 0,
+ * bad dtype) or FLCE_ERR_UNSUPPORTED for sizes the library rejects. */
+int flce_chunk_plan(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, int64_t* n_chunks,
+                    int64_t* chunk_rows);
 
 /* The fused forward + backward.
  *   hidden       device, [BT][H] of dtype          (read)
@@ -267,7 +275,7 @@ int flce_profile_end(flce_handle h, void* stream, double* ms_out, int64_t* count
  * its address on the handle's device. The call allocates nothing (no hipMalloc, no allocating
  * library routine) and, like flce_forward_backward, never synchronises.
  *   Arguments as for flce_forward_backward, without workspace and workspace_bytes.
- *   Chunk plan: the largest chunk_rows_max' <= the handle's chunk_rows_max, a multiple of 256, for
+ *   Chunk plan: the largest chunk_rows_max' <= the handle's row cap (flce_chunk_plan), a multiple of 256, for
  *   which flce_workspace_size (with chunk_rows_max') fits FLCE_STATIC_SCRATCH_BYTES; the result is
  *   bitwise that of flce_forward_backward on a handle configured with chunk_rows_max'.
  *   Sizes whose workspace exceeds the scratch even with 256-row chunks (e.g. V above ~2^19, or a very

@@ -34,6 +34,8 @@ struct flce_ctx {
 namespace {
 
 constexpr int64_t kDefaultChunk = 4096;
+constexpr int64_t kAutoChunkWork = int64_t(1) << 24;   // rows x H: 256 tiles of 256 x 256 in grad_hidden
+constexpr int64_t kAutoChunkBytes = int64_t(1) << 31;  // [rows][V] buffer bound for chunks above the default
 constexpr int kDefaultCUs = 256;  // MI355X, for workspace sizes asked without a handle
 constexpr int64_t kMaxH = 1 << 16;
 constexpr int64_t kMaxV = int64_t(1) << 20;  // keeps every per-tile buffer range below 2 GiB
@@ -41,8 +43,17 @@ constexpr int64_t kMaxBT = (int64_t(1) << 31) - 1;
 
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
-int64_t chunk_max_of(const flce_ctx* h) {
-  return h ? h->chunk_rows_max : kDefaultChunk;
+// Row cap of the chunk plan: the handle's, if one was configured. Otherwise at least 4096 rows, and
+// more for a narrow hidden size: enough that one chunk's grad_hidden product [rows][H] has 256 tiles
+// of 256 x 256 (one per CU of the chip) without splitting the vocabulary, as long as the chunk's
+// [rows][V] buffer stays within 2 GiB.
+int64_t chunk_cap(const flce_ctx* h, int64_t H, int64_t V, int dtype) {
+  if (h && h->chunk_rows_max > 0) return h->chunk_rows_max;
+  const int64_t esz = dtype == 0 ? 2 : 4;
+  const int64_t by_work = round_up((kAutoChunkWork + H - 1) / H, flce::kRowAlign);
+  const int64_t by_mem = kAutoChunkBytes / (round_up(V, flce::kTile) * esz) / flce::kRowAlign * flce::kRowAlign;
+  const int64_t c = by_work < by_mem ? by_work : by_mem;
+  return c > kDefaultChunk ? c : kDefaultChunk;
 }
 int ncu_of(const flce_ctx* h) {
   return h ? h->ncu : kDefaultCUs;
@@ -353,7 +364,7 @@ int run_fused(flce_ctx* h, int64_t cmax, const void* hidden, const void* W, cons
     return FLCE_ERR_INVALID_ARG;
   if (BT > 0 && (!aligned(hidden, 16) || !aligned(labels, 8))) return FLCE_ERR_INVALID_ARG;
   if (gh_rows && !aligned(grad_hidden, 16)) return FLCE_ERR_INVALID_ARG;
-  if (cmax <= 0) cmax = h->chunk_rows_max;  // 0: the handle's chunk cap
+  if (cmax <= 0) cmax = chunk_cap(h, H, V, dtype);  // 0: the handle's chunk cap
   const Layout L = layout(BT, H, V, dtype, cmax, h->ncu, true);
   if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
 
@@ -470,7 +481,8 @@ int run_forward(flce_ctx* h, const void* hidden, const void* W, const int64_t* l
       !aligned(lse_rows, 4))
     return FLCE_ERR_INVALID_ARG;
   if (BT > 0 && (!aligned(hidden, 16) || !aligned(labels, 8))) return FLCE_ERR_INVALID_ARG;
-  const Layout L = layout(BT, H, V, dtype, h->chunk_rows_max, h->ncu, false);
+  const int64_t cmax = chunk_cap(h, H, V, dtype);
+  const Layout L = layout(BT, H, V, dtype, cmax, h->ncu, false);
   if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
 
   DeviceGuard g(h->device);
@@ -484,7 +496,7 @@ int run_forward(flce_ctx* h, const void* hidden, const void* W, const int64_t* l
 
   FLCE_LAUNCH(FLCE_K_PREPASS, flce::launch_prepass(p, labels, w, h->d_status, stream));
   int64_t n_chunks, crows;
-  plan(BT, h->chunk_rows_max, &n_chunks, &crows);
+  plan(BT, cmax, &n_chunks, &crows);
   for (int64_t ci = 0; ci < n_chunks && BT > 0; ++ci) {
     const int64_t row0 = ci * crows;
     const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
@@ -504,7 +516,7 @@ extern "C" {
 int flce_create(flce_handle* out, int device, const flce_config* cfg) {
   if (!out) return FLCE_ERR_INVALID_ARG;
   *out = nullptr;
-  int64_t cmax = kDefaultChunk;
+  int64_t cmax = 0;  // automatic (chunk_cap)
   if (cfg) {
     for (int i = 0; i < 3; ++i)
       if (cfg->reserved[i] != 0) return FLCE_ERR_INVALID_ARG;
@@ -553,13 +565,16 @@ int flce_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dty
   if (!bytes) return FLCE_ERR_INVALID_ARG;
   const int rc = check_sizes(BT, H, V, dtype);
   if (rc != FLCE_OK) return rc;
-  *bytes = layout(BT, H, V, dtype, chunk_max_of(h), ncu_of(h)).total;
+  *bytes = layout(BT, H, V, dtype, chunk_cap(h, H, V, dtype), ncu_of(h)).total;
   return FLCE_OK;
 }
 
-int flce_chunk_plan(flce_handle h, int64_t BT, int64_t* n_chunks, int64_t* chunk_rows) {
-  if (!n_chunks || !chunk_rows || BT < 0) return FLCE_ERR_INVALID_ARG;
-  plan(BT, chunk_max_of(h), n_chunks, chunk_rows);
+int flce_chunk_plan(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, int64_t* n_chunks,
+                    int64_t* chunk_rows) {
+  if (!n_chunks || !chunk_rows) return FLCE_ERR_INVALID_ARG;
+  const int rc = check_sizes(BT, H, V, dtype);
+  if (rc != FLCE_OK) return rc;
+  plan(BT, chunk_cap(h, H, V, dtype), n_chunks, chunk_rows);
   return FLCE_OK;
 }
 
@@ -582,8 +597,8 @@ int flce_forward_backward_static(flce_handle h, const void* hidden, const void* 
   const int rc = check_sizes(BT, H, V, dtype);
   if (rc != FLCE_OK) return rc;
   if (!h->scratch) return FLCE_ERR_HIP;
-  // the largest chunk (a multiple of 256 rows, at most the handle's) whose workspace fits the scratch
-  int64_t cmax = h->chunk_rows_max;
+  // the largest chunk (a multiple of 256 rows, at most the handle's cap) whose workspace fits the scratch
+  int64_t cmax = chunk_cap(h, H, V, dtype);
   while (cmax >= flce::kRowAlign && layout(BT, H, V, dtype, cmax, h->ncu).total > flce::kScratchBytes)
     cmax -= flce::kRowAlign;
   if (cmax < flce::kRowAlign) return FLCE_ERR_WORKSPACE_TOO_SMALL;
@@ -598,7 +613,7 @@ int flce_workspace_size_rows(flce_handle h, const flce_rows* rows, int64_t H, in
   int rc = check_rows(rows, H, dtype, true, &R);
   if (rc == FLCE_OK) rc = check_sizes(R.BT, H, V, dtype);
   if (rc != FLCE_OK) return rc;
-  *bytes = layout(R.BT, H, V, dtype, chunk_max_of(h), ncu_of(h), true).total;
+  *bytes = layout(R.BT, H, V, dtype, chunk_cap(h, H, V, dtype), ncu_of(h), true).total;
   return FLCE_OK;
 }
 
@@ -643,7 +658,7 @@ int flce_forward_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V,
   if (!bytes) return FLCE_ERR_INVALID_ARG;
   const int rc = check_sizes(BT, H, V, dtype);
   if (rc != FLCE_OK) return rc;
-  *bytes = layout(BT, H, V, dtype, chunk_max_of(h), ncu_of(h), false).total;
+  *bytes = layout(BT, H, V, dtype, chunk_cap(h, H, V, dtype), ncu_of(h), false).total;
   return FLCE_OK;
 }
 

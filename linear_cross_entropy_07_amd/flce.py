@@ -72,7 +72,7 @@ def lib() -> ctypes.CDLL:
             L.flce_create.argtypes = [ctypes.POINTER(vp), i32, ctypes.POINTER(_Config)]
             L.flce_destroy.argtypes = [vp]
             L.flce_workspace_size.argtypes = [vp, i64, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
-            L.flce_chunk_plan.argtypes = [vp, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+            L.flce_chunk_plan.argtypes = [vp, i64, i64, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
             L.flce_forward_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, ctypes.c_float,
                                                 i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
             L.flce_forward_workspace_size.argtypes = [vp, i64, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
@@ -137,9 +137,11 @@ def workspace_size_rows(rows: Rows, H: int, V: int, dtype=torch.bfloat16, handle
     return out.value
 
 
-def chunk_plan(BT: int, handle=None):
+def chunk_plan(BT: int, H: int, V: int, dtype=torch.bfloat16, handle=None):
+    """(number of chunks, rows per chunk) of the library's row plan for this problem."""
     n, c = ctypes.c_int64(), ctypes.c_int64()
-    _check(lib().flce_chunk_plan(handle, BT, ctypes.byref(n), ctypes.byref(c)), "flce_chunk_plan")
+    _check(lib().flce_chunk_plan(handle, BT, H, V, _DTYPES[dtype], ctypes.byref(n), ctypes.byref(c)),
+           "flce_chunk_plan")
     return n.value, c.value
 
 
@@ -177,8 +179,8 @@ class FLCE:
     def workspace_size(self, BT, H, V, dtype=torch.bfloat16) -> int:
         return workspace_size(BT, H, V, dtype, self._h)
 
-    def chunk_plan(self, BT):
-        return chunk_plan(BT, self._h)
+    def chunk_plan(self, BT, H, V, dtype=torch.bfloat16):
+        return chunk_plan(BT, H, V, dtype, self._h)
 
     def _stream(self, stream, tensors):
         """The stream a call enqueues on. Another stream than the current one first waits for the

@@ -30,8 +30,9 @@ def test_error_strings():
     (0, (0, 0)), (1, (1, 256)), (256, (1, 256)), (4096, (1, 4096)), (4097, (2, 2304)),
     (8192, (2, 4096)), (33768, (9, 3840)), (32768, (8, 4096)), (12345, (4, 3328))])
 def test_chunk_plan_default(BT, expect):
-    """Balanced plan with the default 4096-row cap: n = ceil(BT / 4096) chunks of a multiple of 256 rows."""
-    n, c = flce.chunk_plan(BT)
+    """Balanced plan with the automatic cap at the Llama-3-8B head (H = 4096: 4096 rows): n = ceil(BT /
+    4096) chunks of a multiple of 256 rows."""
+    n, c = flce.chunk_plan(BT, 4096, 128256)
     assert (n, c) == expect
     if BT:
         assert (n - 1) * c < BT <= n * c and c % 256 == 0 and c <= 4096
@@ -41,7 +42,7 @@ def test_chunk_plan_ragged_sweep_covers_rows():
     from linear_cross_entropy_07_amd import inputs
 
     for bt in inputs.ragged_bt_list(0, 20):
-        n, c = flce.chunk_plan(bt)
+        n, c = flce.chunk_plan(bt, 4096, 128256)
         assert (n - 1) * c < bt <= n * c
 
 
@@ -151,7 +152,7 @@ def test_rows_workspace_size():
     shifted = _rows(B=8, T=1025, hs=(1025 * H, H), gs=(1025 * H, H), ls=(1025, 1))
     assert flce.workspace_size_rows(shifted, H, V) == flce.workspace_size(8192, H, V)
     # the scaled copy of one chunk of hidden rows is part of every fused workspace
-    n, c = flce.chunk_plan(8192)
+    n, c = flce.chunk_plan(8192, H, V)
     assert flce.workspace_size(8192, H, V) >= c * V * 2 + 2 * c * H * 2
     # no shift, contiguous [B, T, H]: plain again
     plain = _rows(B=8, T=1024, shift=0, hs=(1024 * H, H), gs=(1024 * H, H), ls=(1024, 1))
@@ -232,15 +233,49 @@ def test_header_compiles_as_c_and_cpp(tmp_path, compiler, std):
 
 def test_chunk_plan_invariants_random_bt():
     """For any B*T up to 2^31 - 1: n chunks of C rows cover it with a non-empty last chunk, C is a
-    multiple of 256 and at most the 4096-row default, and n is the fewest chunks of that size."""
+    multiple of 256 and at most the automatic cap (4096 rows at H = 4096), and n is the fewest chunks
+    of that size."""
     import numpy as np
 
     rng = np.random.default_rng(5)
     for bt in [1, 255, 256, 257, 4095, 4096, 4097, 2**31 - 1] + rng.integers(1, 2**31 - 1, size=200).tolist():
-        n, c = flce.chunk_plan(int(bt))
+        n, c = flce.chunk_plan(int(bt), 4096, 128256)
         assert c % 256 == 0 and 0 < c <= 4096
         assert (n - 1) * c < bt <= n * c
         assert n == -(-bt // 4096)
+
+
+@pytest.mark.parametrize("H,V,dtype,cap", [
+    (4096, 128256, "bf16", 4096),     # Llama-3-8B head: 2^24 / H = 4096
+    (3584, 256000, "bf16", 4096),     # Gemma2 head: 4864 by the work rule, 4096 by the 2 GiB bound
+    (768, 50257, "bf16", 21248),      # GPT-2 head: 22016 by the work rule, 21248 by the 2 GiB bound
+    (768, 50257, "fp32", 10496),      # fp32 buffer: the 2 GiB bound halves
+    (2048, 32000, "bf16", 8192),      # 2^24 / 2048 = 8192, 32000 columns stay far under 2 GiB
+    (64, 1000, "bf16", 262144),       # narrow and small: the work rule alone
+    (64, 1 << 20, "fp32", 4096),      # the 4096-row floor wins over the 2 GiB bound
+])
+def test_chunk_plan_automatic_cap(H, V, dtype, cap):
+    """The automatic row cap max(4096, min(ceil(2^24 / H) rounded up to 256, the largest multiple of 256
+    whose [rows][V_pad] buffer fits 2 GiB)), seen through the plan of a B*T far above it."""
+    import torch
+
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    esz = 2 if dtype == "bf16" else 4
+    vpad = -(-V // 256) * 256
+    by_work = -(-(1 << 24) // H)
+    by_work = -(-by_work // 256) * 256
+    by_mem = (1 << 31) // (vpad * esz) // 256 * 256
+    assert max(4096, min(by_work, by_mem)) == cap
+    bt = 1 << 30
+    n, c = flce.chunk_plan(bt, H, V, dt)
+    assert n == -(-bt // cap) and c <= cap and (n - 1) * c < bt <= n * c
+    # the GPT-2 head at B*T = 32768 runs in two chunks of 16384 rows
+    assert flce.chunk_plan(32768, 768, 50257) == (2, 16384)
+    # invalid sizes are rejected
+    with pytest.raises(flce.FlceError):
+        flce.chunk_plan(100, 0, 1000)
+    with pytest.raises(flce.FlceError):
+        flce.chunk_plan(-1, 64, 1000)
 
 
 def test_recompute_workspace_size_keeps_a_vocabulary_slice():

@@ -33,7 +33,7 @@ def _fullsize_check(X, W, y, softcap, label):
     e = flce.FLCE(dev)
     BT, H = X.shape
     V = W.shape[0]
-    announce(label, f"BT={BT} H={H} V={V} softcap={softcap} chunks={e.chunk_plan(BT)}")
+    announce(label, f"BT={BT} H={H} V={V} softcap={softcap} chunks={e.chunk_plan(BT, H, V)}")
     Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
     loss, gh, gw = e.forward_backward(Xd, Wd, yd, softcap=softcap)
     torch.cuda.synchronize()

@@ -30,7 +30,7 @@ def _run_device(e, X, W, y, softcap, reduction, v_slice):
     rl, rgh, rgw = e.forward_backward_recompute(Xd, Wd, yd, -100, softcap, reduction, v_slice)
     fl = e.forward_backward(Xd, Wd, yd, -100, softcap, reduction)[0].clone()
     one = eng(max(256, X.shape[0]))
-    assert one.chunk_plan(X.shape[0])[0] == 1
+    assert one.chunk_plan(X.shape[0], X.shape[1], W.shape[0], X.dtype)[0] == 1
     fl1, fgh, fgw = one.forward_backward(Xd, Wd, yd, -100, softcap, reduction)
     torch.cuda.synchronize(dev)
     assert torch.equal(rl, fl), (float(rl), float(fl))
