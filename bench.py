@@ -53,7 +53,50 @@ def parse():
                          "with the next-token label shift done by the library (the *_rows entry points)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for the FETCH_SIZE/WRITE_SIZE scale)")
+    ap.add_argument("--no-peak-calib", action="store_true",
+                    help="skip the measured ceilings (MFMA-only loop, device copy) reported beside the result")
     return ap.parse_args()
+
+
+def measured_peaks(dev) -> dict:
+    """The ceilings this GPU sustains, from libflce_calib.so (after the timed steps): an MFMA-only loop
+    (1024 blocks of 8 waves, 8 independent v_mfma_f32_32x32x16_bf16 chains per wave on random bf16
+    operands that change from one MFMA to the next, 65536 iterations; best of 3 launches) and a 1 GiB
+    device-to-device copy (best of 5). The loop's exactness on +-2^-10 operands (twice the iterations,
+    exactly twice the output) and the copy's destination are checked."""
+    import ctypes
+
+    from linear_cross_entropy_07_amd import build_lib
+
+    L = ctypes.CDLL(build_lib.CALIB_LIB)
+    d = ctypes.c_double
+    L.flce_calib_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint,
+                                       ctypes.c_int, ctypes.POINTER(d), ctypes.POINTER(d), ctypes.POINTER(d)]
+    L.flce_calib_copy.argtypes = [ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(d),
+                                  ctypes.POINTER(d), ctypes.POINTER(ctypes.c_int)]
+
+    def mfma(blocks, iters, reps, full_random):
+        tf, ms, chk = d(), d(), d()
+        rc = L.flce_calib_mfma_bf16(dev.index, blocks, iters, reps, 1, full_random, ctypes.byref(tf),
+                                    ctypes.byref(ms), ctypes.byref(chk))
+        if rc != 0:
+            raise SystemExit(f"MFMA calibration failed (rc {rc})")
+        return tf.value, ms.value, chk.value
+
+    blocks, iters = 1024, 65536  # ~80 ms per launch: the sustained rate (shorter runs read ~2% higher)
+    a, b = mfma(1, 64, 1, 0)[2], mfma(1, 128, 1, 0)[2]
+    if a == 0.0 or b != 2.0 * a:
+        raise SystemExit(f"MFMA calibration not exact ({a}, {b})")
+    tf, ms, _ = mfma(blocks, iters, 3, 1)
+    gbs, cms, ok = d(), d(), ctypes.c_int()
+    rc = L.flce_calib_copy(dev.index, 1 << 30, 5, ctypes.byref(gbs), ctypes.byref(cms), ctypes.byref(ok))
+    if rc != 0 or ok.value != 1:
+        raise SystemExit(f"copy calibration failed (rc {rc}, ok {ok.value})")
+    return {"mfma_bf16_tflops": round(tf, 1), "mfma_loop_ms": round(ms, 3),
+            "copy_gbs": round(gbs.value, 1), "copy_ms": round(cms.value, 3),
+            "how": f"MFMA-only loop: {blocks} blocks x 8 waves x {iters} iterations x 8 chains of "
+                   "v_mfma_f32_32x32x16_bf16 on random bf16 operands changing per MFMA, best of 3; copy: "
+                   "1 GiB device to device, (read + write) / time, best of 5"}
 
 
 def kernel_source_hash() -> str:
@@ -419,6 +462,11 @@ def main():
                                  if not (nseq or recompute) else None),
                      "flops_per_launch": flops_per_launch},
     }
+    if not args.no_peak_calib:
+        mp = measured_peaks(dev)
+        out["measured_peaks"] = mp
+        out["mfma_frac_step_of_measured"] = round(step_flops / (ms_med * 1e-3) / (mp["mfma_bf16_tflops"] * 1e12), 4)
+        out["roofline"]["frac_of_measured_peak"] = round(achieved / (mp["mfma_bf16_tflops"] * 1e12), 4)
     if not args.no_cpu_baseline:
         rows = cpu_rows_for(BT, H, V, fwd_only, args.cpu_rows)
         Xc, yc = X, y

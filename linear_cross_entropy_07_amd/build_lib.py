@@ -41,6 +41,22 @@ def build(verbose: bool = False) -> str:
     return DEFAULT_LIB
 
 
+CALIB_LIB = os.path.join(PKG, "libflce_calib.so")
+
+
+def build_calib(verbose: bool = False) -> str:
+    """Compile the benchmark's peak-calibration library (MFMA-only loop, device copy) for gfx950."""
+    tmp = CALIB_LIB + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", INCLUDE, os.path.join(CSRC, "flce_calib.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-8000:]}")
+    os.replace(tmp, CALIB_LIB)
+    return CALIB_LIB
+
+
 EXAMPLE_SRC = os.path.join(PKG, "examples", "flce_from_c.c")
 EXAMPLE_BIN = os.path.join(PKG, "examples", "flce_from_c")
 

@@ -21,6 +21,21 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+def test_calibration_library_exports_its_header():
+    """libflce_calib.so (the benchmark's measured ceilings) exports what include/flce_calib.h declares."""
+    import os
+    import re
+
+    if not os.path.exists(build_lib.CALIB_LIB):
+        build_lib.build_calib()
+    text = open(os.path.join(build_lib.INCLUDE, "flce_calib.h")).read()
+    names = sorted(set(re.findall(r"^\s*\w+\s+(flce_calib_\w+)\s*\(", text, re.M)))
+    assert names == ["flce_calib_copy", "flce_calib_mfma_bf16"]
+    C = ctypes.CDLL(build_lib.CALIB_LIB)
+    for n in names:
+        assert hasattr(C, n), n
+
+
 def test_error_strings():
     for code in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(L.flce_error_string(code), bytes)

@@ -41,6 +41,10 @@ def test_bench_modes_print_the_contract_line(args):
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
     assert 0.0 < r["frac"] < 1.0 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert d["peak_bytes"]["workspace"] < d["peak_bytes"]["full_bf16_logits_not_allocated"]
+    mp = d["measured_peaks"]
+    assert 1000.0 < mp["mfma_bf16_tflops"] <= 2525.0 and 1000.0 < mp["copy_gbs"] <= 8080.0
+    assert abs(r["frac_of_measured_peak"] - r["achieved"] / mp["mfma_bf16_tflops"]) < 1e-3
+    assert 0.0 < d["mfma_frac_step_of_measured"] < 1.0
     if "--no-cpu-baseline" not in args:
         c = d["cpu_baseline"]
         assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and "256" in c["sample"]
