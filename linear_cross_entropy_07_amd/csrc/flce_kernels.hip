@@ -26,10 +26,11 @@
 // f enters by linearity (an output-row scale for grad_hidden, a scaled copy of the chunk's hidden
 // rows for grad_W).
 //
-// One GEMM core serves the three products: 256 threads (4 waves of 64) compute a 256 x 256 tile,
-// each wave a 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (or 32x32x2f32 for
-// fp32 inputs). Operands reach LDS by DMA (buffer loads that write LDS directly) into a ring of
-// kStages stages of kStepBytes of K per row, XOR-swizzled against bank conflicts.
+// One GEMM core serves the three products: 512 threads (8 waves of 64) compute a 256 x 256 tile,
+// each wave a 128 x 64 part as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (or 32x32x2f32 for fp32
+// inputs; FLCE_MFMA=16 selects 8 x 4 blocks of 16x16x32 instead). Operands reach LDS by DMA (buffer
+// loads that write LDS directly) into a ring of kStages stages of kStepBytes of K per row,
+// XOR-swizzled against bank conflicts.
 #include <mutex>
 
 #include "flce_internal.h"
@@ -57,9 +58,31 @@ constexpr int NTHR = 64 * NW;    // threads per GEMM block
 constexpr int TILE = kTile;      // 256
 constexpr int WM = TILE / 2;     // wave tile rows (M): 128, one 128-wide V segment in the logits GEMM
 constexpr int WN = TILE / (NW / 2);  // wave tile columns (N): 64 or 128
-constexpr int TBM = WM / 32;     // 32x32 MFMA blocks per wave tile along M (4)
-constexpr int TBN = WN / 32;     // ... along N (2 or 4)
+// MFMA block: 32 x 32 (v_mfma_f32_32x32x16_bf16, K = 16 per instruction) or 16 x 16
+// (v_mfma_f32_16x16x32_bf16, K = 32). Both do the same flops per cycle on paper and read the same
+// LDS bytes per flop here. On random data an MFMA-only loop of the 16 x 16 form sustains about 12%
+// more under the chip's power limit (2.03 against 1.80 PF/s), but the three GEMMs measured even
+// with it (within 1% per product), so the 32 x 32 form, with half the MFMA instructions, stays.
+#ifndef FLCE_MFMA
+#define FLCE_MFMA 32
+#endif
+constexpr int MB = FLCE_MFMA;    // edge of one MFMA output block
+static_assert(MB == 16 || MB == 32, "16x16 or 32x32 MFMA blocks");
+constexpr int NR = MB * MB / 64;  // accumulator registers per block and lane (4 or 16)
+constexpr int TBM = WM / MB;     // MFMA blocks per wave tile along M (8 or 4)
+constexpr int TBN = WN / MB;     // ... along N (4 or 2 with 8 waves)
 static_assert(NW == 4 || NW == 8, "4 or 8 waves per GEMM block");
+typedef float facc __attribute__((ext_vector_type(NR)));
+// Accumulator layout: lane l holds column l % MB of its block and, in register r, row acc_row(r, l):
+// 32 x 32: 8 (r / 4) + 4 (l / 32) + r % 4; 16 x 16: 4 (l / 16) + r. In both, registers 4g .. 4g+3
+// are four consecutive rows, and acc_row(r, l) - acc_row(0, l) = acc_row(r, 0).
+__device__ __forceinline__ int acc_row(int r, int lane) {
+  return MB == 32 ? 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) : 4 * (lane >> 4) + r;
+}
+// 16-byte K chunk of a fragment read by this lane: 32 x 32 blocks take K 16 s .. 16 s + 15 per
+// substep s, each lane half 8 of them; 16 x 16 blocks take K 0 .. 31 of the step, each 16-lane group
+// 8 of them (one substep per step over K, split in two over the M blocks).
+__device__ __forceinline__ int frag_chunk(int s, int lane) { return MB == 32 ? 2 * s + (lane >> 5) : (lane >> 4); }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 // q = exp(s - c) is stored against a per-row reference c, the exponent of its segment factor clamped
@@ -88,16 +111,30 @@ __device__ __forceinline__ float tanh_via_exp(float x) {
 }
 
 // ---- MFMA on one 16-byte chunk of K per lane --------------------------------------------------
-__device__ __forceinline__ void mma(f32x16& acc, u32x4 a, u32x4 b, __bf16*) {
+#if FLCE_MFMA == 32
+__device__ __forceinline__ void mma(facc& acc, u32x4 a, u32x4 b, __bf16*) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
-__device__ __forceinline__ void mma(f32x16& acc, u32x4 a, u32x4 b, float*) {
+#else
+__device__ __forceinline__ void mma(facc& acc, u32x4 a, u32x4 b, __bf16*) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+#endif
+__device__ __forceinline__ void mma(facc& acc, u32x4 a, u32x4 b, float*) {
   const f32x4 fa = __builtin_bit_cast(f32x4, a), fb = __builtin_bit_cast(f32x4, b);
-  // lane half h holds k = 4h .. 4h+3 of this 8-wide K slice in both operands; each of the four
-  // K=2 MFMAs pairs the e-th element of both halves, so A and B see the same k assignment.
+  // each lane group (halves for 32 x 32, quarters for 16 x 16) holds 4 consecutive k of this K slice
+  // in both operands; each of the four MFMAs pairs the e-th element of every group, so A and B see
+  // the same k assignment.
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[e], fb[e], acc, 0, 0, 0);
+  for (int e = 0; e < 4; ++e) {
+#if FLCE_MFMA == 32
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[e], fb[e], acc, 0, 0, 0);
+#else
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[e], fb[e], acc, 0, 0, 0);
+#endif
+  }
 }
 
 // ---- 16-byte chunk conversions -------------------------------------------------------------
@@ -184,7 +221,7 @@ __device__ __forceinline__ void bstore_b128(rsrc_t r, u32 off, u32x4 v) {
 }
 
 // Accumulator addressing for row-major [rows][ld] output tiles whose element (0, 0) is the buffer
-// base: a per-lane offset for each 32-column block j (kOOB past ncols) plus a wave-uniform row offset
+// base: a per-lane offset for each MB-column block j (kOOB past ncols) plus a wave-uniform row offset
 // for (i, r), passed as the scalar offset of the buffer instruction. All tiles here keep
 // row * ld * ESZ below 2^31, so 32-bit arithmetic is exact.
 template <int ESZ>
@@ -193,15 +230,15 @@ struct AccAddr {
   int ld;
   __device__ __forceinline__ AccAddr(int ld_, int ncols) : ld(ld_) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
-    const int row0 = wm * WM + 4 * (lane >> 5);
+    const int row0 = wm * WM + acc_row(0, lane);
 #pragma unroll
     for (int j = 0; j < TBN; ++j) {
-      const int c = wn * WN + 32 * j + (lane & 31);
+      const int c = wn * WN + MB * j + lane % MB;
       col[j] = c < ncols ? (u32)(row0 * ld + c) * (u32)ESZ : kOOB;
     }
   }
   __device__ __forceinline__ u32 row(int i, int r) const {
-    return (u32)((32 * i + 8 * (r >> 2) + (r & 3)) * ld) * (u32)ESZ;
+    return (u32)((MB * i + acc_row(r, 0)) * ld) * (u32)ESZ;
   }
 };
 __device__ __forceinline__ float bload_f32(rsrc_t r, u32 voff, u32 soff) {
@@ -260,14 +297,14 @@ struct OpK {
       dma16(desc, k < kmax ? rowoff[q] + (u32)(k * sizeof(T)) : kOOB, lds + (kDmaPerOp * wave + q) * 1024);
     }
   }
-  // fragment of rows rowbase + 32 i + lane % 32 for chunk kcol
-  static constexpr int kFragReads = 1;  // LDS reads per 32-row fragment
+  // fragment of rows rowbase + MB i + lane % MB for chunk kcol
+  static constexpr int kFragReads = 1;  // LDS reads per fragment
   template <int NB>
   __device__ __forceinline__ void frag(const char* st, int rowbase, int kcol, u32x4 (&f)[NB]) const {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int row = rowbase + 32 * i + (lane & 31);
+      const int row = rowbase + MB * i + lane % MB;
       f[i] = *(const u32x4*)(st + row * kStepBytes + ((kcol ^ swz(row)) << 4));
     }
   }
@@ -277,7 +314,9 @@ struct OpK {
 // contiguously. In LDS a row keeps that layout (256 * sizeof(T) bytes), 16-byte chunk c stored at
 // slot c ^ (kMnXor * (k & 3)). bf16 fragments come from two ds_read_b64_tr_b16: in each 16-lane group,
 // lane j points at row k0 + j/4, columns nb + 4 (j % 4) .. +3, and lane i receives column nb + i of
-// rows k0 .. k0+3 (gfx950 transpose read). fp32 fragments are four ds_read_b32.
+// rows k0 .. k0+3 (gfx950 transpose read). The 16-lane groups differ in k0 (the lane's K chunk) and,
+// for 32 x 32 blocks, in nb (columns 0-15 or 16-31 of the block). fp32 fragments are four
+// ds_read_b32.
 #ifndef FLCE_MN_XOR
 #define FLCE_MN_XOR 4
 #endif
@@ -316,18 +355,18 @@ struct OpMN {
 #pragma unroll
     for (int q = 0; q < kDmaPerOp; ++q) dma16(desc, off[q], lds + (kDmaPerOp * wave + q) * 1024);
   }
-  static constexpr int kFragReads = sizeof(T) == 2 ? 2 : 4;  // LDS reads per 32-column fragment
+  static constexpr int kFragReads = sizeof(T) == 2 ? 2 : 4;  // LDS reads per fragment
   template <int NB>
   __device__ __forceinline__ void frag(const char* st, int colbase, int kcol, u32x4 (&f)[NB]) const {
     const int lane = threadIdx.x & 63;
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const int n = colbase + 32 * i + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const int n = colbase + MB * i + (MB == 32 ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);
         u32x4 v;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-          const int k = 4 * (2 * kcol + r) + ((lane & 15) >> 2);  // kcol = 2 s + half
+          const int k = 4 * (2 * kcol + r) + ((lane & 15) >> 2);  // kcol = frag_chunk(s, lane)
           const char* a = st + k * ROWB + (((n >> 3) ^ (kMnXor * (k & 3))) << 4) + ((n & 7) << 1);
           const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) i16x4*)(size_t)lds_addr(a));
@@ -340,7 +379,7 @@ struct OpMN {
     } else {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const int n = colbase + 32 * i + (lane & 31);
+        const int n = colbase + MB * i + lane % MB;
         u32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -354,9 +393,8 @@ struct OpMN {
 };
 
 // ---- the MFMA tile core --------------------------------------------------------------------
-// acc[i][j] is the 32x32 block (wave_m*128 + 32 i, wave_n*128 + 32 j) of the 256 x 256 tile. In the
-// 32x32 MFMA result layout, lane l holds column (l % 32) and, in register r, row
-// 8 * (r / 4) + 4 * (l / 32) + r % 4 of its block.
+// acc[i][j] is the MB x MB block (wave_m * WM + MB i, wave_n * WN + MB j) of the 256 x 256 tile, laid
+// out as acc_row describes.
 //
 // K is consumed in steps of kStepBytes through a ring of kStages LDS stages filled by DMA, kStages-1
 // steps ahead; a step's DMA is issued at its start, into the slot the previous step read. A step is
@@ -376,22 +414,22 @@ __device__ __forceinline__ void gemm_prologue(const LA& la, const LB& lb, int kb
 
 template <typename T, class LA, class LB>
 __device__ __forceinline__ void gemm_main(const LA& la, const LB& lb, int kb, int ke, char* smem,
-                                          f32x16 (&acc)[TBM][TBN]) {
+                                          facc (&acc)[TBM][TBN]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1, half = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
 #pragma unroll
   for (int i = 0; i < TBM; ++i)
 #pragma unroll
     for (int j = 0; j < TBN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.0f;
   const u32 lbase = lds_addr(smem);
   // any older vector-memory operations (loads and stores count alike) only make this wait stricter
   __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
   asm volatile("s_barrier" ::: "memory");
   u32x4 fa[2][TBM], fb[2][TBN];
-  la.frag(smem, wm * WM, half, fa[0]);
-  lb.frag(smem + kOpBytes, wn * WN, half, fb[0]);
+  la.frag(smem, wm * WM, frag_chunk(0, lane), fa[0]);
+  lb.frag(smem + kOpBytes, wn * WN, frag_chunk(0, lane), fb[0]);
   for (int ks = kb; ks < ke; ++ks) {
     const int t = ks - kb;
     const char* st = smem + (t % kStages) * kStageBytes;
@@ -403,14 +441,14 @@ __device__ __forceinline__ void gemm_main(const LA& la, const LB& lb, int kb, in
 #pragma unroll
     for (int s = 0; s < kSub; ++s) {
       if (s + 1 < kSub) {
-        la.frag(st, wm * WM, 2 * (s + 1) + half, fa[(s + 1) & 1]);
-        lb.frag(st + kOpBytes, wn * WN, 2 * (s + 1) + half, fb[(s + 1) & 1]);
+        la.frag(st, wm * WM, frag_chunk(s + 1, lane), fa[(s + 1) & 1]);
+        lb.frag(st + kOpBytes, wn * WN, frag_chunk(s + 1, lane), fb[(s + 1) & 1]);
       } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         const char* nx = smem + ((t + 1) % kStages) * kStageBytes;
-        la.frag(nx, wm * WM, half, fa[(s + 1) & 1]);
-        lb.frag(nx + kOpBytes, wn * WN, half, fb[(s + 1) & 1]);
+        la.frag(nx, wm * WM, frag_chunk(0, lane), fa[(s + 1) & 1]);
+        lb.frag(nx + kOpBytes, wn * WN, frag_chunk(0, lane), fb[(s + 1) & 1]);
       }
 #pragma unroll
       for (int i = 0; i < TBM; ++i)
@@ -431,21 +469,21 @@ __device__ __forceinline__ void gemm_main(const LA& la, const LB& lb, int kb, in
 // behind the DMA writes (better for K-contiguous first operands).
 template <typename T, bool INTERLEAVE, class LA, class LB>
 __device__ __forceinline__ void gemm_main_u(const LA& la, const LB& lb, int kb, int ke, char* smem,
-                                            f32x16 (&acc)[TBM][TBN]) {
+                                            facc (&acc)[TBM][TBN]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1, half = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
 #pragma unroll
   for (int i = 0; i < TBM; ++i)
 #pragma unroll
     for (int j = 0; j < TBN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.0f;
   const u32 lbase = lds_addr(smem);
   __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
   asm volatile("s_barrier" ::: "memory");
   u32x4 fa[2][TBM], fb[2][TBN];
-  la.frag(smem, wm * WM, half, fa[0]);
-  lb.frag(smem + kOpBytes, wn * WN, half, fb[0]);
+  la.frag(smem, wm * WM, frag_chunk(0, lane), fa[0]);
+  lb.frag(smem + kOpBytes, wn * WN, frag_chunk(0, lane), fb[0]);
   for (int ks0 = kb; ks0 < ke; ks0 += kStages) {
 #pragma unroll
     for (int t = 0; t < kStages; ++t) {
@@ -457,14 +495,14 @@ __device__ __forceinline__ void gemm_main_u(const LA& la, const LB& lb, int kb, 
 #pragma unroll
       for (int s = 0; s < kSub; ++s) {
         if (s + 1 < kSub) {
-          la.frag(st, wm * WM, 2 * (s + 1) + half, fa[(s + 1) & 1]);
-          lb.frag(st + kOpBytes, wn * WN, 2 * (s + 1) + half, fb[(s + 1) & 1]);
+          la.frag(st, wm * WM, frag_chunk(s + 1, lane), fa[(s + 1) & 1]);
+          lb.frag(st + kOpBytes, wn * WN, frag_chunk(s + 1, lane), fb[(s + 1) & 1]);
         } else {
           __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           const char* nx = smem + ((t + 1) % kStages) * kStageBytes;
-          la.frag(nx, wm * WM, half, fa[(s + 1) & 1]);
-          lb.frag(nx + kOpBytes, wn * WN, half, fb[(s + 1) & 1]);
+          la.frag(nx, wm * WM, frag_chunk(0, lane), fa[(s + 1) & 1]);
+          lb.frag(nx + kOpBytes, wn * WN, frag_chunk(0, lane), fb[(s + 1) & 1]);
         }
 #pragma unroll
         for (int i = 0; i < TBM; ++i)
@@ -488,22 +526,100 @@ __device__ __forceinline__ void gemm_main_u(const LA& la, const LB& lb, int kb, 
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The pipeline for 16 x 16 blocks: one MFMA covers the step's 32 K per block, so a step is split in
+// two substeps over the M blocks (the wave's first TBM/2 row blocks, then the others), each with all
+// TBN column blocks. The A fragments of the second half are read while the first half runs; at the
+// step's barrier the next step's first-half A fragments and all its B fragments are read, into the
+// other B buffer, while the second half runs. Unrolled by the ring depth (even), so buffer indices
+// and stage offsets are constants.
+template <typename T, bool INTERLEAVE, class LA, class LB>
+__device__ __forceinline__ void gemm_main16(const LA& la, const LB& lb, int kb, int ke, char* smem,
+                                            facc (&acc)[TBM][TBN]) {
+  static_assert(MB == 16 && kChunks == 4 && kStages % 2 == 0, "16 x 16 blocks: 64-byte steps, even ring");
+  constexpr int HM = TBM / 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1, kq = frag_chunk(0, lane);
+#pragma unroll
+  for (int i = 0; i < TBM; ++i)
+#pragma unroll
+    for (int j = 0; j < TBN; ++j)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.0f;
+  const u32 lbase = lds_addr(smem);
+  __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
+  asm volatile("s_barrier" ::: "memory");
+  u32x4 fa[2][HM], fb[2][TBN];
+  la.frag(smem, wm * WM, kq, fa[0]);
+  lb.frag(smem + kOpBytes, wn * WN, kq, fb[0]);
+  for (int ks0 = kb; ks0 < ke; ks0 += kStages) {
+#pragma unroll
+    for (int t = 0; t < kStages; ++t) {
+      const int ks = ks0 + t;
+      const char* st = smem + t * kStageBytes;
+      const int nslot = (t + kStages - 1) % kStages;
+      la.issue(ks + kStages - 1, lbase + nslot * kStageBytes);
+      lb.issue(ks + kStages - 1, lbase + nslot * kStageBytes + kOpBytes);
+      // substep 0: the first HM row blocks; the second half's A fragments are read meanwhile
+      la.frag(st, wm * WM + HM * MB, kq, fa[1]);
+#pragma unroll
+      for (int i = 0; i < HM; ++i)
+#pragma unroll
+        for (int j = 0; j < TBN; ++j) mma(acc[i][j], fa[0][i], fb[t & 1][j], (T*)nullptr);
+      if constexpr (INTERLEAVE) {
+        constexpr int nr = HM * LA::kFragReads, nm = HM * TBN, np = nr < nm ? nr : nm;
+#pragma unroll
+        for (int q = 0; q < np; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (nm > np) __builtin_amdgcn_sched_group_barrier(0x008, nm - np, 0);
+        if constexpr (nr > np) __builtin_amdgcn_sched_group_barrier(0x100, nr - np, 0);
+      }
+      // substep 1: the second half; after the barrier the next step's fragments are read meanwhile
+      __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const char* nx = smem + ((t + 1) % kStages) * kStageBytes;
+      la.frag(nx, wm * WM, kq, fa[0]);
+      lb.frag(nx + kOpBytes, wn * WN, kq, fb[(t + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < HM; ++i)
+#pragma unroll
+        for (int j = 0; j < TBN; ++j) mma(acc[HM + i][j], fa[1][i], fb[t & 1][j], (T*)nullptr);
+      if constexpr (INTERLEAVE) {
+        constexpr int nr = HM * LA::kFragReads + TBN * LB::kFragReads, nm = HM * TBN;
+        constexpr int np = nr < nm ? nr : nm;
+#pragma unroll
+        for (int q = 0; q < np; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (nm > np) __builtin_amdgcn_sched_group_barrier(0x008, nm - np, 0);
+        if constexpr (nr > np) __builtin_amdgcn_sched_group_barrier(0x100, nr - np, 0);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Main-loop schedules of the GEMM core.
 enum Sched { kRolled = 0, kUnrolled = 1, kInterleaved = 2 };
 template <typename T, int SCHED, class LA, class LB>
 __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int kb, int ke, char* smem,
-                                          f32x16 (&acc)[TBM][TBN]) {
+                                          facc (&acc)[TBM][TBN]) {
   if (kb >= ke) {
 #pragma unroll
     for (int i = 0; i < TBM; ++i)
 #pragma unroll
       for (int j = 0; j < TBN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.0f;
     return;
   }
   gemm_prologue(la, lb, kb, smem);
-  if constexpr (SCHED == kRolled)
+  if constexpr (MB == 16)
+    gemm_main16<T, SCHED == kInterleaved && sizeof(T) == 2>(la, lb, kb, ke, smem, acc);
+  else if constexpr (SCHED == kRolled)
     gemm_main<T>(la, lb, kb, ke, smem, acc);
   else
     gemm_main_u<T, SCHED == kInterleaved>(la, lb, kb, ke, smem, acc);
@@ -572,7 +688,7 @@ struct DwArgs {
 #define FLCE_SCHED_DX 2
 #endif
 #ifndef FLCE_SCHED_DW
-#define FLCE_SCHED_DW 2
+#define FLCE_SCHED_DW (FLCE_MFMA == 16 ? 1 : 2)
 #endif
 constexpr int kSchedFwd = FLCE_SCHED_FWD;
 constexpr int kSchedDx = FLCE_SCHED_DX;
@@ -592,7 +708,7 @@ __device__ __forceinline__ void fwd_labels(const FwdArgs& a, int c0, int (&ylab)
   const rsrc_t ry = make_rsrc(a.y, (int64_t)a.rows * 4);
 #pragma unroll
   for (int j = 0; j < TBN; ++j) {
-    const int c = c0 + wn * WN + 32 * j + (lane & 31);
+    const int c = c0 + wn * WN + MB * j + lane % MB;
     const int yv = __builtin_amdgcn_raw_buffer_load_b32(ry, c * 4, 0, 0);
     ylab[j] = c < a.rows && yv >= 0 ? yv - a.yoff : -1;
   }
@@ -607,23 +723,26 @@ __device__ __forceinline__ u32 qlds(int cl, int vl) {  // byte address of q(cl, 
 }
 
 // QONLY: store q only (slices of the recompute mode), no statistics or label logits.
+// For each column block j, a lane holds column c (a chunk row) and WM / (64 / MB) of the wave's 128
+// v values of that row: the 64 / MB lanes that share c (c + k MB) hold the rest, and the row's
+// segment statistics are combined across them with lane exchanges.
 template <typename T, bool CAP, bool EDGE, bool STORE_Q, bool QONLY, int J0, int JG>
-__device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc)[TBM][TBN], int v0, int c0,
+__device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, facc (&acc)[TBM][TBN], int v0, int c0,
                                                   const int (&ylab)[TBN], char* smem) {
   using S = typename Traits<T>::S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
-  const int vw = v0 + wm * WM, seg = vw / kSeg, half = lane >> 5;
+  const int vw = v0 + wm * WM, seg = vw / kSeg, col = lane % MB, vl0 = acc_row(0, lane);
   const float cap = a.softcap, icap = CAP ? 1.0f / cap : 0.0f;
   // references of the lane's rows (0 past the chunk), consumed in phase 3
   float cr[TBN];
   if constexpr (STORE_Q) {
     const rsrc_t rc = make_rsrc(a.cref, (int64_t)a.rows * 4);
 #pragma unroll
-    for (int j = J0; j < J0 + JG; ++j) cr[j] = bload_f32(rc, (u32)(c0 + wn * WN + 32 * j + (lane & 31)) * 4, 0);
+    for (int j = J0; j < J0 + JG; ++j) cr[j] = bload_f32(rc, (u32)(c0 + wn * WN + MB * j + col) * 4, 0);
   }
-  // Row blocks J0 .. J0+JG-1. They are independent; each phase runs over all of them so that the
-  // single wave per SIMD has independent work (and the cross-half exchanges are in flight together).
-  // Phase 1: softcap in place and the maxima (4 chains per j).
+  // Column blocks J0 .. J0+JG-1. They are independent; each phase runs over all of them so that the
+  // wave has independent work (and the cross-lane exchanges are in flight together).
+  // Phase 1: softcap in place and the maxima (one chain per row block i).
   float mx[TBN] = {};
 #pragma unroll
   for (int j = J0; j < J0 + JG; ++j) {
@@ -632,26 +751,30 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
     for (int i = 0; i < TBM; ++i) {
       m4[i] = kNegInf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < NR; ++r) {
         float s = acc[i][j][r];
         if constexpr (CAP) {
           s = cap * tanh_via_exp(s * icap);
           acc[i][j][r] = s;
         }
         if constexpr (EDGE) {
-          const int v = vw + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int v = vw + MB * i + acc_row(r, lane);
           s = v < a.V ? s : kNegInf;
         }
         m4[i] = fmaxf(m4[i], s);
       }
     }
-    mx[j] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    float m = m4[0];
+#pragma unroll
+    for (int i = 1; i < TBM; ++i) m = fmaxf(m, m4[i]);
+    mx[j] = m;
   }
-  // Phase 2: the two lanes c and c + 32 hold the two halves of a row's 128-wide segment.
-  {
+  // Phase 2: the lanes c, c + MB, ... hold the parts of a row's 128-wide segment.
+#pragma unroll
+  for (int x = MB; x < 64; x *= 2) {
     float o[TBN];
 #pragma unroll
-    for (int j = J0; j < J0 + JG; ++j) o[j] = __shfl_xor(mx[j], 32);
+    for (int j = J0; j < J0 + JG; ++j) o[j] = __shfl_xor(mx[j], x);
 #pragma unroll
     for (int j = J0; j < J0 + JG; ++j) mx[j] = fmaxf(mx[j], o[j]);
   }
@@ -664,24 +787,24 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
   float sum[TBN] = {};
 #pragma unroll
   for (int j = J0; j < J0 + JG; ++j) {
-    const int c = c0 + wn * WN + 32 * j + (lane & 31);
+    const int c = c0 + wn * WN + MB * j + col;
     const float ms = mx[j] == kNegInf ? 0.0f : mx[j];
     const float msl = -ms * kLog2e;
     const float kq = STORE_Q ? ex2(fminf(ms - cr[j], kRefSpan) * kLog2e) : 1.0f;
-    const u32 qrow = (u32)(((int64_t)(c - c0) * a.V_pad + wm * WM + 4 * half) * (int64_t)sizeof(S));
+    const u32 qrow = (u32)(((int64_t)(c - c0) * a.V_pad + wm * WM + vl0) * (int64_t)sizeof(S));
     float sum4[TBM];
 #pragma unroll
     for (int i = 0; i < TBM; ++i) {
       sum4[i] = 0.0f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < NR / 4; ++g) {
         float q[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const float s = acc[i][j][4 * g + rr];
           float e = ex2(fmaf(s, kLog2e, msl));  // 2^((s - ms) log2 e); 1 (to rounding) at the max
           if constexpr (EDGE) {
-            const int v = vw + 32 * i + 8 * g + 4 * half + rr;
+            const int v = vw + MB * i + acc_row(4 * g + rr, lane);
             e = v < a.V ? e : 0.0f;
           }
           sum4[i] += e;
@@ -692,11 +815,13 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
             q[rr] = e * kq;
           }
         }
-        const u32 qoff = qrow + (u32)((32 * i + 8 * g) * sizeof(S));
+        // registers 4g .. 4g+3 are rows acc_row(4g) .. +3 of block i: four consecutive v
+        const int vblk = MB * i + acc_row(4 * g, 0);
+        const u32 qoff = qrow + (u32)(vblk * sizeof(S));
         if constexpr (!STORE_Q) {
           (void)qoff;
         } else if constexpr (kStageQ<T>) {
-          *(u32x2*)(smem + qlds(c - c0, wm * WM + 32 * i + 8 * g + 4 * half)) = pack4_bf16(q[0], q[1], q[2], q[3]);
+          *(u32x2*)(smem + qlds(c - c0, wm * WM + vl0 + vblk)) = pack4_bf16(q[0], q[1], q[2], q[3]);
         } else if constexpr (sizeof(S) == 2) {
           bstore_b64(rq, qoff, pack4_bf16(q[0], q[1], q[2], q[3]));
         } else {
@@ -704,22 +829,28 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
         }
       }
     }
-    sum[j] = (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
+    float t = sum4[0];
+#pragma unroll
+    for (int i = 1; i < TBM; ++i) t += sum4[i];
+    sum[j] = t;
   }
   // Phases 4 and 5 (not for vocabulary slices, whose statistics exist already).
   if constexpr (QONLY) return;
   // Phase 4: segment statistics of the tile's rows.
-  {
+#pragma unroll
+  for (int x = MB; x < 64; x *= 2) {
     float o[TBN];
 #pragma unroll
-    for (int j = J0; j < J0 + JG; ++j) o[j] = __shfl_xor(sum[j], 32);
+    for (int j = J0; j < J0 + JG; ++j) o[j] = __shfl_xor(sum[j], x);
 #pragma unroll
-    for (int j = J0; j < J0 + JG; ++j) {
-      const int c = c0 + wn * WN + 32 * j + (lane & 31);
-      if (lane < 32 && c < a.rows) {
-        a.seg_m[(int64_t)c * a.nseg + seg] = mx[j];
-        a.seg_s[(int64_t)c * a.nseg + seg] = sum[j] + o[j];
-      }
+    for (int j = J0; j < J0 + JG; ++j) sum[j] += o[j];
+  }
+#pragma unroll
+  for (int j = J0; j < J0 + JG; ++j) {
+    const int c = c0 + wn * WN + MB * j + col;
+    if (lane < MB && c < a.rows) {
+      a.seg_m[(int64_t)c * a.nseg + seg] = mx[j];
+      a.seg_s[(int64_t)c * a.nseg + seg] = sum[j];
     }
   }
   // Phase 5: the label logit of row c, taken from the same fp32 value that entered the row
@@ -727,32 +858,45 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, f32x16 (&acc
 #pragma unroll
   for (int j = J0; j < J0 + JG; ++j) {
     const unsigned rel = (unsigned)(ylab[j] - vw);
-    const bool mine = rel < (unsigned)WM && (int)((rel >> 2) & 1) == half;
+    // for the lane that holds it: block i = rel / MB, and within the block row rb = rel % MB, which
+    // is acc_row(rsel, lane) for one lane group and register
+    const int rb = (int)(rel % MB);
+    int isel, rsel;
+    bool mine;
+    if constexpr (MB == 32) {
+      mine = rel < (unsigned)WM && ((rb >> 2) & 1) == (lane >> 5);
+      rsel = 4 * (rb >> 3) + (rb & 3);
+    } else {
+      mine = rel < (unsigned)WM && (rb >> 2) == (lane >> 4);
+      rsel = rb & 3;
+    }
+    isel = (int)(rel / MB);
     if (__any(mine)) {
-      // for a lane that holds it: block i = rel / 32, register r = 4 ((rel / 8) % 4) + rel % 4
-      const int isel = (int)(rel >> 5), rsel = 4 * (int)((rel >> 3) & 3) + (int)(rel & 3);
       float sy = 0.0f;
 #pragma unroll
       for (int i = 0; i < TBM; ++i) {
         float t = acc[i][j][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) t = rsel == r ? acc[i][j][r] : t;
+        for (int r = 1; r < NR; ++r) t = rsel == r ? acc[i][j][r] : t;
         sy = isel == i ? t : sy;
       }
       if (mine) {
-        const int c = c0 + wn * WN + 32 * j + (lane & 31);
+        const int c = c0 + wn * WN + MB * j + col;
         a.s_label[c] = sy;
       }
     }
   }
 }
 
-template <typename T, bool CAP, bool EDGE, bool STORE_Q, bool QONLY>
-__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, f32x16 (&acc)[TBM][TBN], int v0, int c0,
+template <typename T, bool CAP, bool EDGE, bool STORE_Q, bool QONLY, int J0 = 0>
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, facc (&acc)[TBM][TBN], int v0, int c0,
                                              const int (&ylab)[TBN], char* smem) {
-  // two row blocks at a time: enough independent work, few enough live values to stay in registers
-  fwd_epilogue_part<T, CAP, EDGE, STORE_Q, QONLY, 0, 2>(a, acc, v0, c0, ylab, smem);
-  if constexpr (TBN > 2) fwd_epilogue_part<T, CAP, EDGE, STORE_Q, QONLY, 2, 2>(a, acc, v0, c0, ylab, smem);
+  // two column blocks at a time: enough independent work, few enough live values to stay in registers
+  if constexpr (J0 < TBN) {
+    constexpr int JG = TBN - J0 < 2 ? TBN - J0 : 2;
+    fwd_epilogue_part<T, CAP, EDGE, STORE_Q, QONLY, J0, JG>(a, acc, v0, c0, ylab, smem);
+    fwd_epilogue<T, CAP, EDGE, STORE_Q, QONLY, J0 + JG>(a, acc, v0, c0, ylab, smem);
+  }
 }
 
 // Staged q tile -> workspace: 32 threads per 512-byte row, each one 16-byte chunk; rows past the
@@ -782,7 +926,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs& a, int v0, int c0, char*
   // the labels are loaded before the main loop, whose first wait on the operand loads covers them
   int ylab[TBN];
   fwd_labels(a, c0, ylab);
-  f32x16 acc[TBM][TBN];
+  facc acc[TBM][TBN];
   const int nk = (int)((a.H + OpK<T>::BK - 1) / OpK<T>::BK);
   static_assert(OpK<T>::BK == OpMN<T>::BK, "operands step through K together");
   gemm_core<T, kSchedFwd>(la, lb, 0, nk, smem, acc);
@@ -824,29 +968,29 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
 constexpr int kDxRowBytes = TILE * 4;
 constexpr int kDxPassRows = WM;
 static_assert(kDxPassRows * kDxRowBytes <= kStages * kStageBytes, "a pass fits the LDS ring");
-static_assert(TBM % (TILE / kDxPassRows) == 0 && kDxPassRows == 2 * 32 * (TBM / (TILE / kDxPassRows)),
+static_assert(TBM % (TILE / kDxPassRows) == 0 && kDxPassRows == 2 * MB * (TBM / (TILE / kDxPassRows)),
               "a pass stages the same number of row blocks of each of the two wave-rows");
 template <typename T>
-__device__ __forceinline__ void dx_store_tile(const DxArgs& a, const f32x16 (&acc)[TBM][TBN], int c0, int h0,
+__device__ __forceinline__ void dx_store_tile(const DxArgs& a, const facc (&acc)[TBM][TBN], int c0, int h0,
                                               int vrows, char* smem) {
   constexpr int OV = 16 / (int)sizeof(T);  // output elements per 16-byte store
   constexpr int TPR = TILE / OV;           // threads per row
   constexpr int RPI = NTHR / TPR;          // rows per read-out iteration
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1, half = lane >> 5;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int ch = (int)threadIdx.x % TPR, h = h0 + ch * OV;
-  constexpr int kBlocksPerPass = TBM / (TILE / kDxPassRows);  // row blocks of a wave per pass (2)
-  constexpr int kWaveRows = 32 * kBlocksPerPass;              // rows of a wave-row per pass (64)
+  constexpr int kBlocksPerPass = TBM / (TILE / kDxPassRows);  // row blocks of a wave per pass
+  constexpr int kWaveRows = MB * kBlocksPerPass;              // rows of a wave-row per pass (64)
 #pragma unroll
   for (int pass = 0; pass < TILE / kDxPassRows; ++pass) {
 #pragma unroll
     for (int ib = 0; ib < kBlocksPerPass; ++ib) {
       const int i = pass * kBlocksPerPass + ib;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = wm * kWaveRows + 32 * ib + 8 * (r >> 2) + 4 * half + (r & 3);
+      for (int r = 0; r < NR; ++r) {
+        const int rl = wm * kWaveRows + MB * ib + acc_row(r, lane);
 #pragma unroll
         for (int j = 0; j < TBN; ++j) {
-          const int cl = wn * WN + 32 * j + (lane & 31);
+          const int cl = wn * WN + MB * j + lane % MB;
           *(float*)(smem + rl * kDxRowBytes + cl * 4) = acc[i][j][r];
         }
       }
@@ -902,7 +1046,7 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
   la.init((const T*)a.ws + (int64_t)c0 * a.V_pad, a.V_pad, min(TILE, a.rows - c0), ke * BK);
   OpMN<T> lb;  // W: source rows are v (K), columns h
   lb.init((const T*)a.W + h0, a.H, (int)min<int64_t>(a.V, (int64_t)ke * BK), (int)min<int64_t>(TILE, a.H - h0));
-  f32x16 acc[TBM][TBN];
+  facc acc[TBM][TBN];
   gemm_core<T, kSchedDx>(la, lb, kb, ke, smem, acc);
 
   // output tile (c0, h0); rows past the chunk and columns past H are dropped
@@ -916,13 +1060,13 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
       // running fp32 sum over the vocabulary slices of the recompute mode (one split)
 #pragma unroll
       for (int i = 0; i < TBM; ++i) {
-        float old[TBN][16];
+        float old[TBN][NR];
 #pragma unroll
         for (int j = 0; j < TBN; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) old[j][r] = bload_f32(ro, ad.col[j], ad.row(i, r));
+          for (int r = 0; r < NR; ++r) old[j][r] = bload_f32(ro, ad.col[j], ad.row(i, r));
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
           for (int j = 0; j < TBN; ++j) bstore_f32(ro, ad.col[j], ad.row(i, r), acc[i][j][r] + old[j][r]);
         __builtin_amdgcn_sched_barrier(0);
@@ -931,7 +1075,7 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
 #pragma unroll
       for (int i = 0; i < TBM; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
           for (int j = 0; j < TBN; ++j) bstore_f32(ro, ad.col[j], ad.row(i, r), acc[i][j][r]);
         __builtin_amdgcn_sched_barrier(0);
@@ -976,7 +1120,7 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
   lb.init((const T*)a.X + h0, a.H, a.rows, (int)min<int64_t>(TILE, a.H - h0));
 
   const int nk = (a.rows + OpMN<T>::BK - 1) / OpMN<T>::BK;
-  f32x16 acc[TBM][TBN];
+  facc acc[TBM][TBN];
   gemm_core<T, kSchedDw>(la, lb, 0, nk, smem, acc);
 
   // row-major [V][H] fp32 tile at (v0, h0): written (first chunk) or read-modify-written (later
@@ -985,24 +1129,25 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
   const rsrc_t rd = make_rsrc(a.dW + (int64_t)v0 * a.H + h0, ((int64_t)vrows * a.H - h0) * 4);
   const AccAddr<4> ad((int)a.H, ncols);
   if (a.accumulate) {
-    // software pipeline over the 16 blocks b = (i, j): the loads of block b + kAhead are issued
-    // before block b is added and stored, so kAhead blocks of loads cover the memory latency
-    constexpr int kAhead = 2, kNB = TBM * TBN;
-    float old[kAhead + 1][16];
+    // software pipeline over the TBM x TBN blocks b = (i, j): the loads of block b + kAhead are
+    // issued before block b is added and stored, so kAhead blocks (32 values per lane) of loads cover
+    // the memory latency
+    constexpr int kAhead = 32 / NR, kNB = TBM * TBN;
+    float old[kAhead + 1][NR];
 #pragma unroll
     for (int b = 0; b < kAhead; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) old[b][r] = bload_f32(rd, ad.col[b % TBN], ad.row(b / TBN, r));
+      for (int r = 0; r < NR; ++r) old[b][r] = bload_f32(rd, ad.col[b % TBN], ad.row(b / TBN, r));
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       if (b + kAhead < kNB) {
         const int bn = b + kAhead;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) old[bn % (kAhead + 1)][r] = bload_f32(rd, ad.col[bn % TBN], ad.row(bn / TBN, r));
+        for (int r = 0; r < NR; ++r) old[bn % (kAhead + 1)][r] = bload_f32(rd, ad.col[bn % TBN], ad.row(bn / TBN, r));
       }
       const int i = b / TBN, j = b % TBN;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < NR; ++r)
         bstore_f32(rd, ad.col[j], ad.row(i, r), acc[i][j][r] + old[b % (kAhead + 1)][r]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1010,7 +1155,7 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
 #pragma unroll
     for (int i = 0; i < TBM; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < NR; ++r)
 #pragma unroll
         for (int j = 0; j < TBN; ++j) bstore_f32(rd, ad.col[j], ad.row(i, r), acc[i][j][r]);
       __builtin_amdgcn_sched_barrier(0);
