@@ -2,7 +2,10 @@
 (default chunk plan): the whole loss, the whole grad_hidden and the whole grad_W of one call against the
 CPU float64 oracle (flce_blocked: every row's logits built in blocks of rows), plus the worst per-row
 error of each gradient, and relations that hold at any size (mean = sum / N, loss additivity over a
-split of the rows, <grad_W, W> = <grad_hidden, hidden>, ignored rows exactly zero).
+split of the rows, <grad_W, W> = <grad_hidden, hidden>, ignored rows exactly zero). The forward-only
+call's per-row loss terms and log-sum-exp are checked row by row against the same oracle run; at the
+Llama-3-8B head also the recompute mode's whole tensors, and the same rows laid out as 8 shifted
+sequences (the benchmark's sequence mode).
 
 Workloads: the Llama-3-8B head, the Gemma2 head (softcap 30), the GPT-2 head, one GPU's vocabulary share
 of the Llama head, and the ragged B*T sweep's two endpoints (4096, 32768) plus three of its seeded draws.
@@ -28,7 +31,27 @@ def _row_errors(got, ref):
     return np.linalg.norm(got[nz] - ref[nz], axis=1) / nr[nz]
 
 
-def _fullsize_check(X, W, y, softcap, label):
+def _check_grads(name, gh_c, gw_c, o_dx, o_dw, valid, scale=1.0):
+    """Whole-tensor and worst-row errors of both gradients against scale times the oracle's."""
+    tol = TOL["bf16"]
+    ref_dx = o_dx if scale == 1.0 else scale * o_dx
+    ref_dw = o_dw if scale == 1.0 else scale * o_dw
+    err_dx = rel_fro(gh_c, ref_dx)
+    err_dw = rel_fro(gw_c, ref_dw)
+    rows_dx = _row_errors(gh_c, ref_dx)
+    rows_dw = _row_errors(gw_c, ref_dw)
+    print(f"   {name}: grad_hidden rel Frobenius {err_dx:.2e} (worst row {rows_dx.max():.2e}); "
+          f"grad_W rel Frobenius {err_dw:.2e} (worst row {rows_dw.max():.2e})", flush=True)
+    assert err_dx <= tol["grad"]
+    assert err_dw <= tol["grad"]
+    # no single row may be off by more than the whole-tensor bar either
+    assert rows_dx.max() <= tol["grad"]
+    assert rows_dw.max() <= tol["grad"]
+    assert not np.any(gh_c[~valid]), "ignored rows must get exactly zero gradient"
+    assert np.isfinite(gw_c).all() and np.isfinite(gh_c).all()
+
+
+def _fullsize_check(X, W, y, softcap, label, recompute=False):
     dev = device()
     e = flce.FLCE(dev)
     BT, H = X.shape
@@ -42,6 +65,17 @@ def _fullsize_check(X, W, y, softcap, label):
     gh_c = gh.double().cpu().numpy()
     gw_c = gw.double().cpu().numpy()
     tol = TOL["bf16"]
+    # the forward-only call's per-row terms (reduction 'none') and log-sum-exp of every row
+    f_rows, f_lse = e.forward(Xd, Wd, yd, softcap=softcap, reduction="none", return_lse=True)
+    f_rows = f_rows.double().cpu().numpy()
+    f_lse = f_lse.double().cpu().numpy()
+    # the recompute mode on the same inputs
+    r_out = None
+    if recompute:
+        rl, rgh, rgw = e.forward_backward_recompute(Xd, Wd, yd, softcap=softcap)
+        torch.cuda.synchronize()
+        r_out = (float(rl), rgh.double().cpu().numpy(), rgw.double().cpu().numpy())
+        del rl, rgh, rgw
 
     # relations that hold at any size, from further GPU calls on the same inputs
     lsum = float(e.forward_backward(Xd, Wd, yd, softcap=softcap, reduction="sum")[0])
@@ -63,32 +97,69 @@ def _fullsize_check(X, W, y, softcap, label):
     valid = (y != -100).numpy()
 
     err_l = abs(loss - o_loss) / abs(o_loss)
-    err_dx = rel_fro(gh_c, o_dx)
-    err_dw = rel_fro(gw_c, o_dw)
-    rows_dx = _row_errors(gh_c, o_dx)
-    rows_dw = _row_errors(gw_c, o_dw)
-    print(f"   loss rel {err_l:.2e}; grad_hidden rel Frobenius {err_dx:.2e} (worst row {rows_dx.max():.2e}); "
-          f"grad_W rel Frobenius {err_dw:.2e} (worst row {rows_dw.max():.2e})", flush=True)
+    print(f"   loss rel {err_l:.2e}", flush=True)
     assert err_l <= tol["loss"]
-    assert err_dx <= tol["grad"]
-    assert err_dw <= tol["grad"]
-    # no single row may be off by more than the whole-tensor bar either
-    assert rows_dx.max() <= tol["grad"]
-    assert rows_dw.max() <= tol["grad"]
-    assert not np.any(gh_c[~valid]), "ignored rows must get exactly zero gradient"
+    _check_grads("fused call", gh_c, gw_c, o_dx, o_dw, valid)
+
+    # forward only, every row: the loss bar applied to each row's term, and each row's lse
+    o_rows, o_lse = d["loss_rows"], d["lse"]
+    e_rows = np.abs(f_rows - o_rows) / np.maximum(np.abs(o_rows), 1.0)
+    e_lse = np.abs(f_lse - o_lse) / np.abs(o_lse)
+    print(f"   forward only: worst row loss term {e_rows.max():.2e}, worst row lse {e_lse.max():.2e} "
+          f"(relative)", flush=True)
+    assert e_rows.max() <= tol["loss"] and e_lse.max() <= tol["loss"]
+    assert not np.any(f_rows[~valid]), "ignored rows have a zero loss term"
+
+    if r_out is not None:
+        r_loss, r_gh, r_gw = r_out
+        err_rl = abs(r_loss - o_loss) / abs(o_loss)
+        print(f"   recompute mode: loss rel {err_rl:.2e}", flush=True)
+        assert err_rl <= tol["loss"]
+        _check_grads("recompute mode", r_gh, r_gw, o_dx, o_dw, valid)
 
     assert abs(lsum / N - loss) <= 1e-5 * loss
     assert abs(l1 + l2 - lsum) <= 1e-5 * lsum
     print(f"   <dW,W> {a:.6e} <dX,X> {b:.6e}", flush=True)
     assert abs(a - b) <= 2e-2 * max(abs(a), abs(b)) + 1e-6
-    assert np.isfinite(gw_c).all() and np.isfinite(gh_c).all()
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_head", "gemma2_head", "gpt2_head", "llama3_8b_head_vshard8"])
 def test_fullsize_workload(name):
     w = inputs.WORKLOADS[name]
     X, W, y = inputs.make_inputs(w, seed=0)
-    _fullsize_check(X, W, y, w.softcap, name)
+    _fullsize_check(X, W, y, w.softcap, name, recompute=name == "llama3_8b_head")
+
+
+def test_fullsize_shifted_sequences():
+    """The Llama-3-8B head's rows as 8 sequences of 1025 positions [8, 1025, 4096] (the benchmark's
+    sequence mode): position t scored against label t+1 by the library, gradients scaled by 0.5; against
+    the oracle on the explicitly gathered (hidden t, label t+1) pairs. The last position of every
+    sequence gets exactly zero gradient."""
+    dev = device()
+    w = inputs.WORKLOADS["llama3_8b_head"]
+    B, T = 8, w.BT // 8 + 1
+    X, W, y = inputs.make_inputs(w, seed=0, BT=B * T)
+    e = flce.FLCE(dev)
+    announce("llama3_8b_head as 8 shifted sequences", f"[{B}, {T}, {w.H}], grad_scale 0.5")
+    X3, y2 = X.view(B, T, w.H), y.view(B, T)
+    loss, gh, gw = e.forward_backward_seq(X3.to(dev), W.to(dev), y2.to(dev), shift=True, grad_scale=0.5)
+    torch.cuda.synchronize()
+    assert e.status() == 0
+    loss = float(loss)
+    gh3 = gh.double().cpu().numpy()
+    gw_c = gw.double().cpu().numpy()
+    del gh, gw
+    torch.cuda.empty_cache()
+    assert not np.any(gh3[:, -1]), "the last position of each sequence has no row"
+    Xs = X3[:, :-1].reshape(-1, w.H)
+    ys = y2[:, 1:].reshape(-1)
+    t0 = time.perf_counter()
+    o_loss, o_dx, o_dw, d = oracle.flce_blocked(Xs, W, ys, -100, 0.0, "mean", block_rows=1024)
+    print(f"   oracle done in {time.perf_counter() - t0:.1f} s (loss {o_loss:.6f}, N={d['N']})", flush=True)
+    err_l = abs(loss - o_loss) / abs(o_loss)
+    print(f"   loss rel {err_l:.2e}", flush=True)
+    assert err_l <= TOL["bf16"]["loss"]
+    _check_grads("sequences", gh3[:, :-1].reshape(-1, w.H), gw_c, o_dx, o_dw, (ys != -100).numpy(), scale=0.5)
 
 
 def _ragged_cases():
