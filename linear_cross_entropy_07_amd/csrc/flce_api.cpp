@@ -98,8 +98,8 @@ struct Layout {
   int64_t chunk_rows;
 };
 
-// Workspace carving. The forward-only path (backward = false) needs no q chunk, no per-row references
-// or factors, no split-K partials and no scaled copy of the chunk's hidden rows.
+// Workspace carving. The forward-only path (backward = false) needs no q chunk, no per-row lse or
+// factors, no split-K partials and no scaled copy of the chunk's hidden rows.
 Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu, bool backward = true) {
   Layout L{};
   int64_t n, rows;
@@ -122,7 +122,7 @@ Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu
   L.off_y = take((size_t)BT * 4);
   L.off_sl = take((size_t)BT * 4);
   L.off_loss = take((size_t)BT * 4);
-  L.off_cref = take(backward ? (size_t)BT * 4 : 0);
+  L.off_cref = take((size_t)BT * 4);
   L.off_lse = take(backward ? (size_t)BT * 4 : 0);
   L.off_fs = take(backward ? (size_t)BT * 4 : 0);
   L.off_part = take(L.splits > 1 ? (size_t)L.splits * rows * H * 4 : 0);
@@ -501,6 +501,7 @@ int run_forward(flce_ctx* h, const void* hidden, const void* W, const int64_t* l
     const int64_t row0 = ci * crows;
     const int64_t rows = (BT - row0) < crows ? (BT - row0) : crows;
     FLCE_LAUNCH(FLCE_K_TRANSPOSE, flce::launch_transpose(p, hidden, w, row0, rows, stream));
+    FLCE_LAUNCH(FLCE_K_ROWREF, flce::launch_rowref(p, hidden, W, w, row0, rows, stream));
     FLCE_LAUNCH(FLCE_K_FWD, flce::launch_fwd(p, W, w, row0, rows, false, stream));
     FLCE_LAUNCH(FLCE_K_ROWS, flce::launch_rows(p, w, row0, rows, loss_rows, lse_rows, stream));
   }

@@ -8,12 +8,13 @@
 //
 //   k_rowref  per row: a reference c = the (softcapped) label logit, one dot product of hidden and
 //             the label's row of W, known before the logits exist.
-//   k_fwd     Z^T tile = W_tile . X_tile^T on MFMA (bf16 -> fp32), epilogue: optional softcap,
-//             per-(row, 128-wide V segment) max and sum of exp, and one 16-bit store per logit of
-//             q = exp(s - c) * (softcap derivative): the softmax numerator against the row's
-//             reference. No [BT, V] tensor exists.
-//   k_lse     per row: lse from the segment statistics and the loss term; a row whose maximum lies
-//             more than kRefSpan above its reference gets the maximum as reference, its stored q
+//   k_fwd     Z^T tile = W_tile . X_tile^T on MFMA (bf16 -> fp32), epilogue: optional softcap, and per
+//             (row, 128-wide V segment) a reference r = max(c, segment max - kRefSpan), the sum of
+//             exp(s - r), and one 16-bit store per logit of q = exp(s - r) * (softcap derivative): the
+//             softmax numerator against the row's reference (r = c but for segments more than
+//             kRefSpan above it). No [BT, V] tensor exists.
+//   k_lse     per row: lse from the segment statistics and the loss term; a row with a segment whose
+//             reference lies above c gets the largest segment reference as its reference, its stored q
 //             rescaled segment by segment to match (the usual rows do nothing more).
 //   k_rowfix  per row: f = g exp(c - lse), so that dZ_v = f q_v for v != label; the label entry of
 //             q becomes (p_y - 1) / f, computed from the exact label logit; and hidden_f = f hidden.
@@ -85,11 +86,11 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
 __device__ __forceinline__ int frag_chunk(int s, int lane) { return MB == 32 ? 2 * s + (lane >> 5) : (lane >> 4); }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
-// q = exp(s - c) is stored against a per-row reference c, the exponent of its segment factor clamped
-// at kRefSpan; a row whose maximum lies more than kRefSpan above c (only possible where the label
-// logit lies that far below the row's maximum) is rescaled to its maximum afterwards.
-// exp(kRefSpan) = 7e20 keeps q, and the fp32 sums of q times W over up to 2^20 vocabulary rows, far
-// from overflow.
+// q = exp(s - c) is stored against a per-row reference c; a segment whose maximum lies more than
+// kRefSpan above c (only possible where the label logit lies that far below it) is stored against its
+// maximum less kRefSpan instead, and its row is rescaled to one reference afterwards. Every stored q is
+// thus at most exp(kRefSpan) = 7e20, which keeps q, and the fp32 sums of q times W over up to 2^20
+// vocabulary rows, far from overflow.
 constexpr float kRefSpan = 48.0f;
 
 template <typename T> struct Traits;
@@ -735,7 +736,7 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, facc (&acc)[
   const float cap = a.softcap, icap = CAP ? 1.0f / cap : 0.0f;
   // references of the lane's rows (0 past the chunk), consumed in phase 3
   float cr[TBN];
-  if constexpr (STORE_Q) {
+  {
     const rsrc_t rc = make_rsrc(a.cref, (int64_t)a.rows * 4);
 #pragma unroll
     for (int j = J0; j < J0 + JG; ++j) cr[j] = bload_f32(rc, (u32)(c0 + wn * WN + MB * j + col) * 4, 0);
@@ -778,19 +779,20 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, facc (&acc)[
 #pragma unroll
     for (int j = J0; j < J0 + JG; ++j) mx[j] = fmaxf(mx[j], o[j]);
   }
-  // Phase 3: the sums of e = exp(s - segment max), and q = e exp(segment max - c) (times the softcap
-  // derivative) = exp(s - c) to the workspace, the exponent of the second factor clamped at kRefSpan
-  // (k_lse rescales rows beyond it). Rows that do not count have c = +inf, hence q = 0.
+  // Phase 3: the segment's reference r = max(c, segment max - kRefSpan), so that every e = exp(s - r)
+  // is at most exp(kRefSpan) (r = c unless the label logit lies more than kRefSpan below the segment
+  // maximum; k_lse rescales such rows), the sums of e, and q = e (times the softcap derivative) to the
+  // workspace. Rows that do not count have c = -inf, hence r = segment max - kRefSpan.
   // q tile: rows c0.. of the chunk (rows past the chunk are dropped), columns v0 .. v0+255 < V_pad
   const rsrc_t rq = make_rsrc((S*)a.ws + (int64_t)c0 * a.V_pad + v0,
                               (int64_t)min(TILE, a.rows - c0) * a.V_pad * (int64_t)sizeof(S));
-  float sum[TBN] = {};
+  float sum[TBN] = {}, rf[TBN];
 #pragma unroll
   for (int j = J0; j < J0 + JG; ++j) {
     const int c = c0 + wn * WN + MB * j + col;
-    const float ms = mx[j] == kNegInf ? 0.0f : mx[j];
-    const float msl = -ms * kLog2e;
-    const float kq = STORE_Q ? ex2(fminf(ms - cr[j], kRefSpan) * kLog2e) : 1.0f;
+    // (a segment wholly past V has no maximum; its e are masked to 0 and its statistics record -inf)
+    rf[j] = mx[j] == kNegInf ? 0.0f : fmaxf(cr[j], mx[j] - kRefSpan);
+    const float msl = -rf[j] * kLog2e;
     const u32 qrow = (u32)(((int64_t)(c - c0) * a.V_pad + wm * WM + vl0) * (int64_t)sizeof(S));
     float sum4[TBM];
 #pragma unroll
@@ -802,7 +804,7 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, facc (&acc)[
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const float s = acc[i][j][4 * g + rr];
-          float e = ex2(fmaf(s, kLog2e, msl));  // 2^((s - ms) log2 e); 1 (to rounding) at the max
+          float e = ex2(fmaf(s, kLog2e, msl));  // 2^((s - r) log2 e)
           if constexpr (EDGE) {
             const int v = vw + MB * i + acc_row(4 * g + rr, lane);
             e = v < a.V ? e : 0.0f;
@@ -810,9 +812,9 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, facc (&acc)[
           sum4[i] += e;
           if constexpr (CAP) {
             const float t = s * icap;
-            q[rr] = (e * kq) * (1.0f - t * t);
+            q[rr] = e * (1.0f - t * t);
           } else {
-            q[rr] = e * kq;
+            q[rr] = e;
           }
         }
         // registers 4g .. 4g+3 are rows acc_row(4g) .. +3 of block i: four consecutive v
@@ -849,7 +851,7 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, facc (&acc)[
   for (int j = J0; j < J0 + JG; ++j) {
     const int c = c0 + wn * WN + MB * j + col;
     if (lane < MB && c < a.rows) {
-      a.seg_m[(int64_t)c * a.nseg + seg] = mx[j];
+      a.seg_m[(int64_t)c * a.nseg + seg] = mx[j] == kNegInf ? kNegInf : rf[j];
       a.seg_s[(int64_t)c * a.nseg + seg] = sum[j];
     }
   }
@@ -1269,8 +1271,9 @@ __device__ __forceinline__ float row_lse(const float* m, const float* sp, int ns
 }
 
 // Reference of each row of a chunk (one wave per row): c = the softcapped label logit, the dot product
-// of the row of hidden with the label's row of W in fp32; +inf for rows that do not count (their q is
-// then 0).
+// of the row of hidden with the label's row of W in fp32; -inf for rows that do not count (their
+// segments then take the segment maximum less kRefSpan as reference, so that their statistics still
+// give the row's lse, and their q, at most exp(kRefSpan), meets a zero factor f in the backward).
 template <typename T>
 __global__ __launch_bounds__(256) void k_rowref(const T* X, RowMap hmap, int64_t row0, int rows, int H, const T* W,
                                                 const int* y32, float softcap, float* cref) {
@@ -1279,7 +1282,7 @@ __global__ __launch_bounds__(256) void k_rowref(const T* X, RowMap hmap, int64_t
   if (r >= rows) return;
   const int y = y32[r];
   if (y < 0) {
-    if (lane == 0) cref[r] = __builtin_huge_valf();
+    if (lane == 0) cref[r] = kNegInf;
     return;
   }
   const T* x = X + hmap(row0 + r);
@@ -1296,12 +1299,12 @@ __global__ __launch_bounds__(256) void k_rowref(const T* X, RowMap hmap, int64_t
   if (lane == 0) cref[r] = softcap > 0.0f ? softcap * tanh_via_exp(acc / softcap) : acc;
 }
 
-// Per row of a chunk (one block per row): lse from the segment statistics and the loss term. A row
-// whose maximum M lies more than kRefSpan above its reference c gets M as its reference; with `q`
-// (the fused call, where q exists already) its stored q is rescaled to match: segment j was stored as
-// exp(s - m_j) exp(min(m_j - c, kRefSpan)) (m_j the segment maximum), so it is multiplied by
-// exp(m_j - M - min(m_j - c, kRefSpan)), a factor at most exp(-kRefSpan). Other rows stop after the
-// statistics.
+// Per row of a chunk (one block per row): lse from the segment statistics and the loss term. Segment j
+// holds the pair (r_j, sum of exp(s - r_j)), r_j its reference. A counted row with a reference M =
+// max_j r_j above its own c (a segment maximum more than kRefSpan above the label logit) gets M as its
+// reference; with `q` (the fused call, where q exists already) its stored q is rescaled to match:
+// segment j was stored as exp(s - r_j), so it is multiplied by exp(r_j - M) <= 1. Other rows stop
+// after the statistics.
 template <typename T>
 __global__ __launch_bounds__(256) void k_lse(const float* seg_m, const float* seg_s, int nseg, const int* y32,
                                              const float* s_label, float* loss_row, float* lse, float* cref,
@@ -1313,7 +1316,7 @@ __global__ __launch_bounds__(256) void k_lse(const float* seg_m, const float* se
   float M;
   row_lse(m, seg_s + (int64_t)c * nseg, nseg, c, y32, s_label, loss_row, lse, &M);
   const float c_old = cref[c];
-  if (!(M - c_old > kRefSpan)) return;  // the same decision in every thread of the block
+  if (!(y32[c] >= 0 && M > c_old)) return;  // the same decision in every thread of the block
   __syncthreads();                      // every thread has read the old reference
   if (threadIdx.x == 0) cref[c] = M;
   if (!q) return;
@@ -1321,7 +1324,7 @@ __global__ __launch_bounds__(256) void k_lse(const float* seg_m, const float* se
   for (int k = (int)threadIdx.x; k < (int)(ldq / KV); k += 256) {
     const float mj = m[k * KV / kSeg];
     if (mj == kNegInf) continue;  // a segment wholly past V: its q is 0
-    const float f = ex2((mj - M - fminf(mj - c_old, kRefSpan)) * kLog2e);
+    const float f = ex2((mj - M) * kLog2e);
     float v[KV];
     unpack(*(const u32x4*)(row + k * KV), v, (S*)nullptr);
 #pragma unroll
