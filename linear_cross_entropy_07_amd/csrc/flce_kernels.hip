@@ -68,6 +68,28 @@ constexpr int WN = TILE / (NW / 2);  // wave tile columns (N): 64 or 128
 #define FLCE_MFMA 32
 #endif
 constexpr int MB = FLCE_MFMA;    // edge of one MFMA output block
+// DMA placement in the unrolled main loop: 0 issues a step's loads at its start; 1 and 2 issue the
+// first operand's loads one after each of the first MFMAs of the step's first substep and the second
+// operand's one after each of the first MFMAs following the step's barrier (2: without a memory
+// clobber on the load statement).
+#ifndef FLCE_DMA_SPREAD
+#define FLCE_DMA_SPREAD 2
+#endif
+// In the explicit order: load d follows MFMA FLCE_DMA_FIRST + d * FLCE_DMA_STRIDE of its substep;
+// FLCE_DMA_BOTH_FIRST puts both operands' loads in the step's first substep (before the barrier);
+// FLCE_XORDER 1 reads the A fragments of a substep before its B fragments.
+#ifndef FLCE_DMA_FIRST
+#define FLCE_DMA_FIRST 0
+#endif
+#ifndef FLCE_DMA_STRIDE
+#define FLCE_DMA_STRIDE 1
+#endif
+#ifndef FLCE_DMA_BOTH_FIRST
+#define FLCE_DMA_BOTH_FIRST 0
+#endif
+#ifndef FLCE_XORDER
+#define FLCE_XORDER 0
+#endif
 static_assert(MB == 16 || MB == 32, "16x16 or 32x32 MFMA blocks");
 constexpr int NR = MB * MB / 64;  // accumulator registers per block and lane (4 or 16)
 constexpr int TBM = WM / MB;     // MFMA blocks per wave tile along M (8 or 4)
@@ -202,8 +224,16 @@ __device__ __forceinline__ void dma16(i32x4 desc, u32 voff, u32 lds) {
   // M0 must be written one instruction before an LDS-DMA load reads it. M0 is a reserved register for
   // the compiler (never allocated; its own users write it right before they read it), so it cannot
   // appear in a clobber list and nothing the compiler emits relies on M0 across this statement.
+#if FLCE_DMA_SPREAD == 2
+  // No memory clobber: fragment reads may be scheduled across the load. Every LDS byte a load writes
+  // is read only after a later s_waitcnt + s_barrier statement, which does clobber memory, and the
+  // slot it writes was last read before an earlier one; volatile statements keep their order.
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(desc), "s"(__builtin_amdgcn_readfirstlane(lds)));
+#else
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :: "v"(voff), "s"(desc), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+#endif
 }
 
 // Range-checked buffer accesses for epilogues: loads outside the range return 0, stores outside it
@@ -261,6 +291,9 @@ constexpr int kOpBytes = TILE * kStepBytes;        // per operand per stage
 constexpr int kStageBytes = 2 * kOpBytes;          // A + B
 constexpr int kDmaPerOp = kOpBytes / (NTHR * 16);  // DMA instructions per thread per operand
 constexpr int kLoadsPerStage = 2 * kDmaPerOp;
+constexpr bool kSpread = FLCE_DMA_SPREAD != 0;
+static_assert(!kSpread || (kStages >= 3 && FLCE_DMA_FIRST + (kDmaPerOp - 1) * FLCE_DMA_STRIDE < TBM * TBN),
+              "DMA spread: 3+ stages, every load after an MFMA of its substep");
 static_assert(kChunks == 4 || kChunks == 8, "64 or 128 bytes of K per step");
 static_assert(kStages >= 2 && kStages * kStageBytes <= 160 * 1024, "LDS ring must fit in 160 KiB");
 // vmcnt field encoding of s_waitcnt (gfx9): low 4 bits and bits 15:14; expcnt and lgkmcnt left at max.
@@ -290,16 +323,21 @@ struct OpK {
       kc[q] = (lane % kChunks) ^ swz(row);
     }
   }
-  __device__ __forceinline__ void issue(int ks, u32 lds) const {
+  __device__ __forceinline__ void issue_one(int ks, u32 lds, int q) const {
     const int wave = threadIdx.x >> 6;
+    const int k = ks * BK + kc[q] * KV;
+    dma16(desc, k < kmax ? rowoff[q] + (u32)(k * sizeof(T)) : kOOB, lds + (kDmaPerOp * wave + q) * 1024);
+  }
+  __device__ __forceinline__ void issue(int ks, u32 lds) const {
 #pragma unroll
-    for (int q = 0; q < kDmaPerOp; ++q) {
-      const int k = ks * BK + kc[q] * KV;
-      dma16(desc, k < kmax ? rowoff[q] + (u32)(k * sizeof(T)) : kOOB, lds + (kDmaPerOp * wave + q) * 1024);
-    }
+    for (int q = 0; q < kDmaPerOp; ++q) issue_one(ks, lds, q);
   }
   // fragment of rows rowbase + MB i + lane % MB for chunk kcol
   static constexpr int kFragReads = 1;  // LDS reads per fragment
+  __device__ __forceinline__ u32x4 frag1(const char* st, int rowbase, int kcol, int i) const {
+    const int row = rowbase + MB * i + (threadIdx.x & 63) % MB;
+    return *(const u32x4*)(st + row * kStepBytes + ((kcol ^ swz(row)) << 4));
+  }
   template <int NB>
   __device__ __forceinline__ void frag(const char* st, int rowbase, int kcol, u32x4 (&f)[NB]) const {
     const int lane = threadIdx.x & 63;
@@ -350,6 +388,10 @@ struct OpMN {
     const int nrows = kvalid - k0 < 0 ? 0 : (kvalid - k0 > BK ? BK : kvalid - k0);
     return make_desc(p + (int64_t)k0 * ldb, (u32)nrows * (u32)ldb);
   }
+  __device__ __forceinline__ void issue_one(int ks, u32 lds, int q) const {
+    const int wave = threadIdx.x >> 6;
+    dma16(step_desc(ks), off[q], lds + (kDmaPerOp * wave + q) * 1024);
+  }
   __device__ __forceinline__ void issue(int ks, u32 lds) const {
     const int wave = threadIdx.x >> 6;
     const i32x4 desc = step_desc(ks);
@@ -357,6 +399,31 @@ struct OpMN {
     for (int q = 0; q < kDmaPerOp; ++q) dma16(desc, off[q], lds + (kDmaPerOp * wave + q) * 1024);
   }
   static constexpr int kFragReads = sizeof(T) == 2 ? 2 : 4;  // LDS reads per fragment
+  __device__ __forceinline__ u32x4 frag1(const char* st, int colbase, int kcol, int i) const {
+    const int lane = threadIdx.x & 63;
+    u32x4 v;
+    if constexpr (sizeof(T) == 2) {
+      const int n = colbase + MB * i + (MB == 32 ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int k = 4 * (2 * kcol + r) + ((lane & 15) >> 2);  // kcol = frag_chunk(s, lane)
+        const char* a = st + k * ROWB + (((n >> 3) ^ (kMnXor * (k & 3))) << 4) + ((n & 7) << 1);
+        const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(size_t)lds_addr(a));
+        const u32x2 w = __builtin_bit_cast(u32x2, t);
+        v[2 * r] = w[0];
+        v[2 * r + 1] = w[1];
+      }
+    } else {
+      const int n = colbase + MB * i + lane % MB;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 4 * kcol + e;
+        v[e] = *(const u32*)(st + k * ROWB + (((n >> 2) ^ (kMnXor * (k & 3))) << 4) + ((n & 3) << 2));
+      }
+    }
+    return v;
+  }
   template <int NB>
   __device__ __forceinline__ void frag(const char* st, int colbase, int kcol, u32x4 (&f)[NB]) const {
     const int lane = threadIdx.x & 63;
@@ -465,10 +532,11 @@ __device__ __forceinline__ void gemm_main(const LA& la, const LB& lb, int kb, in
 
 // The same pipeline with the step loop unrolled by kStages: stage slots and LDS offsets are
 // compile-time constants and the loop body has no exits. The step count is rounded up to a multiple
-// of kStages; steps past ke load zeros (out of range) and add nothing. With INTERLEAVE the scheduler
-// places one fragment read between consecutive MFMAs, so LDS requests trickle instead of queueing
-// behind the DMA writes (better for K-contiguous first operands).
-template <typename T, bool INTERLEAVE, class LA, class LB>
+// of kStages; steps past ke load zeros (out of range) and add nothing. With RPM > 0 the scheduler
+// places RPM fragment reads after each MFMA until the substep's reads are placed, so LDS requests
+// trickle instead of queueing behind the DMA writes, and no read is left after the substep's last
+// MFMA (where the step's barrier, or the next substep's first MFMA, would wait for it in full).
+template <typename T, int RPM, class LA, class LB>
 __device__ __forceinline__ void gemm_main_u(const LA& la, const LB& lb, int kb, int ke, char* smem,
                                             facc (&acc)[TBM][TBN]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -491,15 +559,21 @@ __device__ __forceinline__ void gemm_main_u(const LA& la, const LB& lb, int kb, 
       const int ks = ks0 + t;
       const char* st = smem + t * kStageBytes;
       const int nslot = (t + kStages - 1) % kStages;
-      la.issue(ks + kStages - 1, lbase + nslot * kStageBytes);
-      lb.issue(ks + kStages - 1, lbase + nslot * kStageBytes + kOpBytes);
+      const u32 dst = lbase + nslot * kStageBytes;
+      if constexpr (!kSpread) {
+        la.issue(ks + kStages - 1, dst);
+        lb.issue(ks + kStages - 1, dst + kOpBytes);
+      }
 #pragma unroll
       for (int s = 0; s < kSub; ++s) {
         if (s + 1 < kSub) {
           la.frag(st, wm * WM, frag_chunk(s + 1, lane), fa[(s + 1) & 1]);
           lb.frag(st + kOpBytes, wn * WN, frag_chunk(s + 1, lane), fb[(s + 1) & 1]);
         } else {
-          __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
+          // the next step's stage must have landed: with the second operand's loads of this step
+          // still to come, only the steps after it and this step's first-operand loads may remain
+          __builtin_amdgcn_s_waitcnt(vmcnt_only(kSpread ? (kStages - 3) * kLoadsPerStage + kDmaPerOp
+                                                        : (kStages - 2) * kLoadsPerStage));
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           const char* nx = smem + ((t + 1) % kStages) * kStageBytes;
           la.frag(nx, wm * WM, frag_chunk(0, lane), fa[(s + 1) & 1]);
@@ -508,17 +582,121 @@ __device__ __forceinline__ void gemm_main_u(const LA& la, const LB& lb, int kb, 
 #pragma unroll
         for (int i = 0; i < TBM; ++i)
 #pragma unroll
-          for (int j = 0; j < TBN; ++j) mma(acc[i][j], fa[s & 1][i], fb[s & 1][j], (T*)nullptr);
-        if constexpr (INTERLEAVE) {
-          constexpr int nr = TBM * LA::kFragReads + TBN * LB::kFragReads, nm = TBM * TBN;
-          constexpr int np = nr < nm ? nr : nm;
-#pragma unroll
-          for (int q = 0; q < np; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          for (int j = 0; j < TBN; ++j) {
+            mma(acc[i][j], fa[s & 1][i], fb[s & 1][j], (T*)nullptr);
+            if constexpr (kSpread) {
+              // slot nslot was last read before the previous step's barrier
+              if (s == 0 && i * TBN + j < kDmaPerOp) la.issue_one(ks + kStages - 1, dst, i * TBN + j);
+              if (s == kSub - 1 && i * TBN + j < kDmaPerOp) lb.issue_one(ks + kStages - 1, dst + kOpBytes, i * TBN + j);
+            }
           }
-          if constexpr (nm > np) __builtin_amdgcn_sched_group_barrier(0x008, nm - np, 0);
-          if constexpr (nr > np) __builtin_amdgcn_sched_group_barrier(0x100, nr - np, 0);
+        if constexpr (RPM > 0) {
+          constexpr int nr = TBM * LA::kFragReads + TBN * LB::kFragReads, nm = TBM * TBN;
+          constexpr int gf = nr / RPM < nm ? nr / RPM : nm;               // MFMAs followed by RPM reads
+          constexpr int gp = gf < nm && gf * RPM < nr && nr - gf * RPM < RPM ? 1 : 0;  // one followed by fewer
+          constexpr int placed = gf * RPM + (gp ? nr - gf * RPM : 0);
+#pragma unroll
+          for (int q = 0; q < gf; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // RPM LDS reads
+          }
+          if constexpr (gp) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, nr - gf * RPM, 0);
+          }
+          if constexpr (nm > gf + gp) __builtin_amdgcn_sched_group_barrier(0x008, nm - gf - gp, 0);
+          if constexpr (nr > placed) __builtin_amdgcn_sched_group_barrier(0x100, nr - placed, 0);
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The unrolled pipeline with an explicit instruction order: each MFMA of a substep is followed by
+// the fragment reads assigned to it and, in the spread placement, by one DMA load, and nothing is
+// scheduled across these groups. The next substep's fragments are read in the order its MFMAs use
+// them (B_0, A_0, B_1, A_1, ..., then the remaining A), up to RPM LDS instructions after each
+// MFMA, so the last read of a substep is issued several MFMAs before the barrier that waits for it.
+template <int RPM, class LA, class LB>
+struct XOrder {
+  static constexpr int NFR = TBM + TBN, NM = TBM * TBN;
+  static constexpr bool is_b(int f) { return FLCE_XORDER ? f >= TBM : f < 2 * TBN ? (f % 2 == 0) : false; }
+  static constexpr int idx(int f) { return FLCE_XORDER ? (f < TBM ? f : f - TBM) : f < 2 * TBN ? f / 2 : f - TBN; }
+  static constexpr int reads(int f) { return is_b(f) ? LB::kFragReads : LA::kFragReads; }
+  static constexpr int group(int f) {
+    int c = 0;
+    for (int g = 0; g < f; ++g) c += reads(g);
+    return c / RPM < NM - 1 ? c / RPM : NM - 1;
+  }
+};
+template <typename T, int RPM, class LA, class LB>
+__device__ __forceinline__ void gemm_main_x(const LA& la, const LB& lb, int kb, int ke, char* smem,
+                                            facc (&acc)[TBM][TBN]) {
+  using O = XOrder<RPM, LA, LB>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+  for (int i = 0; i < TBM; ++i)
+#pragma unroll
+    for (int j = 0; j < TBN; ++j)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.0f;
+  const u32 lbase = lds_addr(smem);
+  __builtin_amdgcn_s_waitcnt(vmcnt_only((kStages - 2) * kLoadsPerStage));
+  asm volatile("s_barrier" ::: "memory");
+  u32x4 fa[2][TBM], fb[2][TBN];
+  la.frag(smem, wm * WM, frag_chunk(0, lane), fa[0]);
+  lb.frag(smem + kOpBytes, wn * WN, frag_chunk(0, lane), fb[0]);
+  for (int ks0 = kb; ks0 < ke; ks0 += kStages) {
+#pragma unroll
+    for (int t = 0; t < kStages; ++t) {
+      const int ks = ks0 + t;
+      const char* st = smem + t * kStageBytes;
+      const int nslot = (t + kStages - 1) % kStages;
+      const u32 dst = lbase + nslot * kStageBytes;
+      if constexpr (!kSpread) {
+        la.issue(ks + kStages - 1, dst);
+        lb.issue(ks + kStages - 1, dst + kOpBytes);
+      }
+#pragma unroll
+      for (int s = 0; s < kSub; ++s) {
+        const char* src = st;
+        int kcol = frag_chunk(s + 1, lane);
+        if (s + 1 == kSub) {
+          __builtin_amdgcn_s_waitcnt(vmcnt_only(kSpread && !FLCE_DMA_BOTH_FIRST
+                                                    ? (kStages - 3) * kLoadsPerStage + kDmaPerOp
+                                                    : (kStages - 2) * kLoadsPerStage));
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          src = smem + ((t + 1) % kStages) * kStageBytes;
+          kcol = frag_chunk(0, lane);
+        }
+        const int cb = s & 1, rb = (s + 1) & 1;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < O::NM; ++q) {
+          mma(acc[q / TBN][q % TBN], fa[cb][q / TBN], fb[cb][q % TBN], (T*)nullptr);
+#pragma unroll
+          for (int f = 0; f < O::NFR; ++f) {
+            if (O::group(f) == q) {
+              if (O::is_b(f))
+                fb[rb][O::idx(f)] = lb.frag1(src + kOpBytes, wn * WN, kcol, O::idx(f));
+              else
+                fa[rb][O::idx(f)] = la.frag1(src, wm * WM, kcol, O::idx(f));
+            }
+          }
+          if constexpr (kSpread) {
+            // slot nslot was last read before the previous step's barrier
+#pragma unroll
+            for (int d = 0; d < kDmaPerOp; ++d) {
+              if (q == FLCE_DMA_FIRST + d * FLCE_DMA_STRIDE) {
+                if (s == 0) la.issue_one(ks + kStages - 1, dst, d);
+                if (s == (FLCE_DMA_BOTH_FIRST ? 0 : kSub - 1)) lb.issue_one(ks + kStages - 1, dst + kOpBytes, d);
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -603,8 +781,10 @@ __device__ __forceinline__ void gemm_main16(const LA& la, const LB& lb, int kb, 
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Main-loop schedules of the GEMM core.
-enum Sched { kRolled = 0, kUnrolled = 1, kInterleaved = 2 };
+// Main-loop schedules of the GEMM core: rolled, unrolled, and unrolled with one or two fragment
+// reads placed after each MFMA.
+enum Sched { kRolled = 0, kUnrolled = 1, kInterleaved = 2, kInterleaved2 = 3, kExplicit1 = 4, kExplicit2 = 5,
+             kExplicit3 = 6 };
 template <typename T, int SCHED, class LA, class LB>
 __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int kb, int ke, char* smem,
                                           facc (&acc)[TBM][TBN]) {
@@ -619,11 +799,13 @@ __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int kb, in
   }
   gemm_prologue(la, lb, kb, smem);
   if constexpr (MB == 16)
-    gemm_main16<T, SCHED == kInterleaved && sizeof(T) == 2>(la, lb, kb, ke, smem, acc);
+    gemm_main16<T, SCHED >= kInterleaved && sizeof(T) == 2>(la, lb, kb, ke, smem, acc);
   else if constexpr (SCHED == kRolled)
     gemm_main<T>(la, lb, kb, ke, smem, acc);
+  else if constexpr (SCHED >= kExplicit1)
+    gemm_main_x<T, SCHED - kExplicit1 + 1>(la, lb, kb, ke, smem, acc);
   else
-    gemm_main_u<T, SCHED == kInterleaved>(la, lb, kb, ke, smem, acc);
+    gemm_main_u<T, SCHED == kInterleaved2 ? 2 : SCHED == kInterleaved ? 1 : 0>(la, lb, kb, ke, smem, acc);
 }
 
 // ---- kernel arguments ------------------------------------------------------------------------
@@ -679,17 +861,18 @@ struct DwArgs {
 #ifndef FLCE_GROUP_DW
 #define FLCE_GROUP_DW 4
 #endif
-// Main-loop schedule per product (0 rolled, 1 unrolled, 2 unrolled with one fragment read between
-// consecutive MFMAs); with two waves per SIMD the interleaved schedule measured best for all three
-// products on MI355X at the Llama-3-8B head.
+// Main-loop schedule per product (Sched: 0 rolled, 1 unrolled, 2 and 3 unrolled with one or two
+// fragment reads placed after each MFMA by the scheduler, 4 to 6 the explicit order with up to 1 to 3
+// LDS reads after each MFMA). On MI355X the explicit order with two reads per MFMA and the spread DMA
+// placement measured best for all three products at the Llama-3-8B and GPT-2 heads.
 #ifndef FLCE_SCHED_FWD
-#define FLCE_SCHED_FWD 2
+#define FLCE_SCHED_FWD 5
 #endif
 #ifndef FLCE_SCHED_DX
-#define FLCE_SCHED_DX 2
+#define FLCE_SCHED_DX 5
 #endif
 #ifndef FLCE_SCHED_DW
-#define FLCE_SCHED_DW (FLCE_MFMA == 16 ? 1 : 2)
+#define FLCE_SCHED_DW (FLCE_MFMA == 16 ? 1 : 5)
 #endif
 constexpr int kSchedFwd = FLCE_SCHED_FWD;
 constexpr int kSchedDx = FLCE_SCHED_DX;
