@@ -75,14 +75,15 @@ constexpr int MB = FLCE_MFMA;    // edge of one MFMA output block
 #ifndef FLCE_DMA_SPREAD
 #define FLCE_DMA_SPREAD 2
 #endif
-// In the explicit order: load d follows MFMA FLCE_DMA_FIRST + d * FLCE_DMA_STRIDE of its substep;
-// FLCE_DMA_BOTH_FIRST puts both operands' loads in the step's first substep (before the barrier);
-// FLCE_XORDER 1 reads the A fragments of a substep before its B fragments.
+// In the explicit order: load d follows MFMA FLCE_DMA_FIRST + d * FLCE_DMA_STRIDE of its substep
+// (MFMAs 2 and 4 measured best on MI355X: after the substep's first fragment reads, before its last
+// MFMAs); FLCE_DMA_BOTH_FIRST puts both operands' loads in the step's first substep (before the
+// barrier); FLCE_XORDER 1 reads the A fragments of a substep before its B fragments.
 #ifndef FLCE_DMA_FIRST
-#define FLCE_DMA_FIRST 0
+#define FLCE_DMA_FIRST 2
 #endif
 #ifndef FLCE_DMA_STRIDE
-#define FLCE_DMA_STRIDE 1
+#define FLCE_DMA_STRIDE 2
 #endif
 #ifndef FLCE_DMA_BOTH_FIRST
 #define FLCE_DMA_BOTH_FIRST 0
