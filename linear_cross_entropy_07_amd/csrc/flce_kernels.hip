@@ -915,10 +915,10 @@ __device__ __forceinline__ u32 qlds(int cl, int vl) {  // byte address of q(cl, 
 // Per-wave staging (FLCE_QSTAGE_WAVE, the default): each wave stages half of one column block at a
 // time, the MB rows of half its WM v values (one 128-byte line per row, 16-byte chunks XOR-swizzled by
 // the row), in an area of its own in the ring's last slot, and writes them out itself as whole lines
-// as soon as the half is complete. No block barrier is involved, the stores of one half overlap the
-// arithmetic of the next, and the other slots stay free. Measured on MI355X against staging the whole
-// tile through the ring (one barrier, then all threads store): logits GEMM 3.33 against 3.37 ms at
-// the Llama-3-8B head, 1.30 against 1.36 ms at the GPT-2 head.
+// as soon as the half is complete. No block barrier is involved and the stores of one half overlap
+// the arithmetic of the next. Measured on MI355X against staging the whole tile through the ring
+// (one barrier, then all threads store): logits GEMM 3.33 against 3.37 ms at the Llama-3-8B head,
+// 1.30 against 1.36 ms at the GPT-2 head.
 #ifndef FLCE_QSTAGE_WAVE
 #define FLCE_QSTAGE_WAVE 1
 #endif
@@ -934,19 +934,16 @@ __device__ __forceinline__ u32 qwlds(int cr, int vl) {  // q(row cr of the colum
 // For each column block j, a lane holds column c (a chunk row) and WM / (64 / MB) of the wave's 128
 // v values of that row: the 64 / MB lanes that share c (c + k MB) hold the rest, and the row's
 // segment statistics are combined across them with lane exchanges.
-template <typename T, bool CAP, bool EDGE, bool STORE_Q, bool QONLY, bool PRE, int J0, int JG>
+template <typename T, bool CAP, bool EDGE, bool STORE_Q, bool QONLY, int J0, int JG>
 __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, facc (&acc)[TBM][TBN], int v0, int c0,
-                                                  const int (&ylab)[TBN], const float (&crin)[TBN], char* smem) {
+                                                  const int (&ylab)[TBN], char* smem) {
   using S = typename Traits<T>::S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int vw = v0 + wm * WM, seg = vw / kSeg, col = lane % MB, vl0 = acc_row(0, lane);
   const float cap = a.softcap, icap = CAP ? 1.0f / cap : 0.0f;
-  // references of the lane's rows (0 past the chunk), consumed in phase 3; PRE: loaded by the caller
+  // references of the lane's rows (0 past the chunk), consumed in phase 3
   float cr[TBN];
-  if constexpr (PRE) {
-#pragma unroll
-    for (int j = J0; j < J0 + JG; ++j) cr[j] = crin[j];
-  } else {
+  {
     const rsrc_t rc = make_rsrc(a.cref, (int64_t)a.rows * 4);
 #pragma unroll
     for (int j = J0; j < J0 + JG; ++j) cr[j] = bload_f32(rc, (u32)(c0 + wn * WN + MB * j + col) * 4, 0);
@@ -1120,14 +1117,14 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, facc (&acc)[
   }
 }
 
-template <typename T, bool CAP, bool EDGE, bool STORE_Q, bool QONLY, bool PRE, int J0 = 0>
+template <typename T, bool CAP, bool EDGE, bool STORE_Q, bool QONLY, int J0 = 0>
 __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, facc (&acc)[TBM][TBN], int v0, int c0,
-                                             const int (&ylab)[TBN], const float (&crin)[TBN], char* smem) {
+                                             const int (&ylab)[TBN], char* smem) {
   // two column blocks at a time: enough independent work, few enough live values to stay in registers
   if constexpr (J0 < TBN) {
     constexpr int JG = TBN - J0 < 2 ? TBN - J0 : 2;
-    fwd_epilogue_part<T, CAP, EDGE, STORE_Q, QONLY, PRE, J0, JG>(a, acc, v0, c0, ylab, crin, smem);
-    fwd_epilogue<T, CAP, EDGE, STORE_Q, QONLY, PRE, J0 + JG>(a, acc, v0, c0, ylab, crin, smem);
+    fwd_epilogue_part<T, CAP, EDGE, STORE_Q, QONLY, J0, JG>(a, acc, v0, c0, ylab, smem);
+    fwd_epilogue<T, CAP, EDGE, STORE_Q, QONLY, J0 + JG>(a, acc, v0, c0, ylab, smem);
   }
 }
 
@@ -1147,81 +1144,43 @@ __device__ __forceinline__ void fwd_store_staged(const FwdArgs& a, int v0, int c
   }
 }
 
-// The persistent logits kernel (FLCE_FWD_PERSIST) runs the tiles b, b + gridDim.x, ... of one block
-// in turn: the next tile's first kStages - 1 stages of operands are issued right after a tile's main
-// loop, into the ring slots its epilogue leaves free (q is staged per wave in the last slot), so their
-// latency and the turnover of blocks are hidden behind the epilogue.
-#ifndef FLCE_FWD_PERSIST
-#define FLCE_FWD_PERSIST 0
-#endif
-static_assert(!FLCE_FWD_PERSIST || FLCE_QSTAGE_WAVE, "the persistent logits kernel stages q per wave");
-
 template <typename T>
 __device__ __forceinline__ void fwd_loaders(const FwdArgs& a, int v0, int c0, OpK<T>& la, OpMN<T>& lb) {
   la.init((const T*)a.W + (int64_t)v0 * a.H, a.H, (int)min<int64_t>(TILE, a.V - v0), (int)a.H);  // W rows v0..
   lb.init((const T*)a.XT + c0, a.ldt, (int)a.H, min(TILE, a.rows - c0));  // hidden^T: rows h, columns c0..
 }
-// the prologue of the tile at (v0, c0): stages 0 .. kStages-2 into ring slots 0 .. kStages-2
-template <typename T>
-__device__ __forceinline__ void fwd_prefetch(const FwdArgs& a, int v0, int c0, char* smem) {
-  OpK<T> la;
-  OpMN<T> lb;
-  fwd_loaders<T>(a, v0, c0, la, lb);
-  gemm_prologue(la, lb, 0, smem);
-}
-
 // One 256 x 256 tile of the logits product and its epilogue. STORE_Q = false is the forward-only
 // path: the row statistics and label logits are produced, the q tile is not stored. QONLY: q only.
-// PERSIST: the tile's prologue was issued by the caller; `next` asks for the prologue of the tile at
-// (nv0, nc0) once the main loop is done.
-template <typename T, bool STORE_Q, bool QONLY, bool PERSIST = false>
-__device__ __forceinline__ void fwd_tile(const FwdArgs& a, int v0, int c0, char* smem, bool next = false,
-                                         int nv0 = 0, int nc0 = 0) {
+template <typename T, bool STORE_Q, bool QONLY>
+__device__ __forceinline__ void fwd_tile(const FwdArgs& a, int v0, int c0, char* smem) {
   OpK<T> la;
   OpMN<T> lb;
   fwd_loaders<T>(a, v0, c0, la, lb);
-  // the labels (and, persistent, the row references) are loaded before the main loop, whose waits on
-  // the operand loads cover them
+  // the labels are loaded before the main loop, whose first wait on the operand loads covers them
   int ylab[TBN];
   fwd_labels(a, c0, ylab);
-  float crin[TBN];
-  if constexpr (PERSIST) {
-    const rsrc_t rc = make_rsrc(a.cref, (int64_t)a.rows * 4);
-    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) >> 1;
-#pragma unroll
-    for (int j = 0; j < TBN; ++j) crin[j] = bload_f32(rc, (u32)(c0 + wn * WN + MB * j + lane % MB) * 4, 0);
-  }
   facc acc[TBM][TBN];
   const int nk = (int)((a.H + OpK<T>::BK - 1) / OpK<T>::BK);
   static_assert(OpK<T>::BK == OpMN<T>::BK, "operands step through K together");
-  if constexpr (PERSIST) {
-    gemm_main_sched<T, kSchedFwd>(la, lb, 0, nk, smem, acc);
-    // the main loop ended with every wave past its last read of the ring and all loads landed; the
-    // epilogue stages in the last slot only
-    if (next) fwd_prefetch<T>(a, nv0, nc0, smem);
-  } else {
-    gemm_core<T, kSchedFwd>(la, lb, 0, nk, smem, acc);
-  }
+  gemm_core<T, kSchedFwd>(la, lb, 0, nk, smem, acc);
 
   // wave-uniform selection of the specialised epilogue
   const bool edge = v0 + (((int)threadIdx.x >> 6) & 1) * WM + WM > a.V;
   if (a.softcap > 0.0f) {
     if (edge)
-      fwd_epilogue<T, true, true, STORE_Q, QONLY, PERSIST>(a, acc, v0, c0, ylab, crin, smem);
+      fwd_epilogue<T, true, true, STORE_Q, QONLY>(a, acc, v0, c0, ylab, smem);
     else
-      fwd_epilogue<T, true, false, STORE_Q, QONLY, PERSIST>(a, acc, v0, c0, ylab, crin, smem);
+      fwd_epilogue<T, true, false, STORE_Q, QONLY>(a, acc, v0, c0, ylab, smem);
   } else {
     if (edge)
-      fwd_epilogue<T, false, true, STORE_Q, QONLY, PERSIST>(a, acc, v0, c0, ylab, crin, smem);
+      fwd_epilogue<T, false, true, STORE_Q, QONLY>(a, acc, v0, c0, ylab, smem);
     else
-      fwd_epilogue<T, false, false, STORE_Q, QONLY, PERSIST>(a, acc, v0, c0, ylab, crin, smem);
+      fwd_epilogue<T, false, false, STORE_Q, QONLY>(a, acc, v0, c0, ylab, smem);
   }
   if constexpr (STORE_Q && kStageQ<T> && !FLCE_QSTAGE_WAVE) {
     __syncthreads();
     fwd_store_staged<T>(a, v0, c0, smem);
   }
-  // (persistent: the next main loop's first barrier follows every wave's staging reads, whose data
-  // its q stores consumed, before any load into the last slot is issued)
 }
 
 template <typename T, bool STORE_Q, bool QONLY>
@@ -1229,27 +1188,8 @@ __global__ __launch_bounds__(NTHR) void k_fwd(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes];
   const int mt = (int)(a.V_pad / TILE), nt = (a.rows + TILE - 1) / TILE;
   int tm, tn;
-#if FLCE_FWD_PERSIST
-  // tiles b, b + gridDim.x, ... (gridDim.x a multiple of 8, or the tile count): tile t runs on the XCD
-  // (t mod 8) that one block per tile would give it, so the XCD-aware order is kept
-  const int ntiles = mt * nt;
-  int t = blockIdx.x;
-  grouped(xcd_remap(t, ntiles), mt, nt, kGroupFwd, tm, tn);
-  fwd_prefetch<T>(a, tm * TILE, tn * TILE, smem);
-  for (;;) {
-    const int t2 = t + (int)gridDim.x;
-    int tm2 = 0, tn2 = 0;
-    if (t2 < ntiles) grouped(xcd_remap(t2, ntiles), mt, nt, kGroupFwd, tm2, tn2);
-    fwd_tile<T, STORE_Q, QONLY, true>(a, tm * TILE, tn * TILE, smem, t2 < ntiles, tm2 * TILE, tn2 * TILE);
-    if (t2 >= ntiles) break;
-    t = t2;
-    tm = tm2;
-    tn = tn2;
-  }
-#else
   grouped(xcd_remap(blockIdx.x, gridDim.x), mt, nt, kGroupFwd, tm, tn);
   fwd_tile<T, STORE_Q, QONLY>(a, tm * TILE, tn * TILE, smem);
-#endif
 }
 
 // ---- grad_hidden = f . (q . W) -------------------------------------------------------------------
@@ -1781,12 +1721,7 @@ FwdArgs fwd_args(const Problem& p, const void* W, const Work& w, int64_t row0, i
 hipError_t launch_fwd(const Problem& p, const void* W, const Work& w, int64_t row0, int64_t rows,
                       bool store_q, hipStream_t stream, VSlice vs, bool qonly) {
   const FwdArgs a = fwd_args(p, W, w, row0, rows, vs);
-  unsigned grid = (unsigned)((a.V_pad / TILE) * ((rows + TILE - 1) / TILE));
-  if (FLCE_FWD_PERSIST) {
-    // one block per CU (the LDS ring allows no more), a multiple of 8 so that blocks keep their XCD
-    const unsigned nb = (unsigned)(p.ncu > 8 ? p.ncu / 8 * 8 : 8);
-    if (grid > nb) grid = nb;
-  }
+  const unsigned grid = (unsigned)((a.V_pad / TILE) * ((rows + TILE - 1) / TILE));
   if (!store_q && qonly) return hipErrorInvalidValue;
   if (p.dtype == 0) {
     if (!store_q)
