@@ -68,28 +68,19 @@ constexpr int WN = TILE / (NW / 2);  // wave tile columns (N): 64 or 128
 #define FLCE_MFMA 32
 #endif
 constexpr int MB = FLCE_MFMA;    // edge of one MFMA output block
-// DMA placement in the unrolled main loop: 0 issues a step's loads at its start; 1 and 2 issue the
-// first operand's loads one after each of the first MFMAs of the step's first substep and the second
-// operand's one after each of the first MFMAs following the step's barrier (2: without a memory
-// clobber on the load statement).
+// DMA placement in the unrolled main loop: 0 issues a step's loads at its start; 1 (the default)
+// spreads them, the first operand's loads one after each of a few MFMAs of the step's first substep
+// and the second operand's one after each of a few MFMAs following the step's barrier. In the
+// explicit order load d follows MFMA FLCE_DMA_FIRST + d * FLCE_DMA_STRIDE of its substep (MFMAs 2 and 4
+// measured best on MI355X: after the substep's first fragment reads, before its last MFMAs).
 #ifndef FLCE_DMA_SPREAD
-#define FLCE_DMA_SPREAD 2
+#define FLCE_DMA_SPREAD 1
 #endif
-// In the explicit order: load d follows MFMA FLCE_DMA_FIRST + d * FLCE_DMA_STRIDE of its substep
-// (MFMAs 2 and 4 measured best on MI355X: after the substep's first fragment reads, before its last
-// MFMAs); FLCE_DMA_BOTH_FIRST puts both operands' loads in the step's first substep (before the
-// barrier); FLCE_XORDER 1 reads the A fragments of a substep before its B fragments.
 #ifndef FLCE_DMA_FIRST
 #define FLCE_DMA_FIRST 2
 #endif
 #ifndef FLCE_DMA_STRIDE
 #define FLCE_DMA_STRIDE 2
-#endif
-#ifndef FLCE_DMA_BOTH_FIRST
-#define FLCE_DMA_BOTH_FIRST 0
-#endif
-#ifndef FLCE_XORDER
-#define FLCE_XORDER 0
 #endif
 static_assert(MB == 16 || MB == 32, "16x16 or 32x32 MFMA blocks");
 constexpr int NR = MB * MB / 64;  // accumulator registers per block and lane (4 or 16)
@@ -225,7 +216,7 @@ __device__ __forceinline__ void dma16(i32x4 desc, u32 voff, u32 lds) {
   // M0 must be written one instruction before an LDS-DMA load reads it. M0 is a reserved register for
   // the compiler (never allocated; its own users write it right before they read it), so it cannot
   // appear in a clobber list and nothing the compiler emits relies on M0 across this statement.
-#if FLCE_DMA_SPREAD == 2
+#if FLCE_DMA_SPREAD
   // No memory clobber: fragment reads may be scheduled across the load. Every LDS byte a load writes
   // is read only after a later s_waitcnt + s_barrier statement, which does clobber memory, and the
   // slot it writes was last read before an earlier one; volatile statements keep their order.
@@ -623,8 +614,8 @@ __device__ __forceinline__ void gemm_main_u(const LA& la, const LB& lb, int kb, 
 template <int RPM, class LA, class LB>
 struct XOrder {
   static constexpr int NFR = TBM + TBN, NM = TBM * TBN;
-  static constexpr bool is_b(int f) { return FLCE_XORDER ? f >= TBM : f < 2 * TBN ? (f % 2 == 0) : false; }
-  static constexpr int idx(int f) { return FLCE_XORDER ? (f < TBM ? f : f - TBM) : f < 2 * TBN ? f / 2 : f - TBN; }
+  static constexpr bool is_b(int f) { return f < 2 * TBN ? (f % 2 == 0) : false; }
+  static constexpr int idx(int f) { return f < 2 * TBN ? f / 2 : f - TBN; }
   static constexpr int reads(int f) { return is_b(f) ? LB::kFragReads : LA::kFragReads; }
   static constexpr int group(int f) {
     int c = 0;
@@ -666,9 +657,8 @@ __device__ __forceinline__ void gemm_main_x(const LA& la, const LB& lb, int kb, 
         const char* src = st;
         int kcol = frag_chunk(s + 1, lane);
         if (s + 1 == kSub) {
-          __builtin_amdgcn_s_waitcnt(vmcnt_only(kSpread && !FLCE_DMA_BOTH_FIRST
-                                                    ? (kStages - 3) * kLoadsPerStage + kDmaPerOp
-                                                    : (kStages - 2) * kLoadsPerStage));
+          __builtin_amdgcn_s_waitcnt(vmcnt_only(kSpread ? (kStages - 3) * kLoadsPerStage + kDmaPerOp
+                                                        : (kStages - 2) * kLoadsPerStage));
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           src = smem + ((t + 1) % kStages) * kStageBytes;
           kcol = frag_chunk(0, lane);
@@ -693,7 +683,7 @@ __device__ __forceinline__ void gemm_main_x(const LA& la, const LB& lb, int kb, 
             for (int d = 0; d < kDmaPerOp; ++d) {
               if (q == FLCE_DMA_FIRST + d * FLCE_DMA_STRIDE) {
                 if (s == 0) la.issue_one(ks + kStages - 1, dst, d);
-                if (s == (FLCE_DMA_BOTH_FIRST ? 0 : kSub - 1)) lb.issue_one(ks + kStages - 1, dst + kOpBytes, d);
+                if (s == kSub - 1) lb.issue_one(ks + kStages - 1, dst + kOpBytes, d);
               }
             }
           }
