@@ -90,8 +90,10 @@ int flce_destroy(flce_handle h);
  * device call). h may be NULL (default configuration). The workspace holds one chunk of
  * logits-derived values ([chunk_rows][V rounded up to 256], bf16 for FLCE_BF16, fp32 for
  * FLCE_FP32), per-(row, 128-wide V segment) statistics, per-row data, split-K partials of
- * grad_hidden, and two [chunk_rows][H] copies of the chunk's hidden rows (transposed; scaled by the
- * per-row factor of the backward). It never grows with BT beyond O(BT) bytes of per-row data.
+ * grad_hidden, two [chunk_rows][H] copies of the chunk's hidden rows (transposed; scaled by the
+ * per-row factor of the backward) and, for plans of several chunks whose grad_W grid leaves its last
+ * wave of 256 x 256 tiles under half full, fp32 partial tiles of that wave (at most one per compute
+ * unit). It never grows with BT beyond O(BT) bytes of per-row data.
  * Returns FLCE_OK and writes *bytes, or FLCE_ERR_INVALID_ARG. */
 int flce_workspace_size(flce_handle h, int64_t BT, int64_t H, int64_t V, int dtype, size_t* bytes);
 

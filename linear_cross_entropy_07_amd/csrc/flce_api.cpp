@@ -93,7 +93,8 @@ int dx_splits(int64_t rows, int64_t H, int64_t V_pad, int dtype, int ncu) {
 
 struct Layout {
   size_t off_e, off_m, off_s, off_y, off_sl, off_loss, off_cref, off_lse, off_fs, off_part, off_xt, off_xf, off_params,
-      total;
+      off_tail, total;
+  bool tail = false;  // room for grad_W's split last wave
   int splits;
   int64_t chunk_rows;
 };
@@ -128,6 +129,12 @@ Layout layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t cmax, int ncu
   L.off_part = take(L.splits > 1 ? (size_t)L.splits * rows * H * 4 : 0);
   L.off_xt = take((size_t)rows * H * esz);
   L.off_xf = take(backward ? (size_t)rows * H * esz : 0);
+  // grad_W's split last wave (its partial 256 x 256 fp32 tiles), for calls of several chunks: a
+  // one-chunk call keeps each grad_W tile one sum in K order, as the recompute mode does
+  int tail = 0;
+  const int tsplits = backward && n > 1 ? flce::dw_tail_plan(V, H, rows, dtype, ncu, &tail) : 1;
+  L.tail = tsplits > 1;
+  L.off_tail = take(L.tail ? (size_t)tail * tsplits * flce::kTile * flce::kTile * 4 : 0);
   L.total = off;
   return L;
 }
@@ -332,6 +339,7 @@ Call make_call(flce_ctx* h, const Layout& L, const Rows& R, int64_t H, int64_t V
   w.params = (flce::DevParams*)(base + L.off_params);
   w.xt = base + L.off_xt;
   w.xf = base + L.off_xf;
+  w.dw_tail = L.tail ? (float*)(base + L.off_tail) : nullptr;
   w.chunk_cap = L.chunk_rows;
   return c;
 }

@@ -54,6 +54,7 @@ struct Work {
   float* dx_part;      // [splits][chunk_rows][H] fp32 split-K partials of grad_hidden (may be null)
   void* xt;            // [H][chunk_cap] the current chunk of hidden, transposed
   void* xf;            // [chunk_cap][H] f times the current chunk's rows of hidden (grad_W operand)
+  float* dw_tail;      // [tail][splits][256][256] fp32 partial tiles of grad_W's split last wave (null: no split)
   int64_t chunk_cap;   // row capacity of one chunk (a multiple of 256)
   DevParams* params;   // in the workspace
 };
@@ -107,6 +108,9 @@ hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_
 hipError_t launch_zero_rows(const Problem& p, void* grad_hidden, int64_t B, int64_t off, hipStream_t stream);
 hipError_t launch_dx_reduce(const Problem& p, const Work& w, void* grad_hidden, int64_t row0, int64_t rows,
                             int splits, hipStream_t stream);
+// grad_W's last wave: the number of K parts its tiles are split into (1: none) and, through `tail`,
+// how many tiles that wave has, for a launch over V x H with `rows` of K on `ncu` CUs.
+int dw_tail_plan(int64_t V, int64_t H, int64_t rows, int dtype, int ncu, int* tail);
 hipError_t launch_dw(const Problem& p, const Work& w, float* grad_W, int64_t rows, bool accumulate,
                      hipStream_t stream, VSlice vs = VSlice{});
 hipError_t launch_finalize(const Problem& p, const Work& w, float* loss, hipStream_t stream);

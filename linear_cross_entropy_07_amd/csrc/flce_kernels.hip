@@ -842,6 +842,10 @@ struct DwArgs {
   float* dW;
   int64_t H, V, V_pad;
   int rows, accumulate;
+  // the last wave's tiles split along K: tiles [full, mt * nt) of the grouped order are computed as
+  // tail_splits partial sums each, written to tail_part and added by k_dw_tail
+  int full, tail_splits;
+  float* tail_part;   // [tiles - full][tail_splits][256][256]
 };
 
 // Tile-row group sizes of the grouped tile order (measured on MI355X at the Llama-3-8B head). Each
@@ -1333,18 +1337,45 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes];
 
   const int mt = (int)((a.V + TILE - 1) / TILE), nt = (int)((a.H + TILE - 1) / TILE);
-  int tm, tn;
-  grouped(xcd_remap(blockIdx.x, gridDim.x), mt, nt, kGroupDw, tm, tn);
+  const int nk = (a.rows + OpMN<T>::BK - 1) / OpMN<T>::BK;
+  int tm, tn, kb = 0, ke = nk, part = -1, ti = 0;
+  if ((int)blockIdx.x < a.full) {
+    grouped(xcd_remap(blockIdx.x, a.full), mt, nt, kGroupDw, tm, tn);
+  } else {
+    // a part of one of the last wave's tiles: K steps [nk p / S, nk (p + 1) / S)
+    const int e = (int)blockIdx.x - a.full;
+    ti = e / a.tail_splits;
+    part = e % a.tail_splits;
+    grouped(a.full + ti, mt, nt, kGroupDw, tm, tn);
+    kb = (int)((int64_t)nk * part / a.tail_splits);
+    ke = (int)((int64_t)nk * (part + 1) / a.tail_splits);
+  }
   const int v0 = tm * TILE, h0 = tn * TILE;
 
+  // only the block's K range is loaded: the rounded-up steps past ke of the unrolled loop load zeros
+  const int kend = min(a.rows, ke * OpMN<T>::BK);
   OpMN<T> la;  // q^T: source rows are chunk rows (K), columns are v (M); v0 + 256 <= V_pad
-  la.init((const T*)a.ws + v0, a.V_pad, a.rows, TILE);
+  la.init((const T*)a.ws + v0, a.V_pad, kend, TILE);
   OpMN<T> lb;  // hidden_f: source rows are chunk rows (K), columns h
-  lb.init((const T*)a.X + h0, a.H, a.rows, (int)min<int64_t>(TILE, a.H - h0));
+  lb.init((const T*)a.X + h0, a.H, kend, (int)min<int64_t>(TILE, a.H - h0));
 
-  const int nk = (a.rows + OpMN<T>::BK - 1) / OpMN<T>::BK;
   facc acc[TBM][TBN];
-  gemm_core<T, kSchedDw>(la, lb, 0, nk, smem, acc);
+  gemm_core<T, kSchedDw>(la, lb, kb, ke, smem, acc);
+  if (part >= 0) {
+    // a partial tile: the whole 256 x 256 fp32 block (zeros past V or H) to its own slot
+    float* pt = a.tail_part + ((int64_t)ti * a.tail_splits + part) * (TILE * TILE);
+    const rsrc_t rp = make_rsrc(pt, (int64_t)TILE * TILE * 4);
+    const AccAddr<4> ap(TILE, TILE);
+#pragma unroll
+    for (int i = 0; i < TBM; ++i) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int j = 0; j < TBN; ++j) bstore_f32(rp, ap.col[j], ap.row(i, r), acc[i][j][r]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
+  }
 
   // row-major [V][H] fp32 tile at (v0, h0): written (first chunk) or read-modify-written (later
   // chunks); a row block's loads are all issued before its adds and stores
@@ -1383,6 +1414,31 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
         for (int j = 0; j < TBN; ++j) bstore_f32(rd, ad.col[j], ad.row(i, r), acc[i][j][r]);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+}
+
+// grad_W tiles of a split last wave: the partial sums added in a fixed order (part 0, 1, ...), then
+// written or added to grad_W. One thread per four consecutive columns of one row of one tile.
+__global__ __launch_bounds__(256) void k_dw_tail(const float* part, int splits, int full, int mt, int nt,
+                                                 float* dW, int64_t H, int64_t V, int accumulate) {
+  constexpr int kQuads = TILE * TILE / 4;  // per tile
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int ti = (int)(g / kQuads), e = (int)(g % kQuads) * 4;
+  int tm, tn;
+  grouped(full + ti, mt, nt, kGroupDw, tm, tn);
+  const int64_t v = (int64_t)tm * TILE + e / TILE, h = (int64_t)tn * TILE + e % TILE;
+  if (v >= V || h >= H) return;
+  const float* pt = part + (int64_t)ti * splits * (TILE * TILE) + e;
+  f32x4 s = *(const f32x4*)pt;
+  for (int k = 1; k < splits; ++k) s += *(const f32x4*)(pt + (int64_t)k * (TILE * TILE));
+  float* d = dW + v * H + h;
+  if ((H & 3) == 0) {  // four whole, 16-byte aligned elements of the row (h and H multiples of 4)
+    if (accumulate) s += *(const f32x4*)d;
+    *(f32x4*)d = s;
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (h + c < H) d[c] = accumulate ? d[c] + s[c] : s[c];
   }
 }
 
@@ -1841,6 +1897,19 @@ hipError_t launch_zero_rows(const Problem& p, void* grad_hidden, int64_t B, int6
   return hipGetLastError();
 }
 
+int dw_tail_plan(int64_t V, int64_t H, int64_t rows, int dtype, int ncu, int* tail) {
+  // a last wave under half full is split along K, into at most 4 parts of at least 2 ring depths
+  const int64_t tiles = ((V + TILE - 1) / TILE) * ((H + TILE - 1) / TILE);
+  if (ncu <= 0) ncu = 256;
+  const int t = (int)(tiles % ncu);
+  const int64_t bk = kStepBytes / (dtype == 0 ? 2 : 4), nk = (rows + bk - 1) / bk;
+  int splits = t > 0 && 2 * t <= ncu ? ncu / t : 1;
+  if (splits > 4) splits = 4;
+  while (splits > 1 && nk / splits < 2 * kStages) --splits;
+  *tail = splits > 1 ? t : 0;
+  return splits;
+}
+
 hipError_t launch_dw(const Problem& p, const Work& w, float* grad_W, int64_t rows, bool accumulate,
                      hipStream_t stream, VSlice vs) {
   if (vs.vn < 0) vs = VSlice{0, p.V};
@@ -1854,11 +1923,23 @@ hipError_t launch_dw(const Problem& p, const Work& w, float* grad_W, int64_t row
   a.V_pad = V_pad;
   a.rows = (int)rows;
   a.accumulate = accumulate ? 1 : 0;
-  const unsigned grid = (unsigned)(((vs.vn + TILE - 1) / TILE) * ((p.H + TILE - 1) / TILE));
+  const int mt = (int)((vs.vn + TILE - 1) / TILE), nt = (int)((p.H + TILE - 1) / TILE), tiles = mt * nt;
+  int tail = 0;
+  const int splits = w.dw_tail ? dw_tail_plan(vs.vn, p.H, rows, p.dtype, p.ncu, &tail) : 1;
+  a.full = splits > 1 ? tiles - tail : tiles;
+  a.tail_splits = splits;
+  a.tail_part = w.dw_tail;
+  const unsigned grid = (unsigned)(a.full + (splits > 1 ? tail * splits : 0));
   if (p.dtype == 0)
     k_dw<__bf16><<<grid, NTHR, 0, stream>>>(a);
   else
     k_dw<float><<<grid, NTHR, 0, stream>>>(a);
+  if (splits > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_dw_tail<<<(unsigned)tail * (TILE * TILE / 4 / 256), 256, 0, stream>>>(w.dw_tail, splits, a.full, mt, nt,
+                                                                           a.dW, p.H, vs.vn, a.accumulate);
+  }
   return hipGetLastError();
 }
 

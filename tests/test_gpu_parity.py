@@ -217,6 +217,20 @@ def test_chunking_invariance_and_determinism():
     assert a2[0] == a[0] and np.array_equal(a2[1], a[1]) and np.array_equal(a2[2], a[2])
 
 
+def test_grad_w_split_last_wave():
+    """grad_W tiles of a sparse last wave are computed as K parts and added in a fixed order (calls of
+    several chunks): 3000 rows in chunks of 1024 give 12 grad_W tiles per chunk, each split 4 ways, the
+    later chunks accumulating. Against the oracle, and bitwise repeatable."""
+    announce("grad_W last-wave split: BT 3000, H 256, V 3000, chunks of 1024")
+    w = inputs.custom(BT=3000, H=256, V=3000, dtype="bf16", ignore_frac=0.05, w_std=0.05, name="tail")
+    X, W, y = inputs.make_inputs(w, seed=14)
+    e = eng(1024)
+    a = run_gpu(e, X, W, y)
+    b = run_gpu(e, X, W, y)
+    assert a[0] == b[0] and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+    check_against_oracle(a, X, W, y, "bf16")
+
+
 def test_autograd_wrapper_scales_by_upstream_grad():
     dev = device()
     announce("autograd wrapper, loss / 4")
