@@ -21,7 +21,8 @@
 //   k_dx      grad_hidden chunk = f . (q . W) on MFMA (W read MN-contiguous, transposed by the LDS
 //             transpose reads on its way to the matrix cores; f applied to each output row).
 //   k_dw      grad_W (+)= q^T . hidden_f on MFMA; both operands read MN-contiguous and transposed the
-//             same way; fp32 accumulation in place across chunks.
+//             same way; fp32 accumulation in place across chunks. A last wave of tiles under half
+//             full is split along K into fp32 partials, which k_dw_tail adds in a fixed order.
 // So the softmax is rebuilt from the stored softmax input and the small per-row max/sum statistics,
 // and dlogits are never written: the backward GEMMs take q as it was stored and the per-row factor
 // f enters by linearity (an output-row scale for grad_hidden, a scaled copy of the chunk's hidden
@@ -31,7 +32,8 @@
 // each wave a 128 x 64 part as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (or 32x32x2f32 for fp32
 // inputs; FLCE_MFMA=16 selects 8 x 4 blocks of 16x16x32 instead). Operands reach LDS by DMA (buffer
 // loads that write LDS directly) into a ring of kStages stages of kStepBytes of K per row,
-// XOR-swizzled against bank conflicts.
+// XOR-swizzled against bank conflicts, and the main loop's instruction order is fixed in the source:
+// each MFMA is followed by the fragment reads and DMA loads assigned to it.
 #include <mutex>
 
 #include "flce_internal.h"
@@ -457,11 +459,11 @@ struct OpMN {
 // out as acc_row describes.
 //
 // K is consumed in steps of kStepBytes through a ring of kStages LDS stages filled by DMA, kStages-1
-// steps ahead; a step's DMA is issued at its start, into the slot the previous step read. A step is
-// kSub substeps of 16 MFMAs; the fragments of substep s+1 are read while substep s runs, and those
-// of the next step's substep 0 right after the step's single barrier, while its last substep runs.
-// Prologue: DMA of the first kStages-1 steps (no waits), so that it can be issued early, e.g. while
-// the previous tile of a persistent block is still in its epilogue.
+// steps ahead, into the slot the previous step read: issued at the step's start, or (FLCE_DMA_SPREAD)
+// the first operand's loads within the step's first substep and the second operand's after its
+// barrier. A step is kSub substeps of TBM x TBN MFMAs per wave; the fragments of substep s+1 are
+// read while substep s runs, and those of the next step's substep 0 right after the step's single
+// barrier, while its last substep runs. Prologue: DMA of the first kStages-1 steps (no waits).
 template <class LA, class LB>
 __device__ __forceinline__ void gemm_prologue(const LA& la, const LB& lb, int kb, char* smem) {
   const u32 lbase = lds_addr(smem);
