@@ -1314,22 +1314,29 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
 }
 
 // Fixed-order sum of the split-K partials of grad_hidden times the row's factor f, placed by the row
-// map (and added to what the row holds with `accumulate`). Blocks: x over H, y over chunk rows
-// (grid-stride).
+// map (and added to what the row holds with `accumulate`). Four consecutive columns per thread:
+// 16-byte partial loads and one 4-element store (row starts are multiples of 16 bytes, H of 8).
 template <typename T>
 __global__ __launch_bounds__(256) void k_dx_reduce(const float* part, int splits, int rows, int64_t H, T* out,
-                                                   RowMap gmap, int64_t row0, int accumulate, const float* fscale) {
-  const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (h >= H) return;
-  const int64_t n = (int64_t)rows * H;
-  for (int c = blockIdx.y; c < rows; c += gridDim.y) {
-    const int64_t i = (int64_t)c * H + h;
-    float s = 0.0f;
-    for (int k = 0; k < splits; ++k) s += part[(int64_t)k * n + i];
-    s *= fscale[c];
-    T* dst = out + gmap(row0 + c) + h;
-    if (accumulate) s += (float)*dst;
-    *dst = (T)s;
+                                                    RowMap gmap, int64_t row0, int accumulate, const float* fscale) {
+  const int64_t hq = H / 4, g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (int64_t)rows * hq) return;
+  const int c = (int)(g / hq);
+  const int64_t h = (g - c * hq) * 4, n = (int64_t)rows * H, i = (int64_t)c * H + h;
+  f32x4 s = *(const f32x4*)(part + i);
+  for (int k = 1; k < splits; ++k) s += *(const f32x4*)(part + (int64_t)k * n + i);
+  s *= fscale[c];
+  T* dst = out + gmap(row0 + c) + h;
+  if constexpr (sizeof(T) == 2) {
+    if (accumulate) {
+      const bf16x4 o = *(const bf16x4*)dst;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] += (float)o[e];
+    }
+    *(u32x2*)dst = pack4_bf16(s[0], s[1], s[2], s[3]);
+  } else {
+    if (accumulate) s += *(const f32x4*)dst;
+    *(f32x4*)dst = s;
   }
 }
 
@@ -1878,8 +1885,12 @@ hipError_t launch_dx(const Problem& p, const void* W, const Work& w, void* grad_
 
 hipError_t launch_dx_reduce(const Problem& p, const Work& w, void* grad_hidden, int64_t row0, int64_t rows,
                             int splits, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.H + 255) / 256), (unsigned)(rows < 65535 ? rows : 65535));
   const int acc = p.acc_gh ? 1 : 0;
+  // every output row starts on a multiple of 16 bytes (the entry points check the strides)
+  const RowMap& m = p.gmap;
+  if ((p.H & 3) != 0 || (m.sb & 3) != 0 || (m.st & 3) != 0 || (m.base & 3) != 0 || (((uintptr_t)grad_hidden) & 15) != 0)
+    return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((rows * (p.H / 4) + 255) / 256);
   if (p.dtype == 0)
     k_dx_reduce<__bf16><<<grid, 256, 0, stream>>>(w.dx_part, splits, (int)rows, p.H, (__bf16*)grad_hidden, p.gmap,
                                                   row0, acc, w.fscale + row0);
