@@ -1494,15 +1494,23 @@ __global__ __launch_bounds__(1024) void k_prepass(const int64_t* labels, RowMap 
                                                   int* y32, DevParams* prm, int* status_out) {
   __shared__ int s_cnt[1024];
   __shared__ int s_bad[1024];
+  // thread i takes rows i, i + 1024, ...; the labels of eight of them are loaded together
+  constexpr int kB = 8;
   int cnt = 0, bad = 0;
-  for (int64_t t = threadIdx.x; t < BT; t += 1024) {
-    const int64_t y = labels[lmap(t)];
-    const bool counted = y != ignore_index;
-    const bool out = counted && (y < 0 || y >= V);
-    const bool ok = counted && !out;
-    y32[t] = ok ? (int)y : -1;
-    cnt += ok;
-    bad |= out;
+  for (int64_t t0 = threadIdx.x; t0 < BT; t0 += 1024 * kB) {
+    int64_t yv[kB];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) yv[k] = t0 + 1024 * k < BT ? labels[lmap(t0 + 1024 * k)] : ignore_index;
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      const int64_t t = t0 + 1024 * k, y = yv[k];
+      const bool counted = y != ignore_index;
+      const bool out = counted && (y < 0 || y >= V);
+      const bool ok = counted && !out;
+      if (t < BT) y32[t] = ok ? (int)y : -1;
+      cnt += ok;
+      bad |= out;
+    }
   }
   s_cnt[threadIdx.x] = cnt;
   s_bad[threadIdx.x] = bad;
@@ -1525,35 +1533,43 @@ __global__ __launch_bounds__(1024) void k_prepass(const int64_t* labels, RowMap 
 
 // Per-row log-sum-exp from the per-(row, 128-wide segment) statistics of the logits epilogue, in a
 // fixed order (max over the segments, then the rescaled sum), and the row's loss term (0 on rows that
-// do not count). One 256-thread block per row; every thread returns the row's lse.
+// do not count). One wave per row: lane l takes segments l, l + 64, ... in that order, loaded eight
+// at a time; every lane returns the row's lse and, through max_out, its largest segment reference.
 __device__ __forceinline__ float row_lse(const float* m, const float* sp, int nseg, int c, const int* y32,
                                          const float* s_label, float* loss_row, float* lse_out,
                                          float* max_out = nullptr) {
-  __shared__ float red[4];
-  __shared__ float s_lse, s_max;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kB = 8;
+  const int lane = threadIdx.x & 63;
   float M = kNegInf;
-  for (int j = threadIdx.x; j < nseg; j += 256) M = fmaxf(M, m[j]);
+  for (int j0 = lane; j0 < nseg; j0 += 64 * kB) {
+    float v[kB];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) v[k] = j0 + 64 * k < nseg ? m[j0 + 64 * k] : kNegInf;
+#pragma unroll
+    for (int k = 0; k < kB; ++k) M = fmaxf(M, v[k]);
+  }
   M = wave_max(M);
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  if (threadIdx.x == 0) s_max = M;
-  __syncthreads();
-  float Ssum = 0.0f;
-  for (int j = threadIdx.x; j < nseg; j += 256) Ssum += sp[j] * ex2((m[j] - M) * kLog2e);
-  Ssum = wave_sum(Ssum);
-  if (lane == 0) red[wave] = Ssum;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const float lse = M + __logf((red[0] + red[1]) + (red[2] + red[3]));
-    s_lse = lse;
+  float S = 0.0f;
+  for (int j0 = lane; j0 < nseg; j0 += 64 * kB) {
+    float mv[kB], sv[kB];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      const bool in = j0 + 64 * k < nseg;
+      mv[k] = in ? m[j0 + 64 * k] : kNegInf;
+      sv[k] = in ? sp[j0 + 64 * k] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kB; ++k)
+      if (j0 + 64 * k < nseg) S += sv[k] * ex2((mv[k] - M) * kLog2e);
+  }
+  S = wave_sum(S);
+  const float lse = M + __logf(S);
+  if (lane == 0) {
     loss_row[c] = y32[c] >= 0 ? lse - s_label[c] : 0.0f;
     if (lse_out) lse_out[c] = lse;
   }
-  __syncthreads();
-  if (max_out) *max_out = s_max;
-  return s_lse;
+  if (max_out) *max_out = M;
+  return lse;
 }
 
 // Reference of each row of a chunk (one wave per row): c = the softcapped label logit, the dot product
@@ -1594,20 +1610,21 @@ __global__ __launch_bounds__(256) void k_rowref(const T* X, RowMap hmap, int64_t
 template <typename T>
 __global__ __launch_bounds__(256) void k_lse(const float* seg_m, const float* seg_s, int nseg, const int* y32,
                                              const float* s_label, float* loss_row, float* lse, float* cref,
-                                             void* q, int64_t ldq) {
+                                             void* q, int64_t ldq, int rows) {
   using S = typename Traits<T>::S;
   constexpr int KV = Traits<T>::KV;
-  const int c = blockIdx.x;
+  const int c = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (c >= rows) return;
   const float* m = seg_m + (int64_t)c * nseg;
   float M;
   row_lse(m, seg_s + (int64_t)c * nseg, nseg, c, y32, s_label, loss_row, lse, &M);
+  // every lane has read the old reference (one load instruction of the wave) before lane 0 replaces it
   const float c_old = cref[c];
-  if (!(y32[c] >= 0 && M > c_old)) return;  // the same decision in every thread of the block
-  __syncthreads();                      // every thread has read the old reference
-  if (threadIdx.x == 0) cref[c] = M;
+  if (!(y32[c] >= 0 && M > c_old)) return;  // the same decision in every lane of the wave
+  if (lane == 0) cref[c] = M;
   if (!q) return;
   S* row = (S*)q + (int64_t)c * ldq;
-  for (int k = (int)threadIdx.x; k < (int)(ldq / KV); k += 256) {
+  for (int k = lane; k < (int)(ldq / KV); k += 64) {
     const float mj = m[k * KV / kSeg];
     if (mj == kNegInf) continue;  // a segment wholly past V: its q is 0
     const float f = ex2((mj - M) * kLog2e);
@@ -1619,7 +1636,7 @@ __global__ __launch_bounds__(256) void k_lse(const float* seg_m, const float* se
   }
 }
 
-// Per row of a chunk (one block per row), after the last q of the row is formed.
+// Per row of a chunk (one wave per row), after the last q of the row is formed.
 //   SCALE: f = g exp(c - lse) (0 for rows that do not count), so that dZ_v = f q_v away from the
 //          label; fscale gets f and hidden_f (plain [rows][H]) gets f times the row of hidden.
 //   FOLD:  the label's entry of q (when the label lies in the vocabulary columns [v0, v0 + vn) that q
@@ -1632,19 +1649,22 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_rowfix(const T* X, RowMap hmap, int64_t row0, int H, T* Xf,
                                                 const int* y32, const float* s_label, const float* lse,
                                                 const float* cref, const DevParams* prm, float softcap,
-                                                float* fscale, void* q, int64_t ldq, int v0, int vn, int mode) {
+                                                float* fscale, void* q, int64_t ldq, int v0, int vn, int mode,
+                                                int rows) {
   using S = typename Traits<T>::S;
   constexpr int KV = Traits<T>::KV;
-  const int c = blockIdx.x;
+  const int c = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (c >= rows) return;
   const int y = y32[c];
   const float l = lse[c], cr = cref[c];
   if (mode & 1) {
     const float g = y >= 0 ? prm->ginv : 0.0f;
     const float f = g == 0.0f ? 0.0f : g * ex2((cr - l) * kLog2e);
-    if (threadIdx.x == 0) fscale[c] = f;
+    if (lane == 0) fscale[c] = f;
     const T* x = X + hmap(row0 + c);
     T* xf = Xf + (int64_t)c * H;
-    for (int h = (int)threadIdx.x * KV; h < H; h += 256 * KV) {
+#pragma unroll 4
+    for (int h = lane * KV; h < H; h += 64 * KV) {
       float v[KV];
       unpack(*(const u32x4*)(x + h), v, (T*)nullptr);
 #pragma unroll
@@ -1652,7 +1672,7 @@ __global__ __launch_bounds__(256) void k_rowfix(const T* X, RowMap hmap, int64_t
       *(u32x4*)(xf + h) = pack(v, (T*)nullptr);
     }
   }
-  if ((mode & 2) && threadIdx.x == 0 && y >= v0 && y < v0 + vn) {
+  if ((mode & 2) && lane == 0 && y >= v0 && y < v0 + vn) {
     const float sy = s_label[c];
     const float t = softcap > 0.0f ? sy / softcap : 0.0f;
     const float val = (1.0f - t * t) * ex2((l - cr) * kLog2e) * expm1f(sy - l);
@@ -1660,24 +1680,34 @@ __global__ __launch_bounds__(256) void k_rowfix(const T* X, RowMap hmap, int64_t
   }
 }
 
-// Forward-only path: per-row lse and loss term of one chunk (rows row0 .. of the call), optionally
-// copied to caller buffers indexed by the call's row.
+// Forward-only path: per-row lse and loss term of one chunk (rows row0 .. of the call; one wave per
+// row), optionally copied to caller buffers indexed by the call's row.
 __global__ __launch_bounds__(256) void k_rows(const float* seg_m, const float* seg_s, int nseg,
                                               const int* y32, const float* s_label, float* loss_row,
-                                              float* loss_out, float* lse_out) {
-  const int c = blockIdx.x;
+                                              float* loss_out, float* lse_out, int rows) {
+  const int c = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (c >= rows) return;
   const float lse = row_lse(seg_m + (int64_t)c * nseg, seg_s + (int64_t)c * nseg, nseg, c, y32, s_label,
                             loss_row, lse_out);
-  (void)lse;
-  if (threadIdx.x == 0 && loss_out) loss_out[c] = loss_row[c];
+  if ((threadIdx.x & 63) == 0 && loss_out) loss_out[c] = y32[c] >= 0 ? lse - s_label[c] : 0.0f;
 }
 
 // Fixed-order loss reduction (one block).
 __global__ __launch_bounds__(1024) void k_finalize(const float* loss_row, int64_t BT,
                                                    const DevParams* prm, int reduction, float* loss) {
   __shared__ float sh[1024];
+  // thread i adds rows i, i + 1024, ... in that order; eight of them are loaded together
+  constexpr int kB = 8;
   float s = 0.0f;
-  for (int64_t t = threadIdx.x; t < BT; t += 1024) s += loss_row[t];
+  int64_t t = threadIdx.x;
+  for (; t + 1024 * (kB - 1) < BT; t += 1024 * kB) {
+    float v[kB];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) v[k] = loss_row[t + 1024 * k];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) s += v[k];
+  }
+  for (; t < BT; t += 1024) s += loss_row[t];
   sh[threadIdx.x] = s;
   __syncthreads();
   for (int o = 512; o > 0; o >>= 1) {
@@ -1812,11 +1842,13 @@ hipError_t launch_lse(const Problem& p, const Work& w, int64_t row0, int64_t row
                       hipStream_t stream) {
   void* q = rescale_q ? w.ws_e : nullptr;
   if (p.dtype == 0)
-    k_lse<__bf16><<<(unsigned)rows, 256, 0, stream>>>(w.seg_m, w.seg_s, (int)p.nseg, w.y32 + row0, w.s_label + row0,
-                                                      w.loss_row + row0, w.lse + row0, w.cref + row0, q, p.V_pad);
+    k_lse<__bf16><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(w.seg_m, w.seg_s, (int)p.nseg, w.y32 + row0,
+                                                                  w.s_label + row0, w.loss_row + row0, w.lse + row0,
+                                                                  w.cref + row0, q, p.V_pad, (int)rows);
   else
-    k_lse<float><<<(unsigned)rows, 256, 0, stream>>>(w.seg_m, w.seg_s, (int)p.nseg, w.y32 + row0, w.s_label + row0,
-                                                     w.loss_row + row0, w.lse + row0, w.cref + row0, q, p.V_pad);
+    k_lse<float><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(w.seg_m, w.seg_s, (int)p.nseg, w.y32 + row0,
+                                                                 w.s_label + row0, w.loss_row + row0, w.lse + row0,
+                                                                 w.cref + row0, q, p.V_pad, (int)rows);
   return hipGetLastError();
 }
 
@@ -1825,21 +1857,22 @@ hipError_t launch_rowfix(const Problem& p, const void* hidden, const Work& w, in
   if (vs.vn < 0) vs = VSlice{0, p.V};
   const int64_t ldq = (vs.vn + TILE - 1) / TILE * TILE;
   if (p.dtype == 0)
-    k_rowfix<__bf16><<<(unsigned)rows, 256, 0, stream>>>(
+    k_rowfix<__bf16><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(
         (const __bf16*)hidden, p.hmap, row0, (int)p.H, (__bf16*)w.xf, w.y32 + row0, w.s_label + row0, w.lse + row0,
-        w.cref + row0, w.params, p.softcap, w.fscale + row0, w.ws_e, ldq, (int)vs.v0, (int)vs.vn, mode);
+        w.cref + row0, w.params, p.softcap, w.fscale + row0, w.ws_e, ldq, (int)vs.v0, (int)vs.vn, mode, (int)rows);
   else
-    k_rowfix<float><<<(unsigned)rows, 256, 0, stream>>>(
+    k_rowfix<float><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(
         (const float*)hidden, p.hmap, row0, (int)p.H, (float*)w.xf, w.y32 + row0, w.s_label + row0, w.lse + row0,
-        w.cref + row0, w.params, p.softcap, w.fscale + row0, w.ws_e, ldq, (int)vs.v0, (int)vs.vn, mode);
+        w.cref + row0, w.params, p.softcap, w.fscale + row0, w.ws_e, ldq, (int)vs.v0, (int)vs.vn, mode, (int)rows);
   return hipGetLastError();
 }
 
 hipError_t launch_rows(const Problem& p, const Work& w, int64_t row0, int64_t rows, float* loss_rows,
                        float* lse_rows, hipStream_t stream) {
-  k_rows<<<(unsigned)rows, 256, 0, stream>>>(w.seg_m, w.seg_s, (int)p.nseg, w.y32 + row0, w.s_label + row0,
-                                             w.loss_row + row0, loss_rows ? loss_rows + row0 : nullptr,
-                                             lse_rows ? lse_rows + row0 : nullptr);
+  k_rows<<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(w.seg_m, w.seg_s, (int)p.nseg, w.y32 + row0,
+                                                         w.s_label + row0, w.loss_row + row0,
+                                                         loss_rows ? loss_rows + row0 : nullptr,
+                                                         lse_rows ? lse_rows + row0 : nullptr, (int)rows);
   return hipGetLastError();
 }
 
