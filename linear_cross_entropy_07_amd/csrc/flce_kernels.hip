@@ -1452,27 +1452,52 @@ __global__ __launch_bounds__(256) void k_dw_tail(const float* part, int splits, 
 }
 
 // ---- hidden chunk transpose: [rows][H] -> [H][ldt] through a 64 x 64 LDS tile ------------------
-// Row r of the chunk is call row row0 + r, found in hidden by the row map.
+// Row r of the chunk is call row row0 + r, found in hidden by the row map. Global memory is read and
+// written in 16-byte pieces (H is a multiple of 8 and the row strides of hidden and of the transposed
+// chunk are multiples of 16 bytes). A piece of the output that starts before `rows` is written whole:
+// its elements past `rows` are zeros, inside the chunk's capacity (a multiple of 256 rows). In LDS a
+// tile row takes 4 bytes more than its 64 elements, so that the column reads of a wave fall in
+// distinct banks.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* X, RowMap hmap, int64_t row0, int rows, int H, T* XT,
                                                    int64_t ldt) {
-  __shared__ T tile[64][65];
+  constexpr int KV = 16 / (int)sizeof(T);  // elements per 16-byte piece
+  constexpr int PR = 64 / KV;              // pieces per 64 elements
+  constexpr int ROWB = 64 * (int)sizeof(T) + 4;  // LDS bytes per tile row
+  __shared__ __attribute__((aligned(16))) char tile[64 * ROWB];
   __shared__ int64_t roff[64];
   const int r0 = blockIdx.y * 64, h0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  if (threadIdx.x < 64) roff[tx] = r0 + tx < rows ? hmap(row0 + r0 + tx) : 0;
+  if (threadIdx.x < 64) roff[threadIdx.x] = r0 + (int)threadIdx.x < rows ? hmap(row0 + r0 + threadIdx.x) : 0;
   __syncthreads();
+  u32x4 v[64 * PR / 256];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int r = r0 + ty + 4 * k, h = h0 + tx;
-    const bool in = r < rows && h < H;
-    tile[ty + 4 * k][tx] = in ? X[roff[ty + 4 * k] + h] : (T)0.0f;
+  for (int q = 0; q < 64 * PR / 256; ++q) {
+    const int idx = (int)threadIdx.x + 256 * q, r = idx / PR, h = h0 + (idx % PR) * KV;
+    v[q] = r0 + r < rows && h < H ? *(const u32x4*)(X + roff[r] + h) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int q = 0; q < 64 * PR / 256; ++q) {
+    const int idx = (int)threadIdx.x + 256 * q, r = idx / PR, c = idx % PR;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *(u32*)(tile + r * ROWB + c * 16 + 4 * e) = v[q][e];
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int h = h0 + ty + 4 * k, r = r0 + tx;
-    if (h < H && r < rows) XT[(int64_t)h * ldt + r] = tile[tx][ty + 4 * k];
+  for (int q = 0; q < 64 * PR / 256; ++q) {
+    const int idx = (int)threadIdx.x + 256 * q, hh = idx / PR, rc = idx % PR;
+    const int h = h0 + hh, r = r0 + rc * KV;
+    u32x4 o;
+    if constexpr (sizeof(T) == 2) {
+      unsigned short e16[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) e16[e] = *(const unsigned short*)(tile + (rc * 8 + e) * ROWB + hh * 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (u32)e16[2 * e] | ((u32)e16[2 * e + 1] << 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = *(const u32*)(tile + (rc * 4 + e) * ROWB + hh * 4);
+    }
+    if (h < H && r < rows) *(u32x4*)(XT + (int64_t)h * ldt + r) = o;
   }
 }
 
