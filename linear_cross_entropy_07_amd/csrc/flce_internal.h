@@ -42,7 +42,8 @@ struct DevParams {
 
 // Views of the workspace for one call (carved by the host).
 struct Work {
-  void* ws_e;          // [chunk_rows][V_pad] q = exp(s - c) (softcap derivative), bf16 or fp32
+  void* ws_e;          // chunk_rows x V_pad q = exp(s - c) (softcap derivative), bf16 or fp32, in blocks
+                       // of 256 rows x one 64-byte K step, ordered by tile of rows, then by v
   float* seg_m;        // [chunk_rows][nseg]: segment max
   float* seg_s;        // [chunk_rows][nseg]: segment sum of exp(s - segment max)
   int* y32;            // [BT] label or -1 for rows that do not count

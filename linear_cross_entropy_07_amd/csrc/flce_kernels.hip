@@ -12,7 +12,9 @@
 //             (row, 128-wide V segment) a reference r = max(c, segment max - kRefSpan), the sum of
 //             exp(s - r), and one 16-bit store per logit of q = exp(s - r) * (softcap derivative): the
 //             softmax numerator against the row's reference (r = c but for segments more than
-//             kRefSpan above it). No [BT, V] tensor exists.
+//             kRefSpan above it). q is stored in blocks of 256 rows x one K step of grad_hidden, so
+//             that each K step of the backward GEMMs reads long contiguous runs. No [BT, V] tensor
+//             exists.
 //   k_lse     per row: lse from the segment statistics and the loss term; a row with a segment whose
 //             reference lies above c gets the largest segment reference as its reference, its stored q
 //             rescaled segment by segment to match (the usual rows do nothing more).
@@ -118,6 +120,17 @@ template <> struct Traits<float> {
   using S = float;
   static constexpr int KV = 4;
 };
+
+// Layout of q in the workspace: blocks of 256 chunk rows x kQB values (kStepBytes per row, one K
+// step of the grad_hidden product), ordered by 256-row tile, then by v. A grad_hidden K step of one
+// tile is then one contiguous 16 KiB block, and a grad_W K step (the tile's 256 v of a few chunk rows)
+// is 256 / kQB runs of those rows. nkv = V_pad / kQB blocks per tile of rows.
+template <typename S>
+constexpr int kQB = kStepBytes / (int)sizeof(S);
+template <typename S>
+__host__ __device__ __forceinline__ int64_t q_index(int64_t c, int64_t v, int64_t nkv) {
+  return (((c >> 8) * nkv + v / kQB<S>) * 256 + (c & 255)) * kQB<S> + v % kQB<S>;
+}
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -343,6 +356,38 @@ struct OpK {
   }
 };
 
+// K-contiguous operand in the blocked q layout (the rows of one tile, K = v): step ks is one 16 KiB
+// block, row r of it at r * kStepBytes. Same LDS layout and fragments as OpK. Rows past the chunk
+// hold values no output row uses (the grad_hidden rows past the chunk are dropped).
+template <typename T>
+struct OpKB : OpK<T> {
+  using OpK<T>::BK;
+  using OpK<T>::KV;
+  using OpK<T>::RPI;
+  const char* base;  // the tile's first block
+  __device__ __forceinline__ void init(const T* blocks, int kmax_) {
+    base = (const char*)blocks;
+    this->kmax = kmax_;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < kDmaPerOp; ++q) {
+      const int row = RPI * (kDmaPerOp * wave + q) + lane / kChunks;
+      this->kc[q] = (lane % kChunks) ^ OpK<T>::swz(row);
+      this->rowoff[q] = (u32)(row * kStepBytes + this->kc[q] * 16);
+    }
+  }
+  __device__ __forceinline__ void issue_one(int ks, u32 lds, int q) const {
+    const int wave = threadIdx.x >> 6;
+    const int k = ks * BK + this->kc[q] * KV;
+    const i32x4 d = make_desc(base + (int64_t)ks * (TILE * kStepBytes), TILE * kStepBytes);
+    dma16(d, k < this->kmax ? this->rowoff[q] : kOOB, lds + (kDmaPerOp * wave + q) * 1024);
+  }
+  __device__ __forceinline__ void issue(int ks, u32 lds) const {
+#pragma unroll
+    for (int q = 0; q < kDmaPerOp; ++q) issue_one(ks, lds, q);
+  }
+};
+
 // MN-contiguous operand: a source row is one K index holding the tile's 256 M/N elements
 // contiguously. In LDS a row keeps that layout (256 * sizeof(T) bytes), 16-byte chunk c stored at
 // slot c ^ (kMnXor * (k & 3)). bf16 fragments come from two ds_read_b64_tr_b16: in each 16-lane group,
@@ -451,6 +496,45 @@ struct OpMN {
         f[i] = v;
       }
     }
+  }
+};
+
+// MN-contiguous operand from the blocked q layout: q^T of one tile's 256 v, K = chunk rows. The
+// 16-byte chunk c of K row k (v = v0 + c KV ..) lies in block (v0 + c KV) / kQB of k's tile of rows,
+// at row k % 256. Same LDS layout and fragments as OpMN; K rows from kvalid on load zeros.
+template <typename T>
+struct OpMNB : OpMN<T> {
+  using OpMN<T>::KV;
+  using OpMN<T>::BK;
+  using OpMN<T>::CPR;
+  using OpMN<T>::RPI;
+  static constexpr int QB = kQB<T>;
+  static_assert(TILE % BK == 0, "a K step stays within one tile of rows");
+  const char* base;     // tile of rows 0, the block of v0
+  int64_t tstride;      // bytes per tile of rows
+  int rowk[kDmaPerOp];  // the lane's K row within a step
+  __device__ __forceinline__ void init(const T* q, int64_t nkv, int v0, int kvalid_) {
+    base = (const char*)(q + (int64_t)(v0 / QB) * TILE * QB);
+    tstride = nkv * TILE * kStepBytes;
+    this->kvalid = kvalid_;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < kDmaPerOp; ++q) {
+      const int row = RPI * (kDmaPerOp * wave + q) + lane / CPR;
+      const int c = (lane % CPR) ^ (kMnXor * (row & 3));
+      rowk[q] = row;
+      this->off[q] = (u32)((c * KV / QB) * (TILE * kStepBytes) + row * kStepBytes + (c * KV % QB) * (int)sizeof(T));
+    }
+  }
+  __device__ __forceinline__ void issue_one(int ks, u32 lds, int q) const {
+    const int wave = threadIdx.x >> 6, k0 = ks * BK;
+    const char* b = base + (int64_t)(k0 >> 8) * tstride + (int64_t)(k0 & (TILE - 1)) * kStepBytes;
+    const i32x4 d = make_desc(b, (u32)(TILE / QB) * (TILE * kStepBytes));
+    dma16(d, rowk[q] < this->kvalid - k0 ? this->off[q] : kOOB, lds + (kDmaPerOp * wave + q) * 1024);
+  }
+  __device__ __forceinline__ void issue(int ks, u32 lds) const {
+#pragma unroll
+    for (int q = 0; q < kDmaPerOp; ++q) issue_one(ks, lds, q);
   }
 };
 
@@ -826,7 +910,7 @@ struct FwdArgs {
 
 struct DxArgs {
   const void* W;
-  const void* ws;     // q of the chunk, [rows][V_pad]
+  const void* ws;     // q of the chunk, blocked layout (q_index) with V_pad / kQB blocks per tile of rows
   const float* fscale;  // chunk row 0: the per-row factor f of dZ = f q (applied to the output rows)
   void* out;          // grad_hidden (splits == 1): row r of the call starts at element gmap(r)
   RowMap gmap;
@@ -840,7 +924,7 @@ struct DxArgs {
 
 struct DwArgs {
   const void* X;      // hidden_f = f hidden of the chunk, [rows][H]
-  const void* ws;     // q of the chunk, [rows][V_pad]
+  const void* ws;     // q of the chunk, blocked layout (q_index) with V_pad / kQB blocks per tile of rows
   float* dW;
   int64_t H, V, V_pad;
   int rows, accumulate;
@@ -901,23 +985,17 @@ __device__ __forceinline__ void fwd_labels(const FwdArgs& a, int c0, int (&ylab)
   }
 }
 
-// q tiles of 16-bit values are staged through the (then idle) LDS ring and written out as whole
-// 128-byte lines; the accumulator layout alone gives 8-byte pieces of 32 different rows per store.
-template <typename T>
-constexpr bool kStageQ = sizeof(typename Traits<T>::S) == 2 && kStages * kStageBytes >= TILE * TILE * 2;
-__device__ __forceinline__ u32 qlds(int cl, int vl) {  // byte address of q(cl, vl) in the staged tile
-  return (u32)(cl * (TILE * 2) + (((vl >> 3) ^ (cl & 31)) << 4) + ((vl & 7) << 1));
-}
-// Per-wave staging (FLCE_QSTAGE_WAVE, the default): each wave stages half of one column block at a
-// time, the MB rows of half its WM v values (one 128-byte line per row, 16-byte chunks XOR-swizzled by
-// the row), in an area of its own in the ring's last slot, and writes them out itself as whole lines
-// as soon as the half is complete. No block barrier is involved and the stores of one half overlap
-// the arithmetic of the next. Measured on MI355X against staging the whole tile through the ring
+// q tiles of 16-bit values are staged per wave through the (then idle) LDS ring: each wave stages
+// half of one column block at a time, the MB rows of half its WM v values (one 128-byte line per row,
+// 16-byte chunks XOR-swizzled by the row), in an area of its own in the ring's last slot, and writes
+// them out itself as soon as the half is complete, as 64-byte pieces that with those of the
+// neighbouring rows make 2 KiB runs of the blocked layout. No block barrier is involved and the
+// stores of one half overlap the arithmetic of the next. (The accumulator layout alone gives 8-byte
+// pieces of 32 rows per store.) Measured on MI355X against staging the whole tile through the ring
 // (one barrier, then all threads store): logits GEMM 3.33 against 3.37 ms at the Llama-3-8B head,
 // 1.30 against 1.36 ms at the GPT-2 head.
-#ifndef FLCE_QSTAGE_WAVE
-#define FLCE_QSTAGE_WAVE 1
-#endif
+template <typename T>
+constexpr bool kStageQ = sizeof(typename Traits<T>::S) == 2;
 constexpr int kQwRow = WM;                  // bytes per staged row: WM / 2 16-bit values
 constexpr int kQwBytes = MB * kQwRow;       // per wave and half column block
 constexpr int kQwBase = (kStages - 1) * kStageBytes;
@@ -986,9 +1064,14 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, facc (&acc)[
   // is at most exp(kRefSpan) (r = c unless the label logit lies more than kRefSpan below the segment
   // maximum; k_lse rescales such rows), the sums of e, and q = e (times the softcap derivative) to the
   // workspace. Rows that do not count have c = -inf, hence r = segment max - kRefSpan.
-  // q tile: rows c0.. of the chunk (rows past the chunk are dropped), columns v0 .. v0+255 < V_pad
-  const rsrc_t rq = make_rsrc((S*)a.ws + (int64_t)c0 * a.V_pad + v0,
-                              (int64_t)min(TILE, a.rows - c0) * a.V_pad * (int64_t)sizeof(S));
+  // q tile: rows c0.. of the chunk, columns v0 .. v0+255 < V_pad, in the tile of rows c0 / 256 of the
+  // blocked layout; rows past the chunk are not stored
+  constexpr int QB = kQB<S>;
+  const int64_t nkv = a.V_pad / QB;
+  const rsrc_t rq = make_rsrc((S*)a.ws + (int64_t)(c0 / TILE) * nkv * TILE * QB, nkv * TILE * kStepBytes);
+  const auto qoff = [&](int cl, int v) -> u32 {  // byte offset of q(c0 + cl, v) in that tile of rows
+    return c0 + cl < a.rows ? (u32)(((v / QB) * TILE + cl) * QB + v % QB) * (u32)sizeof(S) : kOOB;
+  };
   float sum[TBN] = {}, rf[TBN];
 #pragma unroll
   for (int j = J0; j < J0 + JG; ++j) {
@@ -996,7 +1079,9 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, facc (&acc)[
     // (a segment wholly past V has no maximum; its e are masked to 0 and its statistics record -inf)
     rf[j] = mx[j] == kNegInf ? 0.0f : fmaxf(cr[j], mx[j] - kRefSpan);
     const float msl = -rf[j] * kLog2e;
-    const u32 qrow = (u32)(((int64_t)(c - c0) * a.V_pad + wm * WM + vl0) * (int64_t)sizeof(S));
+    // the lane's offset of q(c, v0 + wm WM + vl0) for the unstaged (fp32) stores, or past the range
+    const u32 qlane = c < a.rows ? qoff(c - c0, v0 + wm * WM + vl0) : kOOB;
+    (void)qlane;
     float sum4[TBM];
 #pragma unroll
     for (int i = 0; i < TBM; ++i) {
@@ -1022,21 +1107,21 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, facc (&acc)[
         }
         // registers 4g .. 4g+3 are rows acc_row(4g) .. +3 of block i: four consecutive v
         const int vblk = MB * i + acc_row(4 * g, 0);
-        const u32 qoff = qrow + (u32)(vblk * sizeof(S));
         if constexpr (!STORE_Q) {
-          (void)qoff;
-        } else if constexpr (kStageQ<T> && FLCE_QSTAGE_WAVE) {
+        } else if constexpr (kStageQ<T>) {
           *(u32x2*)(smem + kQwBase + wave * kQwBytes + qwlds(col, vl0 + vblk - (i / (TBM / 2)) * (WM / 2))) =
               pack4_bf16(q[0], q[1], q[2], q[3]);
-        } else if constexpr (kStageQ<T>) {
-          *(u32x2*)(smem + qlds(c - c0, wm * WM + vl0 + vblk)) = pack4_bf16(q[0], q[1], q[2], q[3]);
-        } else if constexpr (sizeof(S) == 2) {
-          bstore_b64(rq, qoff, pack4_bf16(q[0], q[1], q[2], q[3]));
         } else {
-          bstore_b128(rq, qoff, __builtin_bit_cast(u32x4, f32x4{q[0], q[1], q[2], q[3]}));
+          // v = v0 + wm WM + vl0 + vblk: the lane's part vl0 (< 16) and vblk % kQB (at most 8) stay
+          // within one block, so the offset is the lane's qlane plus a constant per (i, g). The sum is
+          // selected per lane: with the constant in the scalar offset register instead, these 16-byte
+          // stores, whose data registers the next instruction rewrites, stored wrong data in some lanes
+          // on MI355X (no wait state is inserted for that form).
+          const u32 o = c < a.rows ? qlane + (u32)(((vblk / QB) * TILE * QB + vblk % QB) * (int)sizeof(S)) : kOOB;
+          bstore_b128(rq, o, __builtin_bit_cast(u32x4, f32x4{q[0], q[1], q[2], q[3]}));
         }
       }
-      if constexpr (STORE_Q && kStageQ<T> && FLCE_QSTAGE_WAVE) {
+      if constexpr (STORE_Q && kStageQ<T>) {
         if (i % (TBM / 2) == TBM / 2 - 1) {
           // half h of the wave's v values for the MB rows of column block j, one line per row
           const int h = i / (TBM / 2);
@@ -1048,8 +1133,7 @@ __device__ __forceinline__ void fwd_epilogue_part(const FwdArgs& a, facc (&acc)[
             const int cr = r0 + lane / kCh;
             const u32x4 v = *(const u32x4*)(wb + cr * kQwRow + ((ch ^ (cr & (kCh - 1))) << 4));
             const int cl = wn * WN + MB * j + cr;  // chunk row within the tile
-            bstore_b128(rq, (u32)((int64_t)cl * a.V_pad * (int64_t)sizeof(S)) +
-                                (u32)((wm * WM + h * (WM / 2) + ch * 8) * sizeof(S)), v);
+            bstore_b128(rq, qoff(cl, v0 + wm * WM + h * (WM / 2) + ch * 8), v);
           }
         }
       }
@@ -1124,22 +1208,6 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, facc (&acc)[TBM][
   }
 }
 
-// Staged q tile -> workspace: 32 threads per 512-byte row, each one 16-byte chunk; rows past the
-// chunk are dropped by the range-checked store.
-template <typename T>
-__device__ __forceinline__ void fwd_store_staged(const FwdArgs& a, int v0, int c0, const char* smem) {
-  using S = typename Traits<T>::S;
-  const rsrc_t rq = make_rsrc((S*)a.ws + (int64_t)c0 * a.V_pad + v0,
-                              (int64_t)min(TILE, a.rows - c0) * a.V_pad * (int64_t)sizeof(S));
-  const int t = threadIdx.x, ch = t & 31;
-  constexpr int kRowsPerPass = NTHR / 32;
-#pragma unroll 4
-  for (int row = t >> 5; row < TILE; row += kRowsPerPass) {
-    const u32x4 v = *(const u32x4*)(smem + row * (TILE * 2) + ((ch ^ (row & 31)) << 4));
-    bstore_b128(rq, (u32)((int64_t)row * a.V_pad * (int64_t)sizeof(S)) + (u32)(ch * 16), v);
-  }
-}
-
 template <typename T>
 __device__ __forceinline__ void fwd_loaders(const FwdArgs& a, int v0, int c0, OpK<T>& la, OpMN<T>& lb) {
   la.init((const T*)a.W + (int64_t)v0 * a.H, a.H, (int)min<int64_t>(TILE, a.V - v0), (int)a.H);  // W rows v0..
@@ -1172,10 +1240,6 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs& a, int v0, int c0, char*
       fwd_epilogue<T, false, true, STORE_Q, QONLY>(a, acc, v0, c0, ylab, smem);
     else
       fwd_epilogue<T, false, false, STORE_Q, QONLY>(a, acc, v0, c0, ylab, smem);
-  }
-  if constexpr (STORE_Q && kStageQ<T> && !FLCE_QSTAGE_WAVE) {
-    __syncthreads();
-    fwd_store_staged<T>(a, v0, c0, smem);
   }
 }
 
@@ -1271,8 +1335,8 @@ __global__ __launch_bounds__(NTHR) void k_dx(DxArgs a) {
   const int nk = (int)(a.V_pad / BK);
   const int kb = split * a.ksteps_per_split;
   const int ke = min(nk, kb + a.ksteps_per_split);
-  OpK<T> la;  // q rows of the chunk, K = v (only this split's K range is loaded)
-  la.init((const T*)a.ws + (int64_t)c0 * a.V_pad, a.V_pad, min(TILE, a.rows - c0), ke * BK);
+  OpKB<T> la;  // q rows of the chunk (blocked layout), K = v (only this split's K range is loaded)
+  la.init((const T*)a.ws + (int64_t)(c0 / TILE) * nk * TILE * BK, ke * BK);
   OpMN<T> lb;  // W: source rows are v (K), columns h
   lb.init((const T*)a.W + h0, a.H, (int)min<int64_t>(a.V, (int64_t)ke * BK), (int)min<int64_t>(TILE, a.H - h0));
   facc acc[TBM][TBN];
@@ -1363,8 +1427,8 @@ __global__ __launch_bounds__(NTHR) void k_dw(DwArgs a) {
 
   // only the block's K range is loaded: the rounded-up steps past ke of the unrolled loop load zeros
   const int kend = min(a.rows, ke * OpMN<T>::BK);
-  OpMN<T> la;  // q^T: source rows are chunk rows (K), columns are v (M); v0 + 256 <= V_pad
-  la.init((const T*)a.ws + v0, a.V_pad, kend, TILE);
+  OpMNB<T> la;  // q^T from the blocked layout: K = chunk rows, M = v; v0 + 256 <= V_pad
+  la.init((const T*)a.ws, a.V_pad / kQB<T>, v0, kend);
   OpMN<T> lb;  // hidden_f: source rows are chunk rows (K), columns h
   lb.init((const T*)a.X + h0, a.H, kend, (int)min<int64_t>(TILE, a.H - h0));
 
@@ -1635,7 +1699,7 @@ __global__ __launch_bounds__(256) void k_rowref(const T* X, RowMap hmap, int64_t
 template <typename T>
 __global__ __launch_bounds__(256) void k_lse(const float* seg_m, const float* seg_s, int nseg, const int* y32,
                                              const float* s_label, float* loss_row, float* lse, float* cref,
-                                             void* q, int64_t ldq, int rows) {
+                                             void* q, int64_t qvpad, int rows) {
   using S = typename Traits<T>::S;
   constexpr int KV = Traits<T>::KV;
   const int c = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1648,16 +1712,17 @@ __global__ __launch_bounds__(256) void k_lse(const float* seg_m, const float* se
   if (!(y32[c] >= 0 && M > c_old)) return;  // the same decision in every lane of the wave
   if (lane == 0) cref[c] = M;
   if (!q) return;
-  S* row = (S*)q + (int64_t)c * ldq;
-  for (int k = lane; k < (int)(ldq / KV); k += 64) {
+  const int64_t nkv = qvpad / kQB<S>;
+  for (int k = lane; k < (int)(qvpad / KV); k += 64) {
     const float mj = m[k * KV / kSeg];
     if (mj == kNegInf) continue;  // a segment wholly past V: its q is 0
     const float f = ex2((mj - M) * kLog2e);
+    S* p = (S*)q + q_index<S>(c, (int64_t)k * KV, nkv);  // KV consecutive v, inside one block
     float v[KV];
-    unpack(*(const u32x4*)(row + k * KV), v, (S*)nullptr);
+    unpack(*(const u32x4*)p, v, (S*)nullptr);
 #pragma unroll
     for (int e = 0; e < KV; ++e) v[e] *= f;
-    *(u32x4*)(row + k * KV) = pack(v, (S*)nullptr);
+    *(u32x4*)p = pack(v, (S*)nullptr);
   }
 }
 
@@ -1674,7 +1739,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_rowfix(const T* X, RowMap hmap, int64_t row0, int H, T* Xf,
                                                 const int* y32, const float* s_label, const float* lse,
                                                 const float* cref, const DevParams* prm, float softcap,
-                                                float* fscale, void* q, int64_t ldq, int v0, int vn, int mode,
+                                                float* fscale, void* q, int64_t qvpad, int v0, int vn, int mode,
                                                 int rows) {
   using S = typename Traits<T>::S;
   constexpr int KV = Traits<T>::KV;
@@ -1701,7 +1766,7 @@ __global__ __launch_bounds__(256) void k_rowfix(const T* X, RowMap hmap, int64_t
     const float sy = s_label[c];
     const float t = softcap > 0.0f ? sy / softcap : 0.0f;
     const float val = (1.0f - t * t) * ex2((l - cr) * kLog2e) * expm1f(sy - l);
-    ((S*)q)[(int64_t)c * ldq + (y - v0)] = (S)val;
+    ((S*)q)[q_index<S>(c, y - v0, qvpad / kQB<S>)] = (S)val;
   }
 }
 
@@ -1880,15 +1945,15 @@ hipError_t launch_lse(const Problem& p, const Work& w, int64_t row0, int64_t row
 hipError_t launch_rowfix(const Problem& p, const void* hidden, const Work& w, int64_t row0, int64_t rows,
                          hipStream_t stream, VSlice vs, int mode) {
   if (vs.vn < 0) vs = VSlice{0, p.V};
-  const int64_t ldq = (vs.vn + TILE - 1) / TILE * TILE;
+  const int64_t qvpad = (vs.vn + TILE - 1) / TILE * TILE;
   if (p.dtype == 0)
     k_rowfix<__bf16><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(
         (const __bf16*)hidden, p.hmap, row0, (int)p.H, (__bf16*)w.xf, w.y32 + row0, w.s_label + row0, w.lse + row0,
-        w.cref + row0, w.params, p.softcap, w.fscale + row0, w.ws_e, ldq, (int)vs.v0, (int)vs.vn, mode, (int)rows);
+        w.cref + row0, w.params, p.softcap, w.fscale + row0, w.ws_e, qvpad, (int)vs.v0, (int)vs.vn, mode, (int)rows);
   else
     k_rowfix<float><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(
         (const float*)hidden, p.hmap, row0, (int)p.H, (float*)w.xf, w.y32 + row0, w.s_label + row0, w.lse + row0,
-        w.cref + row0, w.params, p.softcap, w.fscale + row0, w.ws_e, ldq, (int)vs.v0, (int)vs.vn, mode, (int)rows);
+        w.cref + row0, w.params, p.softcap, w.fscale + row0, w.ws_e, qvpad, (int)vs.v0, (int)vs.vn, mode, (int)rows);
   return hipGetLastError();
 }
 
