@@ -356,3 +356,26 @@ def test_profile_kinds_match_the_header():
     count = kinds.pop("count")
     assert count == len(flce.FLCE.KERNELS) == len(kinds)
     assert all(flce.FLCE.KERNELS[v] == k for k, v in kinds.items())
+
+
+def test_no_wide_buffer_store_takes_a_register_scalar_offset(tmp_path):
+    """The device code (gfx950 assembly of the kernels, compiled here) has no 12- or 16-byte buffer
+    store whose scalar offset is a register. The compiler inserts the wait state such a store needs
+    before its data registers are rewritten only when the scalar offset is an inline constant; with a
+    register there, stores of this library once wrote wrong data in some lanes on MI355X."""
+    import os
+    import re
+    import subprocess
+
+    hipcc = build_lib.hipcc()
+    src = os.path.join(build_lib.CSRC, "flce_kernels.hip")
+    out = tmp_path / "k.s"
+    flags = [f for f in build_lib.HIP_FLAGS if f not in ("-fPIC",)]
+    res = subprocess.run([hipcc, *flags, "--cuda-device-only", "-S", "-I", build_lib.INCLUDE, "-I", build_lib.CSRC,
+                          src, "-o", str(out)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-4000:]
+    text = out.read_text()
+    stores = re.findall(r"^\s*buffer_store_dword(?:x3|x4)\b[^\n]*", text, re.M)
+    assert stores, "the kernels store through buffer descriptors"
+    bad = [s.strip() for s in stores if re.search(r",\s*s\d+\s+offen", s) or re.search(r",\s*s\d+\s*$", s)]
+    assert not bad, bad[:5]
